@@ -1,0 +1,306 @@
+/*
+ * oracle.c -- plain fp64 CPU statement of the low-bit linear layers.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may load this
+ * library: only tests/, __graft_entry__.smoke() and the cpu_baseline leg of
+ * bench.py call it.  It includes no header and shares no helper, table or
+ * constant with the HIP library under speculative_verify_amd/csrc; it is
+ * written from the definitions below, not from that code.
+ *
+ * Sources (the pages these definitions come from):
+ *  - "Efficient Qwen Competition" tech report, sec. 2.1 (target model QAD):
+ *    the served weight is the INT4 code matrix W_q times frozen symmetric
+ *    per-group scales s (no zero point), packed as W4A16; sec. 3.3 fixes the
+ *    group size at 128 along the input dimension.
+ *  - ShiftAddQwen README, intro and "Method / Format": every weight group is a
+ *    sum of sign planes, w = sum_p alpha_p * b_p with b_p in {-1,+1} and one
+ *    scale per (plane, group) along the input dimension; the mat-vec is a
+ *    signed add per plane followed by one multiply per plane and group.
+ *  - DFlash summary, sec. 4.1 and the tech report sec. 2.2: the target
+ *    verifies a drafted block in one parallel pass, and greedy (temperature 0)
+ *    decoding takes the argmax of the target's logits.
+ *  - small-vocabulary MTP study, sec. 3.3: a trimmed 32,768-row head whose
+ *    row index can be mapped back to a token id.
+ *
+ * Everything is evaluated in fp64 with no blocking or reordering beyond the
+ * group structure the definitions state.  Output rows are independent, so
+ * the loop over output rows n is split across OpenMP threads; each row's sum
+ * runs in the order written.
+ *
+ * Packed layouts (oracle_pack_*): the pages name the formats but not a byte
+ * layout; the layout is this project's own, stated here element by element
+ * (the same statement is in the repository's design notes):
+ *
+ *   INT4 blob.  N16 = N rounded up to 16, KT = K/128.
+ *     code tile (rt, kt) starts at byte (rt*KT + kt)*1024; inside it,
+ *     lane = 16*q + r owns the 16 bytes at 16*lane, dword t (t = 0..3) at
+ *     16*lane + 4*t (little endian).  That dword holds the codes of row
+ *     n = 16*rt + r at k = 128*kt + 32*t + 8*q + j, j = 0..7: even j = 2i in
+ *     bits [4i, 4i+4), odd j = 2i+1 in bits [16+4i, 20+4i).  A nibble holds
+ *     u = c + 8.  Rows n >= N hold c = 0.
+ *     Then bf16 scales s[n][g], n < N16 (0 for padded rows), row-major.
+ *   Binary-plane blob (P planes).
+ *     tile (rt, kt) starts at byte (rt*KT + kt)*256*P; lane = 16*q + r owns
+ *     4*P bytes at 4*P*lane, dword p at 4*P*lane + 4*p.  That dword holds the
+ *     signs of plane p, row n = 16*rt + r, k = 128*kt + 32*t + 8*q + j:
+ *     even j = 2i at bit 4t + i, odd j = 2i+1 at bit 16 + 4t + i.  Bit set
+ *     means b = -1.  Rows n >= N hold b = +1.
+ *     Then fp16 alpha[p][n][g], n < N16 (0 for padded rows), row-major.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* bfloat16 is the upper 16 bits of an IEEE-754 binary32; widening is exact. */
+double oracle_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits; exponent field 0 encodes subnormals f * 2^-24. */
+double oracle_f16_value(uint16_t bits) {
+  int sign = bits >> 15;
+  int e = (bits >> 10) & 0x1f;
+  int f = bits & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + (double)f, e - 25);
+  return sign ? -v : v;
+}
+
+void oracle_bf16_values(const uint16_t* bits, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_value(bits[i]);
+}
+
+void oracle_f16_values(const uint16_t* bits, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_value(bits[i]);
+}
+
+static double* decode_bf16_array(const uint16_t* bits, int64_t n) {
+  double* v = (double*)malloc((size_t)n * sizeof(double));
+  if (v) oracle_bf16_values(bits, n, v);
+  return v;
+}
+
+/*
+ * W4A16 linear layer (tech report sec. 2.1, 3.3):
+ *   y[m][n] = sum_g s[n][g] * ( sum_{k in group g} c[n][k] * x[m][k] )
+ *   a[m][n] = sum_k | s[n][g(k)] * c[n][k] * x[m][k] |   (tolerance scale)
+ * codes [N][K] int8, scales [N][K/G] bf16 bits, x [M][K] bf16 bits,
+ * y and a [M][N] fp64.  Returns 0, or -1 on bad sizes / no memory.
+ */
+int oracle_linear_w4a16(const int8_t* codes, const uint16_t* scales,
+                        const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                        int64_t G, double* y, double* a) {
+  if (M < 1 || N < 1 || K < 1 || G < 1 || K % G) return -1;
+  const int64_t ng = K / G;
+  double* xv = decode_bf16_array(x, M * K);
+  if (!xv) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t m = 0; m < M; ++m) {
+      double total = 0.0, total_abs = 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        const double s = oracle_bf16_value(scales[n * ng + g]);
+        double inner = 0.0, inner_abs = 0.0;
+        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+          const double p = (double)codes[n * K + k] * xv[m * K + k];
+          inner += p;
+          inner_abs += fabs(p);
+        }
+        total += s * inner;
+        total_abs += fabs(s) * inner_abs;
+      }
+      y[m * N + n] = total;
+      a[m * N + n] = total_abs;
+    }
+  }
+  free(xv);
+  return 0;
+}
+
+/*
+ * Binary-plane linear layer (ShiftAddQwen README, intro and "Format"):
+ *   y[m][n] = sum_g sum_p alpha[p][n][g] * ( sum_{k in g} b[p][n][k] * x[m][k] )
+ *   a[m][n] = sum_k | w[n][k] * x[m][k] |,  w[n][k] = sum_p alpha[p][n][g(k)] b[p][n][k]
+ * signs [P][N][K] int8 in {-1,+1}, alpha [P][N][K/G] fp16 bits.
+ */
+int oracle_linear_binplane(const int8_t* signs, const uint16_t* alpha,
+                           const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                           int64_t G, int64_t P, double* y, double* a) {
+  if (M < 1 || N < 1 || K < 1 || G < 1 || P < 1 || K % G) return -1;
+  const int64_t ng = K / G;
+  double* xv = decode_bf16_array(x, M * K);
+  if (!xv) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t m = 0; m < M; ++m) {
+      double total = 0.0, total_abs = 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        for (int64_t p = 0; p < P; ++p) {
+          const double al = oracle_f16_value(alpha[(p * N + n) * ng + g]);
+          double inner = 0.0;
+          for (int64_t k = g * G; k < (g + 1) * G; ++k)
+            inner += (double)signs[(p * N + n) * K + k] * xv[m * K + k];
+          total += al * inner;
+        }
+        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+          double w = 0.0;
+          for (int64_t p = 0; p < P; ++p)
+            w += oracle_f16_value(alpha[(p * N + n) * ng + g]) *
+                 (double)signs[(p * N + n) * K + k];
+          total_abs += fabs(w * xv[m * K + k]);
+        }
+      }
+      y[m * N + n] = total;
+      a[m * N + n] = total_abs;
+    }
+  }
+  free(xv);
+  return 0;
+}
+
+/*
+ * Greedy verification on a (possibly trimmed) W4A16 head (DFlash summary
+ * sec. 4.1; tech report sec. 2.2; MTP study sec. 3.3):
+ *   z[m][n]   = W4A16 logits as in oracle_linear_w4a16
+ *   idx[m]    = smallest n with z[m][n] == max_n z[m][n]
+ *   out[m]    = row_ids ? row_ids[idx[m]] : idx[m]
+ *   zmax[m]   = z[m][idx[m]],  amax[m] = a[m][idx[m]]
+ *   zsecond[m]= max over n != idx[m] of z[m][n]  (-inf when N == 1)
+ * The logits are materialised here on purpose: this is the slow statement.
+ */
+int oracle_argmax_w4a16(const int8_t* codes, const uint16_t* scales,
+                        const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                        int64_t G, const int32_t* row_ids, int32_t* out,
+                        int32_t* idx, double* zmax, double* amax,
+                        double* zsecond) {
+  double* z = (double*)malloc((size_t)(M * N) * sizeof(double));
+  double* a = (double*)malloc((size_t)(M * N) * sizeof(double));
+  if (!z || !a) {
+    free(z);
+    free(a);
+    return -1;
+  }
+  int rc = oracle_linear_w4a16(codes, scales, x, M, N, K, G, z, a);
+  if (rc == 0) {
+    for (int64_t m = 0; m < M; ++m) {
+      int64_t best = 0;
+      for (int64_t n = 1; n < N; ++n)
+        if (z[m * N + n] > z[m * N + best]) best = n;
+      double second = -INFINITY;
+      for (int64_t n = 0; n < N; ++n)
+        if (n != best && z[m * N + n] > second) second = z[m * N + n];
+      idx[m] = (int32_t)best;
+      out[m] = row_ids ? row_ids[best] : (int32_t)best;
+      zmax[m] = z[m * N + best];
+      amax[m] = a[m * N + best];
+      zsecond[m] = second;
+    }
+  }
+  free(z);
+  free(a);
+  return rc;
+}
+
+/* ---- packed layouts, stated one element at a time (see header) ---- */
+
+static void or_dword(uint8_t* blob, int64_t byte_off, uint32_t v) {
+  for (int b = 0; b < 4; ++b) blob[byte_off + b] |= (uint8_t)(v >> (8 * b));
+}
+
+int64_t oracle_int4_blob_bytes(int64_t N, int64_t K) {
+  const int64_t N16 = (N + 15) / 16 * 16;
+  return N16 * (K / 2) + N16 * (K / 128) * 2;
+}
+
+int oracle_pack_int4(const int8_t* codes, const uint16_t* scales, int64_t N,
+                     int64_t K, uint8_t* blob) {
+  if (N < 1 || K < 128 || K % 128) return -1;
+  const int64_t N16 = (N + 15) / 16 * 16, KT = K / 128, ng = K / 128;
+  memset(blob, 0, (size_t)oracle_int4_blob_bytes(N, K));
+  for (int64_t n = 0; n < N16; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      const int c = n < N ? codes[n * K + k] : 0;
+      if (c < -8 || c > 7) return -2;
+      const uint32_t u = (uint32_t)(c + 8);
+      const int64_t rt = n / 16, r = n % 16, kt = k / 128, kk = k % 128;
+      const int64_t t = kk / 32, q = (kk % 32) / 8, j = kk % 8;
+      const int64_t lane = 16 * q + r;
+      const int64_t off = (rt * KT + kt) * 1024 + 16 * lane + 4 * t;
+      const int bit = (j % 2) ? 16 + 4 * (int)(j / 2) : 4 * (int)(j / 2);
+      or_dword(blob, off, u << bit);
+    }
+  }
+  const int64_t soff = (N16 / 16) * KT * 1024;
+  for (int64_t n = 0; n < N16; ++n)
+    for (int64_t g = 0; g < ng; ++g) {
+      const uint16_t s = n < N ? scales[n * ng + g] : 0;
+      blob[soff + 2 * (n * ng + g)] = (uint8_t)(s & 0xff);
+      blob[soff + 2 * (n * ng + g) + 1] = (uint8_t)(s >> 8);
+    }
+  return 0;
+}
+
+int64_t oracle_binplane_blob_bytes(int64_t N, int64_t K, int64_t P) {
+  const int64_t N16 = (N + 15) / 16 * 16;
+  return N16 * (K / 8) * P + P * N16 * (K / 128) * 2;
+}
+
+int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
+                         int64_t K, int64_t P, uint8_t* blob) {
+  if (N < 1 || K < 128 || K % 128 || P < 1) return -1;
+  const int64_t N16 = (N + 15) / 16 * 16, KT = K / 128, ng = K / 128;
+  memset(blob, 0, (size_t)oracle_binplane_blob_bytes(N, K, P));
+  for (int64_t p = 0; p < P; ++p)
+    for (int64_t n = 0; n < N16; ++n)
+      for (int64_t k = 0; k < K; ++k) {
+        const int b = n < N ? signs[(p * N + n) * K + k] : 1;
+        if (b != 1 && b != -1) return -2;
+        if (b == 1) continue;
+        const int64_t rt = n / 16, r = n % 16, kt = k / 128, kk = k % 128;
+        const int64_t t = kk / 32, q = (kk % 32) / 8, j = kk % 8;
+        const int64_t lane = 16 * q + r;
+        const int64_t off = (rt * KT + kt) * 256 * P + 4 * P * lane + 4 * p;
+        const int bit = (j % 2) ? 16 + 4 * (int)t + (int)(j / 2)
+                                : 4 * (int)t + (int)(j / 2);
+        or_dword(blob, off, 1u << bit);
+      }
+  const int64_t aoff = (N16 / 16) * KT * 256 * P;
+  for (int64_t p = 0; p < P; ++p)
+    for (int64_t n = 0; n < N16; ++n)
+      for (int64_t g = 0; g < ng; ++g) {
+        const uint16_t a = n < N ? alpha[(p * N + n) * ng + g] : 0;
+        const int64_t e = (p * N16 + n) * ng + g;
+        blob[aoff + 2 * e] = (uint8_t)(a & 0xff);
+        blob[aoff + 2 * e + 1] = (uint8_t)(a >> 8);
+      }
+  return 0;
+}

@@ -1,0 +1,260 @@
+"""Pins for the fp64 CPU oracle, against facts fixed outside the oracle itself.
+
+Each test checks the oracle against a closed form, an invariant, a library
+routine on a special case, or a hand-worked fixture, chosen so that a plausible
+slip in the oracle (a dropped term, a wrong sign, a wrong group or k index, a
+transposed operand, the wrong plane's scale) fails at least one of them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_verify_amd import synth
+from conftest import read_golden_bytes
+
+ALL16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+BF16_ONE = 0x3F80
+F16_ONE = 0x3C00
+
+
+def onehot_x(K, k, value_bits=BF16_ONE):
+    x = np.zeros((1, K), np.uint16)
+    x[0, k] = value_bits
+    return x
+
+
+# ---- scalar decoders -------------------------------------------------------
+
+def test_bf16_decode_matches_torch_for_every_pattern():
+    ours = oracle.bf16_values(ALL16)
+    ref = torch.from_numpy(ALL16.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_f16_decode_matches_numpy_for_every_pattern():
+    ours = oracle.f16_values(ALL16)
+    ref = ALL16.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zero and the extreme subnormal / normal values
+    assert oracle.f16_values(np.array([0x8000], np.uint16))[0] == 0.0
+    assert np.signbit(oracle.f16_values(np.array([0x8000], np.uint16))[0])
+    assert oracle.f16_values(np.array([0x0001], np.uint16))[0] == 2.0 ** -24
+    assert oracle.f16_values(np.array([0x7BFF], np.uint16))[0] == 65504.0
+
+
+# ---- W4A16 ------------------------------------------------------------------
+
+def test_w4a16_onehot_selects_one_code_times_its_group_scale():
+    rng = np.random.default_rng(1)
+    N, K = 7, 384
+    codes, scales = synth.int4_weights(rng, N, K)
+    s = oracle.bf16_values(scales)
+    for k in range(K):
+        for vbits in (BF16_ONE, 0xBFC0):  # 1.0 and -1.5
+            v = oracle.bf16_values(np.array([vbits], np.uint16))[0]
+            y, a = oracle.linear_w4a16(codes, scales, onehot_x(K, k, vbits))
+            want = v * s[:, k // 128] * codes[:, k].astype(np.float64)
+            assert np.array_equal(y[0], want), k
+            assert np.array_equal(a[0], np.abs(want)), k
+
+
+def test_w4a16_unit_scales_reduce_to_integer_matmul():
+    rng = np.random.default_rng(2)
+    M, N, K = 3, 33, 512
+    codes = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    scales = np.full((N, K // 128), BF16_ONE, np.uint16)
+    xi = rng.integers(-3, 4, size=(M, K)).astype(np.int64)
+    xbits = synth.f32_to_bf16_bits(xi.astype(np.float32))
+    y, a = oracle.linear_w4a16(codes, scales, xbits)
+    want = xi @ codes.astype(np.int64).T
+    assert np.array_equal(y, want.astype(np.float64))
+    assert np.array_equal(a, (np.abs(xi) @ np.abs(codes.astype(np.int64)).T).astype(np.float64))
+
+
+def test_w4a16_sign_coherent_closed_form():
+    rng = np.random.default_rng(3)
+    N, K = 5, 512
+    codes = np.full((N, K), 7, np.int8)
+    _, scales = synth.int4_weights(rng, N, K)
+    x = synth.f32_to_bf16_bits(np.abs(rng.standard_normal((1, K))).astype(np.float32) + 0.01)
+    y, a = oracle.linear_w4a16(codes, scales, x)
+    xv = oracle.bf16_values(x)[0]
+    s = oracle.bf16_values(scales)
+    want = np.array([sum(7.0 * s[n, g] * xv[g * 128:(g + 1) * 128].sum()
+                         for g in range(K // 128)) for n in range(N)])
+    assert np.allclose(y[0], want, rtol=1e-14, atol=0)
+    assert np.array_equal(y, a)
+
+
+def test_w4a16_additive_over_groups():
+    rng = np.random.default_rng(4)
+    M, N, K = 2, 9, 640
+    codes, scales = synth.int4_weights(rng, N, K)
+    x = synth.activations(rng, M, K)
+    y, a = oracle.linear_w4a16(codes, scales, x)
+    parts = np.zeros_like(y)
+    for g in range(K // 128):
+        sg = np.zeros_like(scales)
+        sg[:, g] = scales[:, g]
+        yg, _ = oracle.linear_w4a16(codes, sg, x)
+        parts += yg
+    assert np.allclose(parts, y, rtol=0, atol=1e-12 * a.max())
+    assert np.all(a >= np.abs(y))
+
+
+# ---- binary planes -----------------------------------------------------------
+
+def test_binplane_single_unit_plane_is_a_signed_sum():
+    rng = np.random.default_rng(5)
+    M, N, K = 2, 17, 256
+    signs, _ = synth.binplane_weights(rng, N, K, P=1)
+    alpha = np.full((1, N, K // 128), F16_ONE, np.uint16)
+    xi = rng.integers(-5, 6, size=(M, K)).astype(np.int64)
+    y, a = oracle.linear_binplane(signs, alpha, synth.f32_to_bf16_bits(xi.astype(np.float32)))
+    assert np.array_equal(y, (xi @ signs[0].astype(np.int64).T).astype(np.float64))
+    assert np.array_equal(a, (np.abs(xi).sum(axis=1)[:, None] * np.ones((1, N))).astype(np.float64))
+
+
+def test_binplane_onehot_is_sum_of_plane_scales_times_signs():
+    rng = np.random.default_rng(6)
+    N, K, P = 6, 256, 3
+    signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+    al = oracle.f16_values(alpha)
+    for k in range(K):
+        y, a = oracle.linear_binplane(signs, alpha, onehot_x(K, k))
+        want = sum(al[p, :, k // 128] * signs[p, :, k] for p in range(P))
+        assert np.array_equal(y[0], want), k
+        assert np.array_equal(a[0], np.abs(want)), k
+
+
+def planes_from_odd_codes(codes):
+    """Three sign planes with c = 4 b1 + 2 b2 + b3 for odd c in [-7, 7]."""
+    c = codes.astype(np.int64)
+    b1 = np.where(c > 0, 1, -1)
+    r = c - 4 * b1
+    b2 = np.where(r > 0, 1, -1)
+    b3 = r - 2 * b2
+    assert np.all(np.abs(b3) == 1)
+    assert np.array_equal(4 * b1 + 2 * b2 + b3, c)
+    return np.stack([b1, b2, b3]).astype(np.int8)
+
+
+def test_three_planes_reproduce_odd_int4_codes():
+    rng = np.random.default_rng(7)
+    M, N, K = 3, 21, 512
+    codes = (2 * rng.integers(-4, 4, size=(N, K)) + 1).astype(np.int8)  # odd in [-7, 7]
+    _, scales = synth.int4_weights(rng, N, K)
+    s = synth.bf16_bits_to_f32(scales)
+    alpha = synth.f32_to_f16_bits(np.stack([4 * s, 2 * s, s]))
+    # every bf16 scale in [0.005, 0.02] and its 2x, 4x are exact in fp16
+    assert np.array_equal(oracle.f16_values(alpha), np.stack([4 * s, 2 * s, s]).astype(np.float64))
+    x = synth.activations(rng, M, K)
+    y4, a4 = oracle.linear_w4a16(codes, scales, x)
+    yb, ab = oracle.linear_binplane(planes_from_odd_codes(codes), alpha, x)
+    assert np.allclose(yb, y4, rtol=0, atol=1e-13 * a4.max())
+    assert np.allclose(ab, a4, rtol=1e-14, atol=0)
+
+
+# ---- greedy argmax -----------------------------------------------------------
+
+def test_argmax_finds_planted_rows_with_closed_form_logit():
+    case = synth.Case("t", "lmhead", 4, 300, 512)
+    codes, scales, x, rows = synth.make_lmhead(case, seed=11)
+    r = oracle.argmax_w4a16(codes, scales, x)
+    assert np.array_equal(r["idx"], rows.astype(np.int32))
+    xv = oracle.bf16_values(x)
+    for m in range(case.M):
+        s = oracle.bf16_values(scales[rows[m]])
+        want = sum(s[g] * 7.0 * np.abs(xv[m, g * 128:(g + 1) * 128]).sum()
+                   for g in range(case.K // 128))
+        assert r["zmax"][m] == pytest.approx(want, rel=1e-14)
+        assert r["amax"][m] == pytest.approx(want, rel=1e-14)
+        assert r["zsecond"][m] < r["zmax"][m]
+
+
+def test_argmax_ties_go_to_lowest_index_and_row_ids_map():
+    case = synth.Case("t", "lmhead", 2, 64, 256)
+    codes, scales, x, rows = synth.make_lmhead(case, seed=12)
+    lo, hi = 3, 40
+    for m in range(case.M):
+        codes[[lo, hi]] = codes[rows[m]]
+        scales[[lo, hi]] = scales[rows[m]]
+        rid = (1000 + 7 * np.arange(case.N)).astype(np.int32)
+        r = oracle.argmax_w4a16(codes, scales, x[m:m + 1], row_ids=rid)
+        assert r["idx"][0] == min(lo, rows[m])
+        assert r["out"][0] == rid[r["idx"][0]]
+        assert r["zsecond"][0] == r["zmax"][0]
+
+
+def test_argmax_agrees_with_first_occurrence_argmax_of_logits():
+    rng = np.random.default_rng(13)
+    M, N, K = 5, 97, 256
+    codes, scales = synth.int4_weights(rng, N, K)
+    x = synth.activations(rng, M, K)
+    y, _ = oracle.linear_w4a16(codes, scales, x)
+    r = oracle.argmax_w4a16(codes, scales, x)
+    assert np.array_equal(r["idx"], np.argmax(y, axis=1).astype(np.int32))
+    assert np.array_equal(r["zmax"], y.max(axis=1))
+
+
+# ---- packed layouts -----------------------------------------------------------
+
+def test_int4_pack_matches_hand_worked_bytes():
+    codes = ((np.arange(128) % 16) - 8).astype(np.int8)[None, :]
+    scales = np.array([[BF16_ONE]], np.uint16)
+    assert oracle.pack_int4(codes, scales).tobytes() == read_golden_bytes("int4_n1_k128.txt")
+
+
+def test_binplane_pack_matches_hand_worked_bytes():
+    signs = np.ones((2, 1, 128), np.int8)
+    signs[0, 0, [0, 1, 42, 127]] = -1
+    signs[1, 0, 64] = -1
+    alpha = np.array([[[F16_ONE]], [[0x3800]]], np.uint16)
+    got = oracle.pack_binplane(signs, alpha).tobytes()
+    assert got == read_golden_bytes("binplane_n1_k128_p2.txt")
+
+
+def test_int4_pack_places_every_code_in_its_own_nibble():
+    N, K = 20, 256
+    seen = {}
+    scales = np.zeros((N, K // 128), np.uint16)
+    code_bytes = ((N + 15) // 16 * 16) * K // 2
+    base = oracle.pack_int4(np.full((N, K), -8, np.int8), scales)[:code_bytes]
+    pad = base != 0  # padded rows hold code 0 (nibble 8)
+    for n in range(N):
+        for k in range(K):
+            codes = np.full((N, K), -8, np.int8)
+            codes[n, k] = 7
+            blob = oracle.pack_int4(codes, scales)[:code_bytes]
+            diff = np.flatnonzero(blob != base)
+            assert len(diff) == 1
+            nib = (int(blob[diff[0]]) >> 4, int(blob[diff[0]]) & 15)
+            assert nib in ((15, 0), (0, 15))
+            key = (int(diff[0]), nib)
+            assert key not in seen
+            seen[key] = (n, k)
+    assert not np.any(pad[: 16 * K // 2 * (N // 16)])  # full tiles carry no padding
+
+
+def test_binplane_pack_places_every_sign_in_its_own_bit():
+    N, K, P = 18, 256, 2
+    alpha = np.zeros((P, N, K // 128), np.uint16)
+    nbytes = ((N + 15) // 16 * 16) * K // 8 * P
+    seen = set()
+    for p in range(P):
+        for n in range(N):
+            for k in range(K):
+                signs = np.ones((P, N, K), np.int8)
+                signs[p, n, k] = -1
+                blob = oracle.pack_binplane(signs, alpha)[:nbytes]
+                nz = np.flatnonzero(blob)
+                assert len(nz) == 1 and bin(int(blob[nz[0]])).count("1") == 1
+                key = (int(nz[0]), int(blob[nz[0]]))
+                assert key not in seen
+                seen.add(key)
+    assert len(seen) == P * N * K
