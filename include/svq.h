@@ -1,0 +1,204 @@
+/*
+ * svq.h -- C ABI of the MI355X (gfx950) low-bit linear-layer library.
+ *
+ * Operations (what each call computes is stated with its declaration):
+ *   W4A16:  y[m][n] = sum_g s[n][g] * sum_{k in g} c[n][k] * x[m][k]
+ *           c in [-8, 7] INT4 codes, s bf16 symmetric per-group scales, no
+ *           zero point, groups of 128 along the input dimension k.
+ *           (Efficient Qwen Competition report, sec. 2.1 "Target Model
+ *           Optimization with QAD" and sec. 3.3 "Drafter Optimization".)
+ *   Binary planes: y[m][n] = sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] * x[m][k]
+ *           b in {-1, +1}, alpha fp16, one scale per (plane, row, group).
+ *           (ShiftAddQwen README, intro and "Method / Format".)
+ *   Greedy verify head: argmax over the W4A16 logits of a (possibly
+ *           vocabulary-trimmed) head, lowest index on ties, optionally mapped
+ *           through a row -> token-id table.  (DFlash summary sec. 4.1 and the
+ *           report's sec. 2.2 for parallel verification; small-vocabulary
+ *           MTP study sec. 3.3 for the trimmed 32,768-row head.)
+ *
+ * Conventions for every call:
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *   - Shapes: W is [N][K] (row n = output feature), x/X is [M][K] row-major,
+ *     y/Y is [M][N] row-major.  K % 128 == 0, G == 128.
+ *   - Return 0 (SVQ_OK) on success or a negative SVQ_ERR_* code.  On error
+ *     nothing is written and svq_last_error() returns a message for the
+ *     calling thread.  No C++ exception crosses this boundary.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no state beyond cached device attributes and the per-thread
+ *     error string.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream); they do not synchronise.  A launch
+ *     error is reported as SVQ_ERR_HIP; faults during execution surface at
+ *     the caller's next synchronisation.  Calls on one stream are ordered;
+ *     calls are reentrant.
+ *
+ * Packed blob layouts (the pages name the formats; the byte layout is this
+ * library's own, chosen so one 64-lane wave reads whole 1 KiB tiles and the
+ * same tile feeds both the mat-vec and the 16x16x32 bf16 MFMA):
+ *   INT4 blob, N16 = N rounded up to 16, KT = K / 128:
+ *     codes: tile (rt, kt) at byte (rt*KT + kt) * 1024.  Inside a tile,
+ *       lane = 16*q + r owns bytes [16*lane, 16*lane + 16) = four
+ *       little-endian dwords t = 0..3.  Dword t holds row n = 16*rt + r at
+ *       k = 128*kt + 32*t + 8*q + j (j = 0..7): even j = 2i in bits
+ *       [4i, 4i+4), odd j = 2i+1 in bits [16+4i, 20+4i), each nibble
+ *       u = c + 8.  Padding rows (n >= N) hold c = 0.
+ *     scales: bf16 s[n][g], n < N16 (0 for padding rows), row-major, right
+ *       after the codes, i.e. at byte N16 * K / 2.
+ *   Binary-plane blob with P planes:
+ *     signs: tile (rt, kt) at byte (rt*KT + kt) * 256 * P.  Lane 16*q + r
+ *       owns 4*P bytes at 4*P*lane; dword p is plane p for row 16*rt + r at
+ *       k = 128*kt + 32*t + 8*q + j: even j = 2i at bit 4t + i, odd j = 2i+1
+ *       at bit 16 + 4t + i.  A set bit means b = -1.  Padding rows hold +1.
+ *     alphas: fp16 alpha[p][n][g], n < N16 (0 for padding rows), row-major,
+ *       right after the signs, i.e. at byte N16 * K / 8 * P.
+ */
+#ifndef SVQ_H
+#define SVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SVQ_OK = 0,
+  SVQ_ERR_NULL = -1,      /* a required pointer is NULL */
+  SVQ_ERR_SHAPE = -2,     /* a size is out of the supported range */
+  SVQ_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
+  SVQ_ERR_RANGE = -4,     /* a code or sign is outside its alphabet */
+  SVQ_ERR_WORKSPACE = -5, /* workspace missing or too small */
+  SVQ_ERR_HIP = -6        /* the HIP runtime reported an error */
+};
+
+#define SVQ_GROUP 128     /* the only supported group size */
+#define SVQ_MAX_M 16      /* rows of a verify block */
+#define SVQ_MAX_P 6       /* sign planes per weight */
+#define SVQ_MAX_K 8192    /* largest input dimension the kernels accept */
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char* svq_last_error(void);
+
+/* Bytes of a packed INT4 blob: N16*K/2 + N16*(K/G)*2.  0 for bad sizes. */
+size_t svq_int4_packed_bytes(int64_t N, int64_t K, int32_t G);
+
+/* Bytes of a packed binary-plane blob: N16*K/8*P + P*N16*(K/G)*2.  0 for bad sizes. */
+size_t svq_binplane_packed_bytes(int64_t N, int64_t K, int32_t G, int32_t P);
+
+/* Workspace bytes that lmhead_argmax needs for M query rows. */
+size_t svq_lmhead_workspace_bytes(int32_t M);
+
+/*
+ * pack_int4_grouped -- HOST pointers, synchronous, CPU only.
+ * Stores INT4 codes with their frozen per-group scales in the INT4 blob
+ * layout above (report sec. 2.1: the updated weights are rounded back onto
+ * the original grid and served as W4A16; sec. 3.3: group size 128).
+ *   codes        [N][K] int8, each in [-8, 7]
+ *   scales_bf16  [N][K/G] bf16 bits
+ *   packed       svq_int4_packed_bytes(N, K, G) bytes, written in full
+ * Errors: NULL, SHAPE (N < 1, K % 128, G != 128), RANGE (first offending
+ * (n, k) is named in the message).
+ */
+int pack_int4_grouped(const int8_t* codes, const uint16_t* scales_bf16,
+                      int64_t N, int64_t K, int32_t G, uint8_t* packed);
+
+/* Inverse of pack_int4_grouped (HOST, for tests and inspection). */
+int unpack_int4_grouped(const uint8_t* packed, int64_t N, int64_t K, int32_t G,
+                        int8_t* codes, uint16_t* scales_bf16);
+
+/*
+ * pack_binary_planes -- HOST pointers, synchronous, CPU only.
+ * Stores P sign planes and their per-(plane, row, group) fp16 scales in the
+ * binary-plane blob layout above (ShiftAddQwen README, "Format": sign planes
+ * plus one scale per plane and group along the input dimension).
+ *   signs      [P][N][K] int8, each -1 or +1
+ *   alpha_f16  [P][N][K/G] fp16 bits
+ *   packed     svq_binplane_packed_bytes(N, K, G, P) bytes, written in full
+ * Errors: NULL, SHAPE (P outside 1..6, N < 1, K % 128, G != 128), RANGE.
+ */
+int pack_binary_planes(const int8_t* signs, const uint16_t* alpha_f16,
+                       int64_t N, int64_t K, int32_t G, int32_t P,
+                       uint8_t* packed);
+
+/* Inverse of pack_binary_planes (HOST, for tests and inspection). */
+int unpack_binary_planes(const uint8_t* packed, int64_t N, int64_t K, int32_t G,
+                         int32_t P, int8_t* signs, uint16_t* alpha_f16);
+
+/*
+ * gemv_w4a16 -- DEVICE pointers, asynchronous on `stream`.
+ * One decode step of a W4A16 linear layer (report sec. 2.1, 3.3):
+ *   y[n] = bf16_rne( sum_g s[n][g] * sum_{k in g} c[n][k] * x[k] ),
+ * accumulated in fp32 per group, scaled per group in fp32.
+ *   packed  INT4 blob, 16-byte aligned
+ *   x       [K] bf16 bits, 16-byte aligned
+ *   y       [N] bf16 bits, 2-byte aligned
+ * Errors: NULL, SHAPE (N < 1, K % 128, K > SVQ_MAX_K, G != 128), ALIGN, HIP.
+ */
+int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y,
+               int64_t N, int64_t K, int32_t G, void* stream);
+
+/*
+ * gemv_binplane -- DEVICE pointers, asynchronous on `stream`.
+ * One decode step of a binary-plane linear layer (ShiftAddQwen README):
+ *   y[n] = bf16_rne( sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] * x[k] ).
+ * Pointers and errors as gemv_w4a16, plus P in 1..6.
+ */
+int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y,
+                  int64_t N, int64_t K, int32_t G, int32_t P, void* stream);
+
+/*
+ * gemm_smallm_w4a16 -- DEVICE pointers, asynchronous on `stream`.
+ * The target's pass over a drafted block of M <= 16 positions (DFlash
+ * summary sec. 4.1: the drafted tokens are verified in parallel; report
+ * sec. 3.2: block size 16):  Y[m][n] = the W4A16 result for row m of X.
+ *   X  [M][K] bf16 bits, 16-byte aligned;  Y [M][N] bf16 bits, 2-byte aligned.
+ * Errors: as gemv_w4a16, plus SHAPE for M outside 1..16.
+ */
+int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
+                      int32_t M, int64_t N, int64_t K, int32_t G, void* stream);
+
+/*
+ * gemm_smallm_binplane -- DEVICE pointers, asynchronous on `stream`.
+ * Y[m][n] = the binary-plane result for row m of X, M in 1..16.
+ */
+int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
+                         int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,
+                         void* stream);
+
+/*
+ * lmhead_argmax -- DEVICE pointers, asynchronous on `stream`.
+ * Greedy decision of a W4A16 LM head for M <= 16 query rows (DFlash summary
+ * sec. 4.1; MTP study sec. 3.3):
+ *   z[m][n]     = W4A16 logits (fp32, never written to memory)
+ *   idx         = smallest n with z[m][n] == max_n z[m][n]
+ *   argmax[m]   = row_ids ? row_ids[idx] : idx          (int32)
+ *   maxlogit[m] = z[m][idx]                              (fp32)
+ *   X          [M][K] bf16 bits, 16-byte aligned
+ *   row_ids    NULL or [N] int32 (trimmed row -> token id), 4-byte aligned
+ *   argmax, maxlogit  [M], 4-byte aligned
+ *   workspace  >= svq_lmhead_workspace_bytes(M) bytes of device memory,
+ *              16-byte aligned; needs no initialisation; its contents are
+ *              scratch and are overwritten by every call.
+ * Errors: as gemm_smallm_w4a16, plus WORKSPACE.  Calls that overlap in time
+ * must not share a workspace.
+ */
+int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M,
+                  int64_t N, int64_t K, int32_t G, const int32_t* row_ids,
+                  int32_t* argmax, float* maxlogit, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * svq_stream_read -- DEVICE pointers, asynchronous on `stream`.
+ * Measurement aid, not part of the method: reads `bytes` (a multiple of 16)
+ * from `src` with 16-byte loads and writes one uint32 checksum per workgroup
+ * into `sink` (>= 4096 * 4 bytes).  Gives the achievable streaming-read
+ * ceiling and the counter calibration for the same launch shape.
+ */
+int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVQ_H */

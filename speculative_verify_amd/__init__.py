@@ -1,0 +1,192 @@
+"""speculative_verify_amd -- low-bit linear layers for MI355X (gfx950).
+
+A thin ctypes binding over ``libsvq.so`` (C ABI in ``include/svq.h``).  It
+only marshals arguments: every step of the computation runs in the library's
+HIP kernels (device calls) or its C++ packers (host calls).  PyTorch supplies
+device memory and the current stream.  If the library is missing, every call
+raises -- there is no fallback path.
+
+Functions (same names as the C ABI):
+  pack_int4_grouped, unpack_int4_grouped, pack_binary_planes,
+  unpack_binary_planes                       host numpy arrays
+  gemv_w4a16, gemv_binplane, gemm_smallm_w4a16, gemm_smallm_binplane,
+  lmhead_argmax, svq_stream_read             torch CUDA tensors
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "SvqError", "lib_path", "load", "int4_packed_bytes", "binplane_packed_bytes",
+    "lmhead_workspace_bytes", "pack_int4_grouped", "unpack_int4_grouped",
+    "pack_binary_planes", "unpack_binary_planes", "gemv_w4a16", "gemv_binplane",
+    "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "svq_stream_read",
+]
+
+GROUP = 128
+ERRORS = {-1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "RANGE", -5: "WORKSPACE", -6: "HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class SvqError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: SVQ_ERR_{ERRORS.get(code, code)} ({code}): {msg}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return os.environ.get("SVQ_LIB", os.path.join(_HERE, "libsvq.so"))
+
+
+def load():
+    """Load libsvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "or python speculative_verify_amd/build.py")
+    lib = ctypes.CDLL(path)
+    V, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "svq_last_error": ([], ctypes.c_char_p),
+        "svq_int4_packed_bytes": ([I64, I64, I32], SZ),
+        "svq_binplane_packed_bytes": ([I64, I64, I32, I32], SZ),
+        "svq_lmhead_workspace_bytes": ([I32], SZ),
+        "pack_int4_grouped": ([V, V, I64, I64, I32, V], ctypes.c_int),
+        "unpack_int4_grouped": ([V, I64, I64, I32, V, V], ctypes.c_int),
+        "pack_binary_planes": ([V, V, I64, I64, I32, I32, V], ctypes.c_int),
+        "unpack_binary_planes": ([V, I64, I64, I32, I32, V, V], ctypes.c_int),
+        "gemv_w4a16": ([V, V, V, I64, I64, I32, V], ctypes.c_int),
+        "gemv_binplane": ([V, V, V, I64, I64, I32, I32, V], ctypes.c_int),
+        "gemm_smallm_w4a16": ([V, V, V, I32, I64, I64, I32, V], ctypes.c_int),
+        "gemm_smallm_binplane": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
+        "lmhead_argmax": ([V, V, I32, I64, I64, I32, V, V, V, V, SZ, V], ctypes.c_int),
+        "svq_stream_read": ([V, SZ, V, V], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        msg = load().svq_last_error().decode(errors="replace")
+        raise SvqError(fn, rc, msg)
+
+
+def _np_ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dev_ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device argument must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError("device argument must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---- sizes ------------------------------------------------------------------
+
+def int4_packed_bytes(N: int, K: int, G: int = GROUP) -> int:
+    return int(load().svq_int4_packed_bytes(N, K, G))
+
+
+def binplane_packed_bytes(N: int, K: int, P: int, G: int = GROUP) -> int:
+    return int(load().svq_binplane_packed_bytes(N, K, G, P))
+
+
+def lmhead_workspace_bytes(M: int) -> int:
+    return int(load().svq_lmhead_workspace_bytes(M))
+
+
+# ---- host packers -------------------------------------------------------------
+
+def pack_int4_grouped(codes: np.ndarray, scales_bf16: np.ndarray, G: int = GROUP) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.int8)
+    scales = np.ascontiguousarray(scales_bf16, np.uint16)
+    N, K = codes.shape
+    out = np.empty(int4_packed_bytes(N, K, G), np.uint8)
+    _check("pack_int4_grouped", load().pack_int4_grouped(_np_ptr(codes), _np_ptr(scales), N, K, G, _np_ptr(out)))
+    return out
+
+
+def unpack_int4_grouped(packed: np.ndarray, N: int, K: int, G: int = GROUP):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    codes = np.empty((N, K), np.int8)
+    scales = np.empty((N, K // G), np.uint16)
+    _check("unpack_int4_grouped",
+           load().unpack_int4_grouped(_np_ptr(packed), N, K, G, _np_ptr(codes), _np_ptr(scales)))
+    return codes, scales
+
+
+def pack_binary_planes(signs: np.ndarray, alpha_f16: np.ndarray, G: int = GROUP) -> np.ndarray:
+    signs = np.ascontiguousarray(signs, np.int8)
+    alpha = np.ascontiguousarray(alpha_f16, np.uint16)
+    P, N, K = signs.shape
+    out = np.empty(binplane_packed_bytes(N, K, P, G), np.uint8)
+    _check("pack_binary_planes",
+           load().pack_binary_planes(_np_ptr(signs), _np_ptr(alpha), N, K, G, P, _np_ptr(out)))
+    return out
+
+
+def unpack_binary_planes(packed: np.ndarray, N: int, K: int, P: int, G: int = GROUP):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    signs = np.empty((P, N, K), np.int8)
+    alpha = np.empty((P, N, K // G), np.uint16)
+    _check("unpack_binary_planes",
+           load().unpack_binary_planes(_np_ptr(packed), N, K, G, P, _np_ptr(signs), _np_ptr(alpha)))
+    return signs, alpha
+
+
+# ---- device calls (torch tensors; bf16/fp16 values as int16/uint16 bits or bf16) --
+
+def gemv_w4a16(packed, x, y, N: int, K: int, G: int = GROUP, stream=None) -> None:
+    _check("gemv_w4a16", load().gemv_w4a16(_dev_ptr(packed), _dev_ptr(x), _dev_ptr(y), N, K, G, _stream(stream)))
+
+
+def gemv_binplane(packed, x, y, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
+    _check("gemv_binplane",
+           load().gemv_binplane(_dev_ptr(packed), _dev_ptr(x), _dev_ptr(y), N, K, G, P, _stream(stream)))
+
+
+def gemm_smallm_w4a16(packed, X, Y, M: int, N: int, K: int, G: int = GROUP, stream=None) -> None:
+    _check("gemm_smallm_w4a16",
+           load().gemm_smallm_w4a16(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, _stream(stream)))
+
+
+def gemm_smallm_binplane(packed, X, Y, M: int, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
+    _check("gemm_smallm_binplane",
+           load().gemm_smallm_binplane(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, P,
+                                       _stream(stream)))
+
+
+def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace,
+                  row_ids=None, G: int = GROUP, stream=None) -> None:
+    _check("lmhead_argmax",
+           load().lmhead_argmax(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, _dev_ptr(row_ids),
+                                _dev_ptr(argmax), _dev_ptr(maxlogit), _dev_ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def svq_stream_read(src, nbytes: int, sink, stream=None) -> None:
+    _check("svq_stream_read", load().svq_stream_read(_dev_ptr(src), nbytes, _dev_ptr(sink), _stream(stream)))

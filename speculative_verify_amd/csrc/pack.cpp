@@ -1,0 +1,209 @@
+// Host-side packers for the INT4 and binary-plane blobs (layouts in svq.h).
+//
+// Packing is offline work: the report (sec. 2.1) rounds the trained weights
+// back onto the frozen INT4 grid "at packing time", and the ShiftAddQwen
+// pipeline writes its sign planes once into its own container.  These
+// routines therefore run on the CPU, synchronously, and validate every code.
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "svq.h"
+#include "svq_internal.h"
+
+namespace {
+
+// Split [0, n) over the host's threads; each chunk is independent.
+template <class F>
+void parallel_for(int64_t n, F f) {
+  int nt = (int)std::thread::hardware_concurrency();
+  if (nt < 1) nt = 1;
+  if (nt > 32) nt = 32;
+  if (n < 64 || nt == 1) {
+    f((int64_t)0, n);
+    return;
+  }
+  std::vector<std::thread> th;
+  const int64_t chunk = (n + nt - 1) / nt;
+  for (int i = 0; i < nt; ++i) {
+    const int64_t lo = i * chunk, hi = lo + chunk < n ? lo + chunk : n;
+    if (lo >= hi) break;
+    th.emplace_back([=] { f(lo, hi); });
+  }
+  for (auto& t : th) t.join();
+}
+
+inline void store_u32(uint8_t* p, uint32_t v) { std::memcpy(p, &v, 4); }
+inline uint32_t load_u32(const uint8_t* p) {
+  uint32_t v;
+  std::memcpy(&v, p, 4);
+  return v;
+}
+
+int check_common(int64_t N, int64_t K, int32_t G) {
+  if (N < 1) return svq::fail(SVQ_ERR_SHAPE, "N must be >= 1 (got %lld)", (long long)N);
+  if (G != SVQ_GROUP) return svq::fail(SVQ_ERR_SHAPE, "group size G must be 128 (got %d)", G);
+  if (K < SVQ_GROUP || K % SVQ_GROUP)
+    return svq::fail(SVQ_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  return SVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t svq_int4_packed_bytes(int64_t N, int64_t K, int32_t G) {
+  if (N < 1 || G != SVQ_GROUP || K < SVQ_GROUP || K % SVQ_GROUP) return 0;
+  const int64_t N16 = svq::round16(N);
+  return (size_t)(N16 * (K / 2) + N16 * (K / G) * 2);
+}
+
+size_t svq_binplane_packed_bytes(int64_t N, int64_t K, int32_t G, int32_t P) {
+  if (N < 1 || G != SVQ_GROUP || K < SVQ_GROUP || K % SVQ_GROUP || P < 1 || P > SVQ_MAX_P) return 0;
+  const int64_t N16 = svq::round16(N);
+  return (size_t)(N16 * (K / 8) * P + (int64_t)P * N16 * (K / G) * 2);
+}
+
+int pack_int4_grouped(const int8_t* codes, const uint16_t* scales_bf16, int64_t N, int64_t K,
+                      int32_t G, uint8_t* packed) {
+  svq::clear_error();
+  if (!codes || !scales_bf16 || !packed) return svq::fail(SVQ_ERR_NULL, "pack_int4_grouped: NULL pointer");
+  if (int rc = check_common(N, K, G)) return rc;
+  for (int64_t i = 0; i < N * K; ++i)
+    if (codes[i] < -8 || codes[i] > 7)
+      return svq::fail(SVQ_ERR_RANGE, "pack_int4_grouped: code %d at (n=%lld, k=%lld) outside [-8, 7]",
+                       (int)codes[i], (long long)(i / K), (long long)(i % K));
+  const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16, ng = K / G;
+  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+    static const int8_t zero_row[32] = {0};
+    for (int64_t rt = lo; rt < hi; ++rt)
+      for (int64_t kt = 0; kt < KT; ++kt) {
+        uint8_t* tile = packed + (rt * KT + kt) * 1024;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int q = lane >> 4, r = lane & 15;
+          const int64_t n = rt * 16 + r;
+          for (int t = 0; t < 4; ++t) {
+            const int8_t* c = n < N ? codes + n * K + kt * 128 + t * 32 + q * 8 : zero_row;
+            uint32_t w = 0;
+            for (int i = 0; i < 4; ++i) {
+              w |= (uint32_t)(c[2 * i] + 8) << (4 * i);
+              w |= (uint32_t)(c[2 * i + 1] + 8) << (16 + 4 * i);
+            }
+            store_u32(tile + 16 * lane + 4 * t, w);
+          }
+        }
+      }
+  });
+  uint8_t* s = packed + N16 * (K / 2);
+  std::memcpy(s, scales_bf16, (size_t)(N * ng * 2));
+  std::memset(s + N * ng * 2, 0, (size_t)((N16 - N) * ng * 2));
+  return SVQ_OK;
+}
+
+int unpack_int4_grouped(const uint8_t* packed, int64_t N, int64_t K, int32_t G, int8_t* codes,
+                        uint16_t* scales_bf16) {
+  svq::clear_error();
+  if (!codes || !scales_bf16 || !packed) return svq::fail(SVQ_ERR_NULL, "unpack_int4_grouped: NULL pointer");
+  if (int rc = check_common(N, K, G)) return rc;
+  const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16, ng = K / G;
+  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+    for (int64_t rt = lo; rt < hi; ++rt)
+      for (int64_t kt = 0; kt < KT; ++kt) {
+        const uint8_t* tile = packed + (rt * KT + kt) * 1024;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int q = lane >> 4, r = lane & 15;
+          const int64_t n = rt * 16 + r;
+          if (n >= N) continue;
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t w = load_u32(tile + 16 * lane + 4 * t);
+            int8_t* c = codes + n * K + kt * 128 + t * 32 + q * 8;
+            for (int i = 0; i < 4; ++i) {
+              c[2 * i] = (int8_t)(((w >> (4 * i)) & 15) - 8);
+              c[2 * i + 1] = (int8_t)(((w >> (16 + 4 * i)) & 15) - 8);
+            }
+          }
+        }
+      }
+  });
+  std::memcpy(scales_bf16, packed + N16 * (K / 2), (size_t)(N * ng * 2));
+  return SVQ_OK;
+}
+
+int pack_binary_planes(const int8_t* signs, const uint16_t* alpha_f16, int64_t N, int64_t K, int32_t G,
+                       int32_t P, uint8_t* packed) {
+  svq::clear_error();
+  if (!signs || !alpha_f16 || !packed) return svq::fail(SVQ_ERR_NULL, "pack_binary_planes: NULL pointer");
+  if (int rc = check_common(N, K, G)) return rc;
+  if (P < 1 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "P must be in 1..6 (got %d)", P);
+  const int64_t total = (int64_t)P * N * K;
+  for (int64_t i = 0; i < total; ++i)
+    if (signs[i] != 1 && signs[i] != -1)
+      return svq::fail(SVQ_ERR_RANGE, "pack_binary_planes: sign %d at (p=%lld, n=%lld, k=%lld) is not +-1",
+                       (int)signs[i], (long long)(i / (N * K)), (long long)((i / K) % N), (long long)(i % K));
+  const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16, ng = K / G;
+  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+    for (int64_t rt = lo; rt < hi; ++rt)
+      for (int64_t kt = 0; kt < KT; ++kt) {
+        uint8_t* tile = packed + (rt * KT + kt) * 256 * P;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int q = lane >> 4, r = lane & 15;
+          const int64_t n = rt * 16 + r;
+          for (int p = 0; p < P; ++p) {
+            uint32_t w = 0;
+            if (n < N) {
+              const int8_t* b = signs + ((int64_t)p * N + n) * K + kt * 128 + q * 8;
+              for (int t = 0; t < 4; ++t)
+                for (int i = 0; i < 4; ++i) {
+                  w |= (uint32_t)(b[32 * t + 2 * i] < 0) << (4 * t + i);
+                  w |= (uint32_t)(b[32 * t + 2 * i + 1] < 0) << (16 + 4 * t + i);
+                }
+            }
+            store_u32(tile + 4 * P * lane + 4 * p, w);
+          }
+        }
+      }
+  });
+  uint8_t* a = packed + N16 * (K / 8) * P;
+  for (int p = 0; p < P; ++p) {
+    std::memcpy(a + (int64_t)p * N16 * ng * 2, alpha_f16 + (int64_t)p * N * ng, (size_t)(N * ng * 2));
+    std::memset(a + ((int64_t)p * N16 + N) * ng * 2, 0, (size_t)((N16 - N) * ng * 2));
+  }
+  return SVQ_OK;
+}
+
+int unpack_binary_planes(const uint8_t* packed, int64_t N, int64_t K, int32_t G, int32_t P, int8_t* signs,
+                         uint16_t* alpha_f16) {
+  svq::clear_error();
+  if (!signs || !alpha_f16 || !packed) return svq::fail(SVQ_ERR_NULL, "unpack_binary_planes: NULL pointer");
+  if (int rc = check_common(N, K, G)) return rc;
+  if (P < 1 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "P must be in 1..6 (got %d)", P);
+  const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16, ng = K / G;
+  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+    for (int64_t rt = lo; rt < hi; ++rt)
+      for (int64_t kt = 0; kt < KT; ++kt) {
+        const uint8_t* tile = packed + (rt * KT + kt) * 256 * P;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int q = lane >> 4, r = lane & 15;
+          const int64_t n = rt * 16 + r;
+          if (n >= N) continue;
+          for (int p = 0; p < P; ++p) {
+            const uint32_t w = load_u32(tile + 4 * P * lane + 4 * p);
+            int8_t* b = signs + ((int64_t)p * N + n) * K + kt * 128 + q * 8;
+            for (int t = 0; t < 4; ++t)
+              for (int i = 0; i < 4; ++i) {
+                b[32 * t + 2 * i] = (w >> (4 * t + i)) & 1 ? -1 : 1;
+                b[32 * t + 2 * i + 1] = (w >> (16 + 4 * t + i)) & 1 ? -1 : 1;
+              }
+          }
+        }
+      }
+  });
+  const uint8_t* a = packed + N16 * (K / 8) * P;
+  for (int p = 0; p < P; ++p)
+    std::memcpy(alpha_f16 + (int64_t)p * N * ng, a + (int64_t)p * N16 * ng * 2, (size_t)(N * ng * 2));
+  return SVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+"""The C-ABI library loads, exports every symbol include/svq.h declares, and
+rejects bad arguments before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import speculative_verify_amd as svq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "svq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["pack_int4_grouped", "pack_binary_planes", "gemv_w4a16", "gemv_binplane",
+                 "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "svq_last_error"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(svq.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_sizes():
+    assert svq.int4_packed_bytes(12288, 4096) == 25165824 + 786432
+    assert svq.binplane_packed_bytes(12288, 4096, 3) == 18874368 + 2359296
+    assert svq.int4_packed_bytes(248320, 4096) == 508559360 + 15892480
+    assert svq.int4_packed_bytes(32768, 4096) == 69206016 - 2097152 + 2097152  # 67108864 + 2097152
+    assert svq.lmhead_workspace_bytes(16) >= 16 * 8 and svq.lmhead_workspace_bytes(17) == 0
+
+
+A = 0x100000  # an aligned address that is never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda l: l.gemv_w4a16(None, A, A, 16, 128, 128, None), -1),
+    (lambda l: l.gemv_w4a16(A, A, A, 0, 128, 128, None), -2),
+    (lambda l: l.gemv_w4a16(A, A, A, 16, 100, 128, None), -2),
+    (lambda l: l.gemv_w4a16(A, A, A, 16, 128 * 65, 128, None), -2),
+    (lambda l: l.gemv_w4a16(A, A, A, 16, 128, 64, None), -2),
+    (lambda l: l.gemv_w4a16(A + 8, A, A, 16, 128, 128, None), -3),
+    (lambda l: l.gemv_w4a16(A, A + 4, A, 16, 128, 128, None), -3),
+    (lambda l: l.gemv_w4a16(A, A, A + 1, 16, 128, 128, None), -3),
+    (lambda l: l.gemv_binplane(A, A, A, 16, 128, 128, 0, None), -2),
+    (lambda l: l.gemv_binplane(A, A, A, 16, 128, 128, 7, None), -2),
+    (lambda l: l.gemm_smallm_w4a16(A, A, A, 0, 16, 128, 128, None), -2),
+    (lambda l: l.gemm_smallm_w4a16(A, A, A, 17, 16, 128, 128, None), -2),
+    (lambda l: l.gemm_smallm_binplane(A, A, A, 4, 16, 128, 128, 0, None), -2),
+    (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, A, None, 0, None), -5),
+    (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, A, A, 8, None), -5),
+    (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, None, A, 1 << 20, None), -1),
+    (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, A + 2, A, A, A, 1 << 20, None), -3),
+    (lambda l: l.svq_stream_read(A, 100, A, None), -2),
+])
+def test_argument_validation(call, code):
+    lib = svq.load()
+    assert call(lib) == code
+    assert lib.svq_last_error().decode()
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device error path")
+def test_no_device_is_a_hip_error_not_a_crash():
+    lib = svq.load()
+    rc = lib.gemv_w4a16(A, A, A, 16, 128, 128, None)
+    assert rc == -6
+    assert "hip" in lib.svq_last_error().decode().lower()

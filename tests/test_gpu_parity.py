@@ -1,0 +1,372 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on MI355X.
+
+Bar: codes/indices bit-exact; every float output within
+|y_gpu - y_oracle| <= 2e-3 * sum_k |w_nk x_k| + 1e-5 (y_oracle unrounded fp64).
+Sizes run from ragged tails and multi-tile cases the oracle finishes in
+seconds up to the full workload shapes, in the launch shapes the bench uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_verify_amd as svq
+from speculative_verify_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS = 2e-3, 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    svq.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.bfloat16).double().cpu().numpy()
+
+
+def check_close(y_gpu: np.ndarray, y: np.ndarray, a: np.ndarray, what: str):
+    err = np.abs(y_gpu - y)
+    tol = REL * a + ABS
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside bound; worst ratio "
+                           f"{(err / tol).max():.3g} at {np.unravel_index((err / tol).argmax(), err.shape)}")
+    return float((err / tol).max())
+
+
+def run_gemv_w4a16(codes, scales, x):
+    N, K = codes.shape
+    blob = dev(svq.pack_int4_grouped(codes, scales))
+    y = torch.empty(N, dtype=torch.int16, device="cuda")
+    svq.gemv_w4a16(blob, dev(x), y, N, K)
+    torch.cuda.synchronize()
+    return bf16_host(y)
+
+
+def run_gemv_binplane(signs, alpha, x):
+    P, N, K = signs.shape
+    blob = dev(svq.pack_binary_planes(signs, alpha))
+    y = torch.empty(N, dtype=torch.int16, device="cuda")
+    svq.gemv_binplane(blob, dev(x), y, N, K, P)
+    torch.cuda.synchronize()
+    return bf16_host(y)
+
+
+def run_gemm_w4a16(codes, scales, X):
+    N, K = codes.shape
+    M = X.shape[0]
+    blob = dev(svq.pack_int4_grouped(codes, scales))
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    svq.gemm_smallm_w4a16(blob, dev(X), Y, M, N, K)
+    torch.cuda.synchronize()
+    return bf16_host(Y)
+
+
+def run_gemm_binplane(signs, alpha, X):
+    P, N, K = signs.shape
+    M = X.shape[0]
+    blob = dev(svq.pack_binary_planes(signs, alpha))
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    svq.gemm_smallm_binplane(blob, dev(X), Y, M, N, K, P)
+    torch.cuda.synchronize()
+    return bf16_host(Y)
+
+
+def run_lmhead(codes, scales, X, row_ids=None, blob=None):
+    N, K = codes.shape
+    M = X.shape[0]
+    if blob is None:
+        blob = dev(svq.pack_int4_grouped(codes, scales))
+    idx = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    mx = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    svq.lmhead_argmax(blob, dev(X), M, N, K, idx, mx, ws,
+                      row_ids=None if row_ids is None else dev(row_ids))
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), mx.double().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# W4A16 mat-vec (M = 1)
+
+@pytest.mark.parametrize("case,seed", [(synth.TINY_W4A16, 0), (synth.TINY_W4A16, 1),
+                                       (synth.DECODE_W4A16, 0), (synth.DECODE_W4A16, 2)])
+def test_gemv_w4a16_configs(case, seed):
+    codes, scales, x = synth.make_w4a16(case, seed)
+    y, a = oracle.linear_w4a16(codes, scales, x)
+    print(f"gemv_w4a16 {case.name} seed={seed}", flush=True)
+    check_close(run_gemv_w4a16(codes, scales, x), y[0], a[0], case.name)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (17, 128), (100, 256), (1000, 384), (333, 1152), (2049, 2048),
+                                 (77, 8192), (4001, 4096)])
+def test_gemv_w4a16_ragged(N, K):
+    rng = np.random.default_rng(N + K)
+    codes, scales = synth.int4_weights(rng, N, K)
+    x = synth.activations(rng, 1, K)
+    y, a = oracle.linear_w4a16(codes, scales, x)
+    check_close(run_gemv_w4a16(codes, scales, x), y[0], a[0], f"N={N} K={K}")
+
+
+def test_gemv_w4a16_onehot_unit_scale_is_exact():
+    # s = 1, x = e_k: y[n] = c[n][k] exactly, for every k position of two tiles.
+    N, K = 40, 256
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    scales = np.full((N, K // 128), 0x3F80, np.uint16)
+    blob = dev(svq.pack_int4_grouped(codes, scales))
+    y = torch.empty(N, dtype=torch.int16, device="cuda")
+    for k in range(K):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3F80
+        svq.gemv_w4a16(blob, dev(x), y, N, K)
+        assert np.array_equal(bf16_host(y), codes[:, k].astype(np.float64)), k
+
+
+# ---------------------------------------------------------------------------
+# Binary-plane mat-vec (M = 1)
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gemv_binplane_config(seed):
+    case = synth.DECODE_BINPLANE
+    signs, alpha, x = synth.make_binplane(case, seed)
+    y, a = oracle.linear_binplane(signs, alpha, x)
+    print(f"gemv_binplane {case.name} seed={seed}", flush=True)
+    check_close(run_gemv_binplane(signs, alpha, x), y[0], a[0], case.name)
+
+
+@pytest.mark.parametrize("N,K,P", [(1, 128, 1), (23, 256, 2), (300, 384, 3), (129, 512, 4), (77, 1024, 5),
+                                   (64, 2048, 6), (1500, 4096, 3), (45, 6144, 3)])
+def test_gemv_binplane_ragged(N, K, P):
+    rng = np.random.default_rng(N + K + P)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+    x = synth.activations(rng, 1, K)
+    y, a = oracle.linear_binplane(signs, alpha, x)
+    check_close(run_gemv_binplane(signs, alpha, x), y[0], a[0], f"N={N} K={K} P={P}")
+
+
+def test_gemv_binplane_onehot_unit_plane_is_exact():
+    N, K = 20, 256
+    rng = np.random.default_rng(6)
+    signs, _ = synth.binplane_weights(rng, N, K, P=1)
+    alpha = np.full((1, N, K // 128), 0x3C00, np.uint16)
+    blob = dev(svq.pack_binary_planes(signs, alpha))
+    y = torch.empty(N, dtype=torch.int16, device="cuda")
+    for k in range(K):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3F80
+        svq.gemv_binplane(blob, dev(x), y, N, K, 1)
+        assert np.array_equal(bf16_host(y), signs[0, :, k].astype(np.float64)), k
+
+
+def test_three_planes_match_int4_on_odd_codes_across_kernels():
+    rng = np.random.default_rng(8)
+    N, K = 500, 1024
+    codes = (2 * rng.integers(-4, 4, size=(N, K)) + 1).astype(np.int8)
+    _, scales = synth.int4_weights(rng, N, K)
+    s = synth.bf16_bits_to_f32(scales)
+    alpha = synth.f32_to_f16_bits(np.stack([4 * s, 2 * s, s]))
+    c = codes.astype(np.int64)
+    b1 = np.where(c > 0, 1, -1)
+    b2 = np.where(c - 4 * b1 > 0, 1, -1)
+    signs = np.stack([b1, b2, c - 4 * b1 - 2 * b2]).astype(np.int8)
+    x = synth.activations(rng, 1, K)
+    y, a = oracle.linear_w4a16(codes, scales, x)
+    check_close(run_gemv_w4a16(codes, scales, x), y[0], a[0], "int4 gemv")
+    check_close(run_gemv_binplane(signs, alpha, x), y[0], a[0], "binplane gemv")
+    X = synth.activations(rng, 16, K)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    check_close(run_gemm_w4a16(codes, scales, X), Y, A, "int4 gemm")
+    check_close(run_gemm_binplane(signs, alpha, X), Y, A, "binplane gemm")
+
+
+# ---------------------------------------------------------------------------
+# Verify-block GEMMs (M <= 16)
+
+@pytest.mark.parametrize("case", synth.VERIFY_W4A16, ids=lambda c: c.name)
+def test_gemm_w4a16_configs(case):
+    codes, scales, X = synth.make_w4a16(case, 0)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    print(f"gemm_w4a16 {case.name}", flush=True)
+    check_close(run_gemm_w4a16(codes, scales, X), Y, A, case.name)
+
+
+@pytest.mark.parametrize("case", synth.VERIFY_BINPLANE, ids=lambda c: c.name)
+def test_gemm_binplane_configs(case):
+    signs, alpha, X = synth.make_binplane(case, 0)
+    Y, A = oracle.linear_binplane(signs, alpha, X)
+    print(f"gemm_binplane {case.name}", flush=True)
+    check_close(run_gemm_binplane(signs, alpha, X), Y, A, case.name)
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_gemm_m_sweep_and_rows_match_gemv(M):
+    rng = np.random.default_rng(100 + M)
+    N, K = 150, 640
+    codes, scales = synth.int4_weights(rng, N, K)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=3)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    Yg = run_gemm_w4a16(codes, scales, X)
+    check_close(Yg, Y, A, f"gemm w4a16 M={M}")
+    Yb, Ab = oracle.linear_binplane(signs, alpha, X)
+    check_close(run_gemm_binplane(signs, alpha, X), Yb, Ab, f"gemm binplane M={M}")
+    # every row of the block meets the bound against the M = 1 result of that row
+    for m in range(M):
+        y1, a1 = oracle.linear_w4a16(codes, scales, X[m:m + 1])
+        check_close(Yg[m], y1[0], a1[0], f"row {m}")
+
+
+def test_gemm_onehot_unit_scale_is_exact():
+    # Row m of X is e_{k_m}; Y[m][n] = c[n][k_m] exactly (checks both MFMA operand layouts).
+    N, K, M = 48, 256, 16
+    rng = np.random.default_rng(9)
+    codes = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    scales = np.full((N, K // 128), 0x3F80, np.uint16)
+    signs, _ = synth.binplane_weights(rng, N, K, P=1)
+    alpha = np.full((1, N, K // 128), 0x3C00, np.uint16)
+    blob = dev(svq.pack_int4_grouped(codes, scales))
+    bblob = dev(svq.pack_binary_planes(signs, alpha))
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    for base in range(0, K, M):
+        ks = [(base + 5 * m) % K for m in range(M)]
+        X = np.zeros((M, K), np.uint16)
+        X[np.arange(M), ks] = 0x3F80
+        svq.gemm_smallm_w4a16(blob, dev(X), Y, M, N, K)
+        assert np.array_equal(bf16_host(Y), codes[:, ks].T.astype(np.float64)), base
+        svq.gemm_smallm_binplane(bblob, dev(X), Y, M, N, K, 1)
+        assert np.array_equal(bf16_host(Y), signs[0][:, ks].T.astype(np.float64)), base
+
+
+# ---------------------------------------------------------------------------
+# Output rounding and accumulation quality
+
+def bf16_rne_candidates(v: np.ndarray, slack: np.ndarray):
+    """The bf16 value(s) a correctly rounded result may take for exact v > 0."""
+    e = np.floor(np.log2(v))
+    ulp = np.exp2(e - 7)
+    lo = np.floor(v / ulp) * ulp
+    hi = lo + ulp
+    mid = lo + ulp / 2
+    even_lo = (np.floor(v / ulp) % 2) == 0
+    pick = np.where(v < mid, lo, np.where(v > mid, hi, np.where(even_lo, lo, hi)))
+    either = np.abs(v - mid) <= slack
+    return pick, lo, hi, either
+
+
+@pytest.mark.parametrize("kind", ["w4a16_gemv", "w4a16_gemm", "binplane_gemv", "binplane_gemm"])
+def test_sign_coherent_outputs_are_correctly_rounded(kind):
+    # x > 0 and every weight positive: |y| = sum |w x|.  The result must be the
+    # bf16 round-to-nearest-even of the exact sum (either neighbour only when the
+    # exact sum lies within 1e-5 * |y| of a rounding midpoint).
+    rng = np.random.default_rng(10)
+    N, K, M = 256, 4096, 16
+    X = synth.f32_to_bf16_bits(np.abs(rng.standard_normal((M, K))).astype(np.float32) + 0.01)
+    if kind.startswith("w4a16"):
+        codes = np.full((N, K), 7, np.int8)
+        codes[::3] = 5
+        _, scales = synth.int4_weights(rng, N, K)
+        Y, A = oracle.linear_w4a16(codes, scales, X)
+        got = run_gemv_w4a16(codes, scales, X[:1])[None] if kind.endswith("gemv") else \
+            run_gemm_w4a16(codes, scales, X)
+    else:
+        signs = np.ones((3, N, K), np.int8)
+        _, alpha = synth.binplane_weights(rng, N, K, P=3)
+        Y, A = oracle.linear_binplane(signs, alpha, X)
+        got = run_gemv_binplane(signs, alpha, X[:1])[None] if kind.endswith("gemv") else \
+            run_gemm_binplane(signs, alpha, X)
+    Y = Y[: got.shape[0]]
+    pick, lo, hi, either = bf16_rne_candidates(Y, 4e-5 * Y)
+    ok = (got == pick) | (either & ((got == lo) | (got == hi)))
+    assert ok.all(), f"{(~ok).sum()} outputs not correctly rounded"
+
+
+def test_results_are_bitwise_deterministic():
+    case = synth.DECODE_W4A16
+    codes, scales, x = synth.make_w4a16(case, 3)
+    a = run_gemv_w4a16(codes, scales, x)
+    b = run_gemv_w4a16(codes, scales, x)
+    assert np.array_equal(a, b)
+    X = synth.activations(np.random.default_rng(4), 16, case.K)
+    assert np.array_equal(run_gemm_w4a16(codes, scales, X), run_gemm_w4a16(codes, scales, X))
+
+
+# ---------------------------------------------------------------------------
+# LM head with fused argmax
+
+@pytest.mark.parametrize("case", synth.LMHEAD, ids=lambda c: c.name)
+def test_lmhead_planted_configs(case):
+    print(f"lmhead {case.name}: generating", flush=True)
+    codes, scales, X, rows = synth.make_lmhead(case, 0)
+    r = oracle.argmax_w4a16(codes, scales, X)
+    assert np.array_equal(r["idx"], rows.astype(np.int32))
+    tol = REL * r["amax"] + ABS
+    assert np.all(r["zmax"] - r["zsecond"] > 10 * tol), "planted margin too small"
+    print(f"lmhead {case.name}: running", flush=True)
+    idx, mx = run_lmhead(codes, scales, X)
+    assert np.array_equal(idx, rows.astype(np.int32))
+    check_close(mx, r["zmax"], r["amax"], "maxlogit")
+
+
+def test_lmhead_row_ids_and_ties():
+    rng = np.random.default_rng(21)
+    case = synth.Case("t", "lmhead", 4, 3000, 1024)
+    codes, scales, X, rows = synth.make_lmhead(case, 21)
+    # Copy each planted row to a lower index in a different tile: the tie goes low.
+    for m in range(case.M):
+        dst = int(rng.integers(0, rows[m])) if rows[m] > 0 else None
+        if dst is not None and dst not in rows:
+            codes[dst] = codes[rows[m]]
+            scales[dst] = scales[rows[m]]
+    rid = rng.permutation(200000)[: case.N].astype(np.int32)
+    r = oracle.argmax_w4a16(codes, scales, X, row_ids=rid)
+    idx, mx = run_lmhead(codes, scales, X, row_ids=rid)
+    assert np.array_equal(idx, r["out"])
+    for m in range(case.M):  # single-row queries take the M = 1 path
+        i1, _ = run_lmhead(codes, scales, X[m:m + 1], row_ids=rid)
+        assert i1[0] == r["out"][m]
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_lmhead_unplanted_pick_is_a_valid_maximum(M):
+    # Without planting, near-ties are possible: any index whose exact logit is
+    # within the two tolerances of the exact maximum is a correct greedy pick.
+    rng = np.random.default_rng(30 + M)
+    N, K = 20000, 2048
+    codes, scales = synth.int4_weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    Z, A = oracle.linear_w4a16(codes, scales, X)
+    idx, mx = run_lmhead(codes, scales, X)
+    for m in range(M):
+        best = int(np.argmax(Z[m]))
+        tol = lambda n: REL * A[m, n] + ABS
+        g = int(idx[m])
+        assert Z[m, g] >= Z[m, best] - tol(g) - tol(best), (m, g, best)
+        assert abs(mx[m] - Z[m, g]) <= tol(g)
+
+
+def test_lmhead_single_row_and_ragged_vocab():
+    rng = np.random.default_rng(40)
+    for N in (1, 15, 17, 1001):
+        codes, scales = synth.int4_weights(rng, N, 256)
+        X = synth.activations(rng, 3, 256)
+        r = oracle.argmax_w4a16(codes, scales, X)
+        idx, mx = run_lmhead(codes, scales, X)
+        Z, A = oracle.linear_w4a16(codes, scales, X)
+        for m in range(3):
+            g = int(idx[m])
+            assert 0 <= g < N
+            assert Z[m, g] >= r["zmax"][m] - 2 * (REL * A[m].max() + ABS)
