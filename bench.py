@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the low-bit weight-streaming hot path on one MI355X.
+
+One step = one pass of every device entry point at its workload shape, each
+on its own freshly drawn weights:
+
+  gemv_w4a16            M=1  K=4096 N=12288        (decode, W4A16 group 128)
+  gemv_binplane         M=1  K=4096 N=12288 P=3    (decode, sign planes)
+  gemm_smallm_w4a16     M=16 K=4096 N=4096, 12288  (verify block)
+  gemm_smallm_binplane  M=16 K=4096 N=4096, 12288  (verify block, P=3)
+  lmhead_argmax         M=1, 16  K=4096 N=32768 (trimmed), 248320 (full)
+
+The metric is weight bytes streamed per second (packed weights + scales +
+activations + outputs, the algorithmic bytes of each call) over the whole
+step.  Each step reads ~1.3 GB of distinct weights, far more than the 256 MB
+last-level cache, so every call streams its weights from HBM.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one
+GPU's share.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+K = 4096
+G = 128
+
+
+def alg_bytes_linear(kind: str, M: int, N: int, P: int = 0) -> int:
+    """Algorithmic bytes of one call: packed weights + scales + X in + Y out."""
+    if kind == "w4a16":
+        w = N * K // 2 + N * (K // G) * 2
+    else:
+        w = N * K // 8 * P + P * N * (K // G) * 2
+    return w + M * K * 2 + M * N * 2
+
+
+def alg_bytes_head(M: int, N: int) -> int:
+    """Packed weights + scales + X in + (int32 index, fp32 max) per row out."""
+    return N * K // 2 + N * (K // G) * 2 + M * K * 2 + M * 8
+
+
+def build_step(svq, synth, torch):
+    """Allocate every call's inputs on the device; return [(name, bytes, fn)]."""
+    calls = []
+    seed = [100]
+
+    def nxt():
+        seed[0] += 1
+        return seed[0]
+
+    def lin(kind, M, N, P=0):
+        if kind == "w4a16":
+            blob = synth.device_int4_blob(N, K, nxt())
+        else:
+            blob = synth.device_binplane_blob(N, K, P, nxt())
+        X = synth.device_activations(M, K, nxt()).view(torch.int16)
+        Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        if kind == "w4a16" and M == 1:
+            fn = lambda: svq.gemv_w4a16(blob, X, Y, N, K)
+            name = f"gemv_w4a16_m1_n{N}"
+        elif kind == "w4a16":
+            fn = lambda: svq.gemm_smallm_w4a16(blob, X, Y, M, N, K)
+            name = f"gemm_smallm_w4a16_m{M}_n{N}"
+        elif M == 1:
+            fn = lambda: svq.gemv_binplane(blob, X, Y, N, K, P)
+            name = f"gemv_binplane_p{P}_m1_n{N}"
+        else:
+            fn = lambda: svq.gemm_smallm_binplane(blob, X, Y, M, N, K, P)
+            name = f"gemm_smallm_binplane_p{P}_m{M}_n{N}"
+        calls.append((name, alg_bytes_linear(kind, M, N, P), fn))
+
+    heads = {}
+
+    def head(M, N):
+        if N not in heads:
+            heads[N] = synth.device_int4_blob(N, K, nxt())
+        blob = heads[N]
+        X = synth.device_activations(M, K, nxt()).view(torch.int16)
+        idx = torch.empty(M, dtype=torch.int32, device="cuda")
+        mx = torch.empty(M, dtype=torch.float32, device="cuda")
+        ws = torch.empty(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        fn = lambda: svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
+        calls.append((f"lmhead_argmax_m{M}_n{N}", alg_bytes_head(M, N), fn))
+
+    # Order: the full head (524 MB) sits between uses of anything small, so no
+    # call finds its weights in the last-level cache from the previous step.
+    head(1, 248320)
+    lin("w4a16", 1, 12288)
+    lin("binplane", 1, 12288, 3)
+    lin("w4a16", 16, 4096)
+    lin("w4a16", 16, 12288)
+    lin("binplane", 16, 4096, 3)
+    lin("binplane", 16, 12288, 3)
+    head(1, 32768)
+    head(16, 248320)
+    head(16, 32768)
+    return calls
+
+
+def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20):
+    """GB/s of a plain 16-byte streaming read over `nbytes` (HBM ceiling)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        svq.svq_stream_read(src, nbytes, sink)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        svq.svq_stream_read(src, nbytes, sink)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    del src
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the same step (weight GB/s)."""
+    import numpy as np
+
+    import oracle
+    from speculative_verify_amd import synth
+
+    shapes = [("w4a16", 1, 12288, 0), ("binplane", 1, 12288, 3), ("w4a16", 16, 4096, 0),
+              ("w4a16", 16, 12288, 0), ("binplane", 16, 4096, 3), ("binplane", 16, 12288, 3),
+              ("head", 1, 248320, 0), ("head", 1, 32768, 0), ("head", 16, 248320, 0),
+              ("head", 16, 32768, 0)]
+    rng = np.random.default_rng(7)
+
+    def run(frac):
+        nbytes, secs = 0, 0.0
+        for kind, M, N, P in shapes:
+            n = max(16, int(N * frac) // 16 * 16)
+            X = synth.activations(rng, M, K)
+            if kind == "binplane":
+                signs, alpha = synth.binplane_weights(rng, n, K, P=P)
+                t0 = time.perf_counter()
+                oracle.linear_binplane(signs, alpha, X)
+                secs += time.perf_counter() - t0
+                nbytes += alg_bytes_linear("binplane", M, n, P)
+            else:
+                codes, scales = synth.int4_weights(rng, n, K)
+                t0 = time.perf_counter()
+                if kind == "head":
+                    oracle.argmax_w4a16(codes, scales, X)
+                    nbytes += alg_bytes_head(M, n)
+                else:
+                    oracle.linear_w4a16(codes, scales, X)
+                    nbytes += alg_bytes_linear("w4a16", M, n)
+                secs += time.perf_counter() - t0
+        return nbytes, secs
+
+    f0 = 1.0 / 64
+    b0, s0 = run(f0)
+    frac = min(1.0, f0 * target_s / max(s0, 1e-3))
+    nbytes, secs = run(frac)
+    return {
+        "value": round(nbytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"each step call on its first {frac:.4%} of output rows (at least 16), "
+                   f"same K, M and value distributions; {nbytes / 1e6:.1f} MB of weights in "
+                   f"{secs:.1f} s of oracle time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share only; --gpus {args.gpus} is not supported "
+              "(the path has no collectives; see the sharding notes in the design document).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import speculative_verify_amd as svq
+    from speculative_verify_amd import synth
+
+    torch.cuda.set_device(0)
+    svq.load()
+    calls = build_step(svq, synth, torch)
+    step_bytes = sum(b for _, b, _ in calls)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for _, _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, (_, _, fn) in enumerate(calls):
+            ev[s][j][0].record()
+            fn()
+            ev[s][j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    kernels = {}
+    for j, (name, nbytes, _) in enumerate(calls):
+        us = sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) * 1e3 / args.steps
+        gbps = nbytes / (us * 1e-6) / 1e9
+        kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(gbps, 1),
+                         "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    dom = max(kernels, key=lambda n: kernels[n]["us"])
+
+    def ratio(a, b):
+        return round(kernels[a]["us"] / kernels[b]["us"], 3)
+
+    result = {
+        "metric": "weight GB/s & % of HBM peak: GEMV M=1, verify GEMM M=16, LM-head+argmax",
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; uniform INT4 codes / Bernoulli sign bits, U(0.005,0.02) bf16 "
+                "scales, fp16 plane scales, N(0,1) bf16 activations)",
+        "config": {
+            "workload": "decode+verify+lmhead step, K=4096, group 128: W4A16 GEMV M1 N12288; "
+                        "binary-plane P3 GEMV M1 N12288; W4A16 and P3 verify GEMM M16 N4096/N12288; "
+                        "W4A16 LM head + argmax M1/M16 N32768 (trimmed) and N248320 (full)",
+            "step_bytes": step_bytes,
+            "frac_hbm_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": kernels[dom]["GBps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": kernels[dom]["frac_hbm_peak"],
+            "traffic": None,
+        },
+        "kernels": kernels,
+        "verify_over_decode_time": {
+            "w4a16_n12288": ratio("gemm_smallm_w4a16_m16_n12288", "gemv_w4a16_m1_n12288"),
+            "binplane_n12288": ratio("gemm_smallm_binplane_p3_m16_n12288", "gemv_binplane_p3_m1_n12288"),
+            "lmhead_n248320": ratio("lmhead_argmax_m16_n248320", "lmhead_argmax_m1_n248320"),
+        },
+    }
+    traffic = load_traffic(dom)
+    if traffic is not None:
+        result["roofline"]["traffic"] = traffic
+    if not args.no_ceiling:
+        result["stream_read_ceiling_GBps"] = round(stream_read_ceiling(svq, torch), 1)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def load_traffic(kernel_name: str):
+    """HBM bytes per launch of `kernel_name` from the committed counter summary,
+    or None when the kernel source changed after the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "speculative_verify_amd", "csrc", "svq.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if t.get("svq_hip_sha256") != digest:
+        return None
+    return t.get("per_launch_bytes", {}).get(kernel_name)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -141,3 +141,50 @@ def make_lmhead(case: Case, seed: int = 0):
     x = activations(rng, case.M, case.K)
     rows = plant_rows(rng, codes, scales, x)
     return codes, scales, x, rows
+
+
+def device_int4_blob(N: int, K: int, seed: int, G: int = GROUP, smin: float = 0.005,
+                     smax: float = 0.02, device: str = "cuda"):
+    """A packed INT4 blob drawn directly on the device (for timing runs).
+
+    Uniform random code bytes give uniform nibbles, i.e. codes uniform in
+    [-8, 7] whatever the byte layout; the scale section gets bf16 values
+    uniform in [smin, smax].  Needs N % 16 == 0 (no padding rows).
+    """
+    assert N % 16 == 0 and K % G == 0
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    code_bytes = N * K // 2
+    blob = torch.empty(code_bytes + N * (K // G) * 2, dtype=torch.uint8, device=device)
+    blob[:code_bytes] = torch.randint(0, 256, (code_bytes,), generator=gen, dtype=torch.uint8,
+                                      device=device)
+    s = torch.empty(N * (K // G), dtype=torch.float32, device=device).uniform_(smin, smax, generator=gen)
+    blob[code_bytes:] = s.to(torch.bfloat16).view(torch.uint8)
+    return blob
+
+
+def device_binplane_blob(N: int, K: int, P: int, seed: int, G: int = GROUP, a1=(0.01, 0.03),
+                         ratio=(0.3, 0.6), device: str = "cuda"):
+    """A packed sign-plane blob drawn on the device: Bernoulli(0.5) sign bits,
+    alpha_1 ~ U(a1), alpha_{p+1} = alpha_p * U(ratio), fp16.  N % 16 == 0."""
+    assert N % 16 == 0 and K % G == 0
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    sign_bytes = N * K // 8 * P
+    ng = K // G
+    blob = torch.empty(sign_bytes + P * N * ng * 2, dtype=torch.uint8, device=device)
+    blob[:sign_bytes] = torch.randint(0, 256, (sign_bytes,), generator=gen, dtype=torch.uint8,
+                                      device=device)
+    a = torch.empty((P, N * ng), dtype=torch.float32, device=device)
+    a[0].uniform_(a1[0], a1[1], generator=gen)
+    for p in range(1, P):
+        a[p] = a[p - 1] * torch.empty(N * ng, device=device).uniform_(ratio[0], ratio[1], generator=gen)
+    blob[sign_bytes:] = a.to(torch.float16).reshape(-1).view(torch.uint8)
+    return blob
+
+
+def device_activations(M: int, K: int, seed: int, device: str = "cuda"):
+    """bf16 activations x ~ N(0, 1), [M][K], drawn on the device."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randn((M, K), generator=gen, device=device).to(torch.bfloat16)
