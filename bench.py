@@ -87,7 +87,7 @@ def build_step(svq, synth, torch):
         X = synth.device_activations(M, K, nxt()).view(torch.int16)
         idx = torch.empty(M, dtype=torch.int32, device="cuda")
         mx = torch.empty(M, dtype=torch.float32, device="cuda")
-        ws = torch.empty(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
         fn = lambda: svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
         calls.append((f"lmhead_argmax_m{M}_n{N}", alg_bytes_head(M, N), fn))
 

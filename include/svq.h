@@ -42,15 +42,19 @@
  *       k = 128*kt + 32*t + 8*q + j (j = 0..7): even j = 2i in bits
  *       [4i, 4i+4), odd j = 2i+1 in bits [16+4i, 20+4i), each nibble
  *       u = c + 8.  Padding rows (n >= N) hold c = 0.
- *     scales: bf16 s[n][g], n < N16 (0 for padding rows), row-major, right
- *       after the codes, i.e. at byte N16 * K / 2.
+ *     scales: right after the codes, i.e. at byte N16 * K / 2: row n < N16
+ *       holds bf16 s[n][g] at entry n*KT4 + g, KT4 = KT rounded up to 4, so
+ *       a lane fetches four groups' scales with one 8-byte load.  Entries
+ *       g >= KT and padding rows are 0.
  *   Binary-plane blob with P planes:
- *     signs: tile (rt, kt) at byte (rt*KT + kt) * 256 * P.  Lane 16*q + r
- *       owns 4*P bytes at 4*P*lane; dword p is plane p for row 16*rt + r at
- *       k = 128*kt + 32*t + 8*q + j: even j = 2i at bit 4t + i, odd j = 2i+1
- *       at bit 16 + 4t + i.  A set bit means b = -1.  Padding rows hold +1.
- *     alphas: fp16 alpha[p][n][g], n < N16 (0 for padding rows), row-major,
- *       right after the signs, i.e. at byte N16 * K / 8 * P.
+ *     signs: tile (rt, kt) at byte (rt*KT + kt) * 256 * P; plane p of the
+ *       tile is the 256 bytes at offset 256*p, in which lane 16*q + r owns
+ *       the dword at 4*lane: plane p, row 16*rt + r, k = 128*kt + 32*t +
+ *       8*q + j: even j = 2i at bit 4t + i, odd j = 2i+1 at bit 16 + 4t + i.
+ *       A set bit means b = -1.  Padding rows hold +1.
+ *     alphas: right after the signs, i.e. at byte N16 * K / 8 * P: fp16
+ *       alpha[p][n][g] at entry (p*N16 + n)*KT4 + g.  Entries g >= KT and
+ *       padding rows are 0.
  */
 #ifndef SVQ_H
 #define SVQ_H
@@ -80,10 +84,10 @@ enum {
 /* Message describing the last error on the calling thread ("" if none). */
 const char* svq_last_error(void);
 
-/* Bytes of a packed INT4 blob: N16*K/2 + N16*(K/G)*2.  0 for bad sizes. */
+/* Bytes of a packed INT4 blob: N16*K/2 + N16*KT4*2.  0 for bad sizes. */
 size_t svq_int4_packed_bytes(int64_t N, int64_t K, int32_t G);
 
-/* Bytes of a packed binary-plane blob: N16*K/8*P + P*N16*(K/G)*2.  0 for bad sizes. */
+/* Bytes of a packed binary-plane blob: N16*K/8*P + P*N16*KT4*2.  0 for bad sizes. */
 size_t svq_binplane_packed_bytes(int64_t N, int64_t K, int32_t G, int32_t P);
 
 /* Workspace bytes that lmhead_argmax needs for M query rows. */
@@ -178,8 +182,12 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
  *   row_ids    NULL or [N] int32 (trimmed row -> token id), 4-byte aligned
  *   argmax, maxlogit  [M], 4-byte aligned
  *   workspace  >= svq_lmhead_workspace_bytes(M) bytes of device memory,
- *              16-byte aligned; needs no initialisation; its contents are
- *              scratch and are overwritten by every call.
+ *              16-byte aligned, all zero before the first call (allocate
+ *              it zeroed).  Every call leaves it zero again, so one
+ *              workspace serves any number of calls of any M.
+ * One launch: each workgroup folds its per-row best (logit, row) into the
+ * workspace with device-scope 64-bit atomic max operations; the last
+ * workgroup to finish reads the result and clears the workspace.
  * Errors: as gemm_smallm_w4a16, plus WORKSPACE.  Calls that overlap in time
  * must not share a workspace.
  */

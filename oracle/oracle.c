@@ -38,14 +38,17 @@
  *     n = 16*rt + r at k = 128*kt + 32*t + 8*q + j, j = 0..7: even j = 2i in
  *     bits [4i, 4i+4), odd j = 2i+1 in bits [16+4i, 20+4i).  A nibble holds
  *     u = c + 8.  Rows n >= N hold c = 0.
- *     Then bf16 scales s[n][g], n < N16 (0 for padded rows), row-major.
+ *     Then bf16 scales: row n (n < N16) holds s[n][g] at entry n*KT4 + g,
+ *     KT4 = KT rounded up to 4; entries g >= KT and padded rows are 0.
  *   Binary-plane blob (P planes).
- *     tile (rt, kt) starts at byte (rt*KT + kt)*256*P; lane = 16*q + r owns
- *     4*P bytes at 4*P*lane, dword p at 4*P*lane + 4*p.  That dword holds the
- *     signs of plane p, row n = 16*rt + r, k = 128*kt + 32*t + 8*q + j:
+ *     tile (rt, kt) starts at byte (rt*KT + kt)*256*P; plane p of the tile
+ *     occupies bytes [256*p, 256*p + 256), where lane = 16*q + r owns the
+ *     dword at 256*p + 4*lane.  That dword holds the signs of plane p, row
+ *     n = 16*rt + r, k = 128*kt + 32*t + 8*q + j:
  *     even j = 2i at bit 4t + i, odd j = 2i+1 at bit 16 + 4t + i.  Bit set
  *     means b = -1.  Rows n >= N hold b = +1.
- *     Then fp16 alpha[p][n][g], n < N16 (0 for padded rows), row-major.
+ *     Then fp16 alphas: alpha[p][n][g] at entry (p*N16 + n)*KT4 + g; entries
+ *     g >= KT and padded rows are 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -237,8 +240,8 @@ static void or_dword(uint8_t* blob, int64_t byte_off, uint32_t v) {
 }
 
 int64_t oracle_int4_blob_bytes(int64_t N, int64_t K) {
-  const int64_t N16 = (N + 15) / 16 * 16;
-  return N16 * (K / 2) + N16 * (K / 128) * 2;
+  const int64_t N16 = (N + 15) / 16 * 16, KT4 = (K / 128 + 3) / 4 * 4;
+  return N16 * (K / 2) + N16 * KT4 * 2;
 }
 
 int oracle_pack_int4(const int8_t* codes, const uint16_t* scales, int64_t N,
@@ -259,19 +262,19 @@ int oracle_pack_int4(const int8_t* codes, const uint16_t* scales, int64_t N,
       or_dword(blob, off, u << bit);
     }
   }
-  const int64_t soff = (N16 / 16) * KT * 1024;
+  const int64_t soff = (N16 / 16) * KT * 1024, KT4 = (KT + 3) / 4 * 4;
   for (int64_t n = 0; n < N16; ++n)
     for (int64_t g = 0; g < ng; ++g) {
       const uint16_t s = n < N ? scales[n * ng + g] : 0;
-      blob[soff + 2 * (n * ng + g)] = (uint8_t)(s & 0xff);
-      blob[soff + 2 * (n * ng + g) + 1] = (uint8_t)(s >> 8);
+      blob[soff + 2 * (n * KT4 + g)] = (uint8_t)(s & 0xff);
+      blob[soff + 2 * (n * KT4 + g) + 1] = (uint8_t)(s >> 8);
     }
   return 0;
 }
 
 int64_t oracle_binplane_blob_bytes(int64_t N, int64_t K, int64_t P) {
-  const int64_t N16 = (N + 15) / 16 * 16;
-  return N16 * (K / 8) * P + P * N16 * (K / 128) * 2;
+  const int64_t N16 = (N + 15) / 16 * 16, KT4 = (K / 128 + 3) / 4 * 4;
+  return N16 * (K / 8) * P + P * N16 * KT4 * 2;
 }
 
 int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
@@ -288,17 +291,17 @@ int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
         const int64_t rt = n / 16, r = n % 16, kt = k / 128, kk = k % 128;
         const int64_t t = kk / 32, q = (kk % 32) / 8, j = kk % 8;
         const int64_t lane = 16 * q + r;
-        const int64_t off = (rt * KT + kt) * 256 * P + 4 * P * lane + 4 * p;
+        const int64_t off = (rt * KT + kt) * 256 * P + 256 * p + 4 * lane;
         const int bit = (j % 2) ? 16 + 4 * (int)t + (int)(j / 2)
                                 : 4 * (int)t + (int)(j / 2);
         or_dword(blob, off, 1u << bit);
       }
-  const int64_t aoff = (N16 / 16) * KT * 256 * P;
+  const int64_t aoff = (N16 / 16) * KT * 256 * P, KT4 = (KT + 3) / 4 * 4;
   for (int64_t p = 0; p < P; ++p)
     for (int64_t n = 0; n < N16; ++n)
       for (int64_t g = 0; g < ng; ++g) {
         const uint16_t a = n < N ? alpha[(p * N + n) * ng + g] : 0;
-        const int64_t e = (p * N16 + n) * ng + g;
+        const int64_t e = (p * N16 + n) * KT4 + g;
         blob[aoff + 2 * e] = (uint8_t)(a & 0xff);
         blob[aoff + 2 * e + 1] = (uint8_t)(a >> 8);
       }

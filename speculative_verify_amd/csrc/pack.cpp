@@ -57,13 +57,13 @@ extern "C" {
 size_t svq_int4_packed_bytes(int64_t N, int64_t K, int32_t G) {
   if (N < 1 || G != SVQ_GROUP || K < SVQ_GROUP || K % SVQ_GROUP) return 0;
   const int64_t N16 = svq::round16(N);
-  return (size_t)(N16 * (K / 2) + N16 * (K / G) * 2);
+  return (size_t)(N16 * (K / 2) + N16 * svq::round4(K / G) * 2);
 }
 
 size_t svq_binplane_packed_bytes(int64_t N, int64_t K, int32_t G, int32_t P) {
   if (N < 1 || G != SVQ_GROUP || K < SVQ_GROUP || K % SVQ_GROUP || P < 1 || P > SVQ_MAX_P) return 0;
   const int64_t N16 = svq::round16(N);
-  return (size_t)(N16 * (K / 8) * P + (int64_t)P * N16 * (K / G) * 2);
+  return (size_t)(N16 * (K / 8) * P + (int64_t)P * N16 * svq::round4(K / G) * 2);
 }
 
 int pack_int4_grouped(const int8_t* codes, const uint16_t* scales_bf16, int64_t N, int64_t K,
@@ -96,9 +96,12 @@ int pack_int4_grouped(const int8_t* codes, const uint16_t* scales_bf16, int64_t 
         }
       }
   });
-  uint8_t* s = packed + N16 * (K / 2);
-  std::memcpy(s, scales_bf16, (size_t)(N * ng * 2));
-  std::memset(s + N * ng * 2, 0, (size_t)((N16 - N) * ng * 2));
+  // Scale rows are KT4 = round4(K/G) entries long; the tail entries and the
+  // padding rows are zero.
+  uint16_t* s = reinterpret_cast<uint16_t*>(packed + N16 * (K / 2));
+  const int64_t KT4 = svq::round4(ng);
+  std::memset(s, 0, (size_t)(N16 * KT4 * 2));
+  for (int64_t n = 0; n < N; ++n) std::memcpy(s + n * KT4, scales_bf16 + n * ng, (size_t)(ng * 2));
   return SVQ_OK;
 }
 
@@ -127,7 +130,9 @@ int unpack_int4_grouped(const uint8_t* packed, int64_t N, int64_t K, int32_t G, 
         }
       }
   });
-  std::memcpy(scales_bf16, packed + N16 * (K / 2), (size_t)(N * ng * 2));
+  const uint16_t* s = reinterpret_cast<const uint16_t*>(packed + N16 * (K / 2));
+  const int64_t KT4 = svq::round4(ng);
+  for (int64_t n = 0; n < N; ++n) std::memcpy(scales_bf16 + n * ng, s + n * KT4, (size_t)(ng * 2));
   return SVQ_OK;
 }
 
@@ -160,16 +165,17 @@ int pack_binary_planes(const int8_t* signs, const uint16_t* alpha_f16, int64_t N
                   w |= (uint32_t)(b[32 * t + 2 * i + 1] < 0) << (16 + 4 * t + i);
                 }
             }
-            store_u32(tile + 4 * P * lane + 4 * p, w);
+            store_u32(tile + 256 * p + 4 * lane, w);
           }
         }
       }
   });
-  uint8_t* a = packed + N16 * (K / 8) * P;
-  for (int p = 0; p < P; ++p) {
-    std::memcpy(a + (int64_t)p * N16 * ng * 2, alpha_f16 + (int64_t)p * N * ng, (size_t)(N * ng * 2));
-    std::memset(a + ((int64_t)p * N16 + N) * ng * 2, 0, (size_t)((N16 - N) * ng * 2));
-  }
+  uint16_t* a = reinterpret_cast<uint16_t*>(packed + N16 * (K / 8) * P);
+  const int64_t KT4 = svq::round4(ng);
+  std::memset(a, 0, (size_t)(P * N16 * KT4 * 2));
+  for (int p = 0; p < P; ++p)
+    for (int64_t n = 0; n < N; ++n)
+      std::memcpy(a + ((int64_t)p * N16 + n) * KT4, alpha_f16 + ((int64_t)p * N + n) * ng, (size_t)(ng * 2));
   return SVQ_OK;
 }
 
@@ -189,7 +195,7 @@ int unpack_binary_planes(const uint8_t* packed, int64_t N, int64_t K, int32_t G,
           const int64_t n = rt * 16 + r;
           if (n >= N) continue;
           for (int p = 0; p < P; ++p) {
-            const uint32_t w = load_u32(tile + 4 * P * lane + 4 * p);
+            const uint32_t w = load_u32(tile + 256 * p + 4 * lane);
             int8_t* b = signs + ((int64_t)p * N + n) * K + kt * 128 + q * 8;
             for (int t = 0; t < 4; ++t)
               for (int i = 0; i < 4; ++i) {
@@ -200,9 +206,11 @@ int unpack_binary_planes(const uint8_t* packed, int64_t N, int64_t K, int32_t G,
         }
       }
   });
-  const uint8_t* a = packed + N16 * (K / 8) * P;
+  const uint16_t* a = reinterpret_cast<const uint16_t*>(packed + N16 * (K / 8) * P);
+  const int64_t KT4 = svq::round4(ng);
   for (int p = 0; p < P; ++p)
-    std::memcpy(alpha_f16 + (int64_t)p * N * ng, a + (int64_t)p * N16 * ng * 2, (size_t)(N * ng * 2));
+    for (int64_t n = 0; n < N; ++n)
+      std::memcpy(alpha_f16 + ((int64_t)p * N + n) * ng, a + ((int64_t)p * N16 + n) * KT4, (size_t)(ng * 2));
   return SVQ_OK;
 }
 

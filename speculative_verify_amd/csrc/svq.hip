@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <cfloat>
 #include <climits>
 #include <cstdint>
@@ -56,8 +57,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 constexpr uint32_t kInt4Magic = 0x43004300u;  // bf16 pair (128, 128)
 constexpr float kInt4Bias = 136.0f;           // 128 + 8: decoded value = 136 + c
 constexpr uint32_t kOnePair = 0x3F803F80u;    // bf16 pair (1, 1)
-constexpr int kMaxWaves = 16;
-constexpr int kLmheadMaxWg = 1024;
 
 struct ArgBest {
   float v;
@@ -81,14 +80,36 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// bf16 pair (136 + c_even, 136 + c_odd) for pair i (k = 2i, 2i+1) of a code dword.
-__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i) {
-  return ((w >> (4 * i)) & 0x000F000Fu) | kInt4Magic;
+// v_and_or_b32 with the mask in an SGPR and the OR constant in a VGPR: the
+// VOP3 encoding takes no literal, so the compiler would otherwise split it
+// into a literal AND and a literal OR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(orv));
+  return d;
 }
 
-// bf16 pair (b_even, b_odd) in {-1, +1} for pair ip = 4t + i of a sign dword.
-__device__ __forceinline__ uint32_t sign_pair(uint32_t w, int ip) {
-  return ((w << (15 - ip)) & 0x80008000u) | kOnePair;
+// bf16 pair (136 + c_even, 136 + c_odd) for pair i (k = 2i, 2i+1) of a code
+// dword; `magic` holds kInt4Magic in a VGPR.
+__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i, uint32_t magic) {
+  return and_or(w >> (4 * i), 0x000F000Fu, magic);
+}
+
+// bf16 pair (b_even, b_odd) in {-1, +1} for pair ip = 4t + i of a sign dword;
+// `one` holds kOnePair in a VGPR.
+__device__ __forceinline__ uint32_t sign_pair(uint32_t w, int ip, uint32_t one) {
+  return and_or(w << (15 - ip), 0x80008000u, one);
+}
+
+// Sum over the four lanes r, r+16, r+32, r+48 of a wave (the q index), via
+// the gfx950 lane-swap instructions (no LDS traffic).
+__device__ __forceinline__ float sum_over_q(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  const uint32_t ua = __float_as_uint(a);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+  return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
 }
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -103,24 +124,69 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t* a, const uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Activation staging: lane (q, r) keeps the bf16 pairs of row `row` at
-// k = 128g + 32t + 8q + [0, 8) for the wave's GPW groups: xp[gi][4t + i] is
-// the pair (k, k+1), k = 128g + 32t + 8q + 2i.  Zero outside [0, KT) / rows.
+// Activation staging: lane (q, r) keeps the bf16 pairs of activation row
+// `row` at k = 128g + 32t + 8q + [0, 8) for the wave's GPW groups:
+// xp[gi][4t + i] is the pair (k, k+1), k = 128g + 32t + 8q + 2i.  Rows >= M
+// and groups >= KT read a clamped (valid) address; mask_x_pairs() zeroes
+// them afterwards, so the loads stay branch-free and can be issued before
+// the weight prefetch while their consumers wait until after it.
 template <int GPW>
-__device__ __forceinline__ void load_x_pairs(const uint32_t* __restrict__ xrow, bool row_ok, int g0, int KT, int q,
+__device__ __forceinline__ void load_x_pairs(const uint32_t* __restrict__ X, int row, int M, int g0, int KT, int q,
                                              uint32_t (&xp)[GPW][16]) {
+  const uint32_t* xrow = X + (size_t)min(row, M - 1) * KT * 64;
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int g = g0 + gi;
+  for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row_ok && g < KT) v = *reinterpret_cast<const uint4*>(xrow + 64 * g + 16 * t + 4 * q);
+      const uint4 v = *reinterpret_cast<const uint4*>(xrow + 64 * min(g0 + gi, KT - 1) + 16 * t + 4 * q);
       xp[gi][4 * t + 0] = v.x;
       xp[gi][4 * t + 1] = v.y;
       xp[gi][4 * t + 2] = v.z;
       xp[gi][4 * t + 3] = v.w;
     }
+}
+
+template <int GPW>
+__device__ __forceinline__ void mask_x_pairs(int row, int M, int g0, int KT, uint32_t (&xp)[GPW][16]) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const bool live = row < M && g0 + gi < KT;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xp[gi][j] = live ? xp[gi][j] : 0u;
+  }
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Activation staging for the M = 1 kernels.  The 16 lanes of a row q all
+// need the same 16 pairs (their k sub-range), so instead of loading them 16
+// times over, lane (q, r) loads only the pair with (t, i) = (r/4, r%4) -- a
+// wave reads each of a group's 64 pairs exactly once -- and DPP row_newbcast
+// then copies pair j of the row to every lane of the row.
+template <int GPW>
+__device__ __forceinline__ void load_x_own(const uint32_t* __restrict__ xw, int g0, int KT, int q, int r,
+                                           uint32_t (&xo)[GPW]) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+    xo[gi] = xw[64 * min(g0 + gi, KT - 1) + 16 * (r >> 2) + 4 * q + (r & 3)];
+}
+
+template <int GPW>
+__device__ __forceinline__ void expand_x(const uint32_t (&xo)[GPW], int g0, int KT, uint32_t (&xp)[GPW][16]) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const bool live = g0 + gi < KT;
+    static_for<0, 16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const uint32_t v = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x150 + j, 0xF, 0xF, false);  // row_newbcast:j
+      xp[gi][j] = live ? v : 0u;
+    });
   }
 }
 
@@ -137,28 +203,161 @@ __device__ __forceinline__ void lane_group_sums(const uint32_t (&xp)[GPW][16], f
 }
 
 // ---------------------------------------------------------------------------
-// M = 1 mat-vec cores.  Each returns the lane's partial sum for row r over its
-// k sub-ranges of the wave's groups.
+// Tile loaders (global -> registers).  Weights and scales are read through
+// buffer resources: an access at an offset past the section's end returns
+// zero without touching memory.  Tiles past the workgroup's last tile (the
+// pipeline's tail) and groups past K (a wave's unused slots) are given such
+// an offset, so every load is unconditional -- the compiler then counts
+// outstanding loads exactly and a D-deep ring of tiles stays in flight while
+// earlier tiles are computed -- and the tail costs no HBM traffic.  Weight
+// bytes are read once per call, so they are loaded non-temporally.
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
+
+// 2^31 (past the end of every section, which are all < 2 GiB) unless `valid`;
+// OR-ed into an in-range offset (always < 2^31),
+// so the choice stays arithmetic instead of becoming a branch around a load.
+__device__ __forceinline__ uint32_t oob_bit(bool valid) { return (uint32_t)(!valid) << 31; }
+constexpr int kAuxStream = 2;                   // cache policy: non-temporal
+constexpr int kBufferFlags = 0x00020000;        // raw (unswizzled, unformatted) buffer
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 ld_stream16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u_t t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxStream);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ uint32_t ld_stream4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAuxStream);
+}
+
 template <int GPW>
-__device__ __forceinline__ float w4a16_tile_partial(const uint4 (&c)[GPW], const uint16_t (&s)[GPW],
-                                                    const uint32_t (&xp)[GPW][16], const float (&xs)[GPW]) {
+struct Int4Slot {
+  uint4 c[GPW];      // the lane's 16 code bytes of each group
+  uint32_t s[GPW];   // bf16 scale bits of (row r, group) in the low half
+};
+
+template <int GPW, int P>
+struct SignSlot {
+  uint32_t w[GPW][P];  // the lane's sign dword of each (group, plane)
+  uint32_t a[P][GPW];  // fp16 alpha bits of (plane, row r, group) in the low half
+};
+
+// GPW consecutive 16-bit values with one load (scale rows are padded to a
+// multiple of four entries, so the run is aligned to its own size).
+template <int GPW>
+__device__ __forceinline__ void load_u16_run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&v)[GPW]) {
+  if constexpr (GPW == 4) {
+    const v2u_t t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v[0] = t.x & 0xFFFFu;
+    v[1] = t.x >> 16;
+    v[2] = t.y & 0xFFFFu;
+    v[3] = t.y >> 16;
+  } else if constexpr (GPW == 2) {
+    const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    v[0] = t & 0xFFFFu;
+    v[1] = t >> 16;
+  } else {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+}
+
+// Buffer views of one packed blob: weights (codes or sign planes) and scales.
+struct BlobView {
+  __amdgpu_buffer_rsrc_t w, s;
+  int KT, KT4, NT;
+};
+
+__device__ __forceinline__ BlobView int4_view(const uint8_t* blob, int KT, int NT) {
+  BlobView v;
+  v.KT = KT;
+  v.KT4 = (KT + 3) & ~3;
+  v.NT = NT;
+  const uint32_t wbytes = (uint32_t)NT * (uint32_t)KT * 1024u;
+  v.w = make_rsrc(blob, wbytes);
+  v.s = make_rsrc(blob + wbytes, (uint32_t)NT * 16u * (uint32_t)v.KT4 * 2u);
+  return v;
+}
+
+__device__ __forceinline__ BlobView sign_view(const uint8_t* blob, int KT, int NT, int P) {
+  BlobView v;
+  v.KT = KT;
+  v.KT4 = (KT + 3) & ~3;
+  v.NT = NT;
+  const uint32_t wbytes = (uint32_t)NT * (uint32_t)KT * 256u * (uint32_t)P;
+  v.w = make_rsrc(blob, wbytes);
+  v.s = make_rsrc(blob + wbytes, (uint32_t)P * (uint32_t)NT * 16u * (uint32_t)v.KT4 * 2u);
+  return v;
+}
+
+// live: this tile is one of the workgroup's (else every load reads zero).
+template <int GPW>
+__device__ __forceinline__ void load_int4_tile(Int4Slot<GPW>& sl, const BlobView& b, int rt, bool live, int g0,
+                                               int lane, int r) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = g0 + gi;
+    const uint32_t off = (uint32_t)(rt * b.KT + g) * 1024u + 16u * lane;
+    sl.c[gi] = ld_stream16(b.w, off | oob_bit(live && g < b.KT));
+  }
+  const uint32_t soff = ((uint32_t)(16 * rt + r) * b.KT4 + g0) * 2u;
+  load_u16_run<GPW>(b.s, soff | oob_bit(live && g0 < b.KT4), sl.s);
+}
+
+template <int GPW, int P>
+__device__ __forceinline__ void load_sign_tile(SignSlot<GPW, P>& sl, const BlobView& b, int rt, bool live, int g0,
+                                               int lane, int r) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = g0 + gi;
+    const uint32_t off = ((uint32_t)(rt * b.KT + g) * 256u * P + 4u * lane) | oob_bit(live && g < b.KT);
+#pragma unroll
+    for (int p = 0; p < P; ++p) sl.w[gi][p] = ld_stream4(b.w, off + 256u * p);
+  }
+  const int N16 = b.NT * 16;
+  const uint32_t oob = oob_bit(live && g0 < b.KT4);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const uint32_t aoff = ((uint32_t)(p * N16 + 16 * rt + r) * b.KT4 + g0) * 2u;
+    load_u16_run<GPW>(b.s, aoff | oob, sl.a[p]);
+  }
+}
+
+// Number of row tiles this workgroup owns in the grid-stride order.
+__device__ __forceinline__ int tiles_of_wg(int NT) { return (NT - 1 - (int)blockIdx.x) / (int)gridDim.x + 1; }
+
+// Row tile of the workgroup's i-th iteration.
+__device__ __forceinline__ int row_tile(int i) { return blockIdx.x + i * gridDim.x; }
+
+// ---------------------------------------------------------------------------
+// M = 1 mat-vec cores.  Each returns the lane's partial sum for row r over its
+// k sub-ranges of the wave's groups.  nxs[g] = -136 * (the lane's sum of x
+// over group g) starts each group's accumulator, which removes the +136
+// carried by every decoded code.
+template <int GPW>
+__device__ __forceinline__ float w4a16_tile_partial(const Int4Slot<GPW>& sl, const uint32_t (&xp)[GPW][16],
+                                                    const float (&nxs)[GPW], uint32_t magic) {
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const uint32_t w[4] = {c[gi].x, c[gi].y, c[gi].z, c[gi].w};
-    float acc = 0.f;
+    const uint32_t w[4] = {sl.c[gi].x, sl.c[gi].y, sl.c[gi].z, sl.c[gi].w};
+    float acc = nxs[gi];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = dot2(int4_pair(w[t], i), xp[gi][4 * t + i], acc);
-    part = fmaf(bf16_to_f32(s[gi]), fmaf(-kInt4Bias, xs[gi], acc), part);
+      for (int i = 0; i < 4; ++i) acc = dot2(int4_pair(w[t], i, magic), xp[gi][4 * t + i], acc);
+    part = fmaf(bf16_to_f32(sl.s[gi]), acc, part);
   }
   return part;
 }
 
 template <int GPW, int P>
-__device__ __forceinline__ float binplane_tile_partial(const uint32_t (&w)[GPW][P], const uint16_t (&al)[GPW][P],
-                                                       const uint32_t (&xp)[GPW][16]) {
+__device__ __forceinline__ float binplane_tile_partial(const SignSlot<GPW, P>& sl, const uint32_t (&xp)[GPW][16],
+                                                       uint32_t one) {
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi)
@@ -166,164 +365,222 @@ __device__ __forceinline__ float binplane_tile_partial(const uint32_t (&w)[GPW][
     for (int p = 0; p < P; ++p) {
       float acc = 0.f;
 #pragma unroll
-      for (int ip = 0; ip < 16; ++ip) acc = dot2(sign_pair(w[gi][p], ip), xp[gi][ip], acc);
-      part = fmaf(f16_to_f32(al[gi][p]), acc, part);
+      for (int ip = 0; ip < 16; ++ip) acc = dot2(sign_pair(sl.w[gi][p], ip, one), xp[gi][ip], acc);
+      part = fmaf(f16_to_f32((uint16_t)sl.a[p][gi]), acc, part);
     }
   return part;
 }
 
-// ---------------------------------------------------------------------------
-// Tile loaders (global -> registers).
-template <int GPW>
-__device__ __forceinline__ void load_int4_tile(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                               int rt, int g0, int KT, int lane, int r, uint4 (&c)[GPW],
-                                               uint16_t (&s)[GPW]) {
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int g = g0 + gi;
-    if (g < KT) {
-      c[gi] = *reinterpret_cast<const uint4*>(codes + ((size_t)rt * KT + g) * 1024 + 16 * lane);
-      s[gi] = scales[(size_t)(16 * rt + r) * KT + g];
-    } else {
-      c[gi] = make_uint4(0u, 0u, 0u, 0u);
-      s[gi] = 0;
-    }
+// Per-tile partials wait in LDS and are combined once per chunk of C tiles,
+// so the waves of a workgroup meet at a barrier only once per chunk.
+constexpr int kChunkGemv = 16;  // tiles per chunk, M = 1 kernels
+constexpr int kChunkGemm = 4;   // tiles per chunk, M <= 16 kernels
+
+// M = 1 chunk epilogue: the chunk's ntiles x 16 row sums, each over the
+// waves' partials; thread tid walks outputs tid, tid + blockDim, ... (so a
+// thread's outputs come in increasing row order).
+template <class F>
+__device__ __forceinline__ void chunk_row_sums(const float* red, int nwaves, int ntiles, F&& emit) {
+  // nwaves * 64 is the block size (blockDim.x itself would be a memory read here).
+  for (int o = threadIdx.x; o < ntiles * 16; o += nwaves * 64) {
+    const int c = o >> 4, rr = o & 15;
+    float s = 0.f;
+    for (int w = 0; w < nwaves; ++w) s += red[(c * nwaves + w) * 16 + rr];
+    emit(c, rr, s);  // (tile in chunk, row in tile, value)
   }
 }
 
-template <int GPW, int P>
-__device__ __forceinline__ void load_sign_tile(const uint8_t* __restrict__ bits, const uint16_t* __restrict__ alpha,
-                                               int rt, int g0, int KT, int N16, int lane, int r,
-                                               uint32_t (&w)[GPW][P], uint16_t (&al)[GPW][P]) {
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int g = g0 + gi;
-    const uint32_t* src =
-        reinterpret_cast<const uint32_t*>(bits + ((size_t)rt * KT + g) * 256 * P + 4 * P * lane);
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (g < KT) {
-        w[gi][p] = src[p];
-        al[gi][p] = alpha[((size_t)p * N16 + 16 * rt + r) * KT + g];
-      } else {
-        w[gi][p] = 0u;
-        al[gi][p] = 0;
-      }
-    }
+// ---------------------------------------------------------------------------
+// lmhead_argmax completion.  A (logit, row) pair becomes one 64-bit key whose
+// unsigned order is the greedy order: the high word is the logit's bits
+// mapped so that unsigned comparison follows float comparison, the low word
+// is 2^32 - 1 - row, so a larger logit wins and the lower row wins a tie.
+// Every workgroup folds its per-query-row best into key[m] with a
+// device-scope atomicMax and waits for the atomic to return before it bumps a
+// completion counter; the workgroup that brings the counter to gridDim.x
+// takes each key with an atomic exchange against zero, writes the outputs and
+// clears the counter.  Keys and counter are only ever touched by device-scope
+// read-modify-write atomics, which every XCD performs at the same point of
+// coherence, and each step is issued only after the step before it has
+// returned, so no cache-wide fence is needed.  A max does not depend on the
+// order of its operands, so neither does the result.
+constexpr int kWsKeys = 0;        // M uint64 keys
+constexpr int kWsCounter = 128;   // uint32 completion counter
+constexpr int kWsBytes = 256;
+
+__device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)n);
+}
+
+__device__ __forceinline__ void argmax_complete(unsigned long long key, bool holds_row, int m, uint8_t* ws, int M,
+                                                int N, const int32_t* __restrict__ row_ids,
+                                                int32_t* __restrict__ out_idx, float* __restrict__ out_max) {
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kWsKeys);
+  unsigned* counter = reinterpret_cast<unsigned*>(ws + kWsCounter);
+  if (holds_row) {
+    const unsigned long long prev = atomicMax(&keys[m], key);
+    asm volatile("" ::"v"(prev));  // a use of the return value waits until the max has been performed
   }
+  __syncthreads();
+  __shared__ int last;
+  if (threadIdx.x == 0) last = atomicAdd(counter, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  if ((int)threadIdx.x < M) {
+    const unsigned long long k = atomicExch(&keys[threadIdx.x], 0ull);
+    const uint32_t o = (uint32_t)(k >> 32);
+    const int n = (int)(0xFFFFFFFFu - (uint32_t)k);
+    // key 0 means no row compared above it: every logit of the row was NaN.
+    const bool found = k != 0ull && n >= 0 && n < N;
+    const uint32_t u = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+    out_idx[threadIdx.x] = !found ? -1 : row_ids ? row_ids[n] : n;
+    out_max[threadIdx.x] = found ? __uint_as_float(u) : __builtin_nanf("");
+  }
+  if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
 
 // ---------------------------------------------------------------------------
 // gemv_w4a16 / lmhead (M = 1).  ARGMAX selects the epilogue.
-template <int GPW, int MAXW, bool ARGMAX>
+template <int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemv_w4a16(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ xw, uint16_t* __restrict__ y,
-                 ArgBest* __restrict__ ws, int N, int KT, int NT) {
+                 uint8_t* __restrict__ ws, const int32_t* __restrict__ row_ids, int32_t* __restrict__ out_idx,
+                 float* __restrict__ out_max, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
-  const uint8_t* codes = blob;
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + (size_t)NT * KT * 1024);
+  const BlobView bv = int4_view(blob, KT, NT);
+  const int T = tiles_of_wg(NT);
 
+  uint32_t xo[GPW];
+  load_x_own<GPW>(xw, g0, KT, q, r, xo);
+  Int4Slot<GPW> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_int4_tile<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    // Issue each slot's loads in the same order the loop refills them.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Keep the whole prefetch issued before anything waits on the activations.
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t xp[GPW][16];
-  float xs[GPW];
-  load_x_pairs<GPW>(xw, true, g0, KT, q, xp);
-  lane_group_sums<GPW>(xp, xs);
+  expand_x<GPW>(xo, g0, KT, xp);
+  float nxs[GPW];
+  lane_group_sums<GPW>(xp, nxs);
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) nxs[gi] *= -kInt4Bias;
+  const uint32_t magic = kInt4Magic;
 
-  __shared__ float red[2][kMaxWaves][16];
+  __shared__ float red[kChunkGemv * MAXW * 16];
   float best_v = -FLT_MAX;
   int best_i = INT_MAX;
-
-  uint4 cur[GPW], nxt[GPW];
-  uint16_t scur[GPW], snxt[GPW];
-  int rt = blockIdx.x;
-  if (rt < NT) load_int4_tile<GPW>(codes, scales, rt, g0, KT, lane, r, cur, scur);
-  for (int it = 0; rt < NT; rt += gridDim.x, ++it) {
-    const int rn = rt + gridDim.x;
-    if (rn < NT) load_int4_tile<GPW>(codes, scales, rn, g0, KT, lane, r, nxt, snxt);
-    float part = w4a16_tile_partial<GPW>(cur, scur, xp, xs);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    if (q == 0) red[it & 1][wave][r] = part;
-    __syncthreads();
-    if (threadIdx.x < 16) {
-      float v = 0.f;
-      for (int w2 = 0; w2 < nwaves; ++w2) v += red[it & 1][w2][threadIdx.x];
-      const int n = 16 * rt + threadIdx.x;
-      if (n < N) {
-        if constexpr (ARGMAX) {
-          if (v > best_v) {  // rows arrive in increasing n per thread
-            best_v = v;
-            best_i = n;
-          }
-        } else {
-          y[n] = f32_to_bf16_rne(v);
-        }
-      }
-    }
+  // Every workgroup owns at least one tile (grid <= number of tiles).
+  int i0 = 0;
+  do {
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      cur[gi] = nxt[gi];
-      scur[gi] = snxt[gi];
-    }
-  }
-  if constexpr (ARGMAX) {
-    if (threadIdx.x < 64) {
-      for (int off = 8; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(best_v, off);
-        const int oi = __shfl_xor(best_i, off);
-        if (better(ov, oi, best_v, best_i)) {
-          best_v = ov;
-          best_i = oi;
-        }
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      const int ci = i % kChunkGemv;
+      // Computed unconditionally (a tile past T holds zeros) so the loop body
+      // stays straight-line; only the staging write is predicated.
+      const float part = sum_over_q(w4a16_tile_partial<GPW>(ring[j], xp, nxs, magic));
+      if (q == 0 && i < T) red[(ci * nwaves + wave) * 16 + r] = part;
+      load_int4_tile<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      if (i < T && (ci == kChunkGemv - 1 || i == T - 1)) {
+        __syncthreads();
+        const int first = i - ci;
+        chunk_row_sums(red, nwaves, ci + 1, [&](int c, int rr, float v) {
+          const int n = 16 * row_tile(first + c) + rr;
+          if (n < N) {
+            if constexpr (ARGMAX) {
+              if (v > best_v) {  // a thread's rows arrive in increasing n
+                best_v = v;
+                best_i = n;
+              }
+            } else {
+              y[n] = f32_to_bf16_rne(v);
+            }
+          }
+        });
+        __syncthreads();
       }
-      if (threadIdx.x == 0) ws[blockIdx.x] = ArgBest{best_v, best_i};
     }
+    i0 += D;
+  } while (i0 < T);
+  if constexpr (ARGMAX) {
+    // Lowest index wins ties; each thread saw its rows in increasing order.
+    __shared__ ArgBest part[MAXW];
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(best_v, off);
+      const int oi = __shfl_xor(best_i, off);
+      if (better(ov, oi, best_v, best_i)) {
+        best_v = ov;
+        best_i = oi;
+      }
+    }
+    if (lane == 0) part[wave] = ArgBest{best_v, best_i};
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int w = 1; w < nwaves; ++w)
+        if (better(part[w].v, part[w].idx, best_v, best_i)) {
+          best_v = part[w].v;
+          best_i = part[w].idx;
+        }
+    argmax_complete(argmax_key(best_v, best_i), threadIdx.x == 0 && best_i < N, 0, ws, 1, N, row_ids, out_idx,
+                    out_max);
   }
 }
 
 // gemv_binplane (M = 1).
-template <int GPW, int MAXW, int P>
+template <int GPW, int MAXW, int D, int P>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemv_binplane(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ xw, uint16_t* __restrict__ y,
                     int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
-  const int N16 = NT * 16;
-  const uint8_t* bits = blob;
-  const uint16_t* alpha = reinterpret_cast<const uint16_t*>(blob + (size_t)NT * KT * 256 * P);
+  const BlobView bv = sign_view(blob, KT, NT, P);
+  const int T = tiles_of_wg(NT);
 
-  uint32_t xp[GPW][16];
-  load_x_pairs<GPW>(xw, true, g0, KT, q, xp);
-
-  __shared__ float red[2][kMaxWaves][16];
-  uint32_t cur[GPW][P], nxt[GPW][P];
-  uint16_t acur[GPW][P], anxt[GPW][P];
-  int rt = blockIdx.x;
-  if (rt < NT) load_sign_tile<GPW, P>(bits, alpha, rt, g0, KT, N16, lane, r, cur, acur);
-  for (int it = 0; rt < NT; rt += gridDim.x, ++it) {
-    const int rn = rt + gridDim.x;
-    if (rn < NT) load_sign_tile<GPW, P>(bits, alpha, rn, g0, KT, N16, lane, r, nxt, anxt);
-    float part = binplane_tile_partial<GPW, P>(cur, acur, xp);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    if (q == 0) red[it & 1][wave][r] = part;
-    __syncthreads();
-    if (threadIdx.x < 16) {
-      float v = 0.f;
-      for (int w2 = 0; w2 < nwaves; ++w2) v += red[it & 1][w2][threadIdx.x];
-      const int n = 16 * rt + threadIdx.x;
-      if (n < N) y[n] = f32_to_bf16_rne(v);
-    }
+  uint32_t xo[GPW];
+  load_x_own<GPW>(xw, g0, KT, q, r, xo);
+  SignSlot<GPW, P> ring[D];
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        cur[gi][p] = nxt[gi][p];
-        acur[gi][p] = anxt[gi][p];
-      }
+  for (int j = 0; j < D; ++j) {
+    load_sign_tile<GPW, P>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    // Issue each slot's loads in the same order the loop refills them.
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // Keep the whole prefetch issued before anything waits on the activations.
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t xp[GPW][16];
+  expand_x<GPW>(xo, g0, KT, xp);
+  const uint32_t one = kOnePair;
+
+  __shared__ float red[kChunkGemv * MAXW * 16];
+  int i0 = 0;
+  do {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      const int ci = i % kChunkGemv;
+      const float part = sum_over_q(binplane_tile_partial<GPW, P>(ring[j], xp, one));
+      if (q == 0 && i < T) red[(ci * nwaves + wave) * 16 + r] = part;
+      load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      if (i < T && (ci == kChunkGemv - 1 || i == T - 1)) {
+        __syncthreads();
+        const int first = i - ci;
+        chunk_row_sums(red, nwaves, ci + 1, [&](int c, int rr, float v) {
+          const int n = 16 * row_tile(first + c) + rr;
+          if (n < N) y[n] = f32_to_bf16_rne(v);
+        });
+        __syncthreads();
+      }
+    }
+    i0 += D;
+  } while (i0 < T);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,207 +596,226 @@ __device__ __forceinline__ void x_group_sums_to_lds(const uint32_t (&xa)[GPW][16
   lane_group_sums<GPW>(xa, xs);
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    float s = xs[gi];
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
+    const float s = sum_over_q(xs[gi]);
     if (q == 0 && g0 + gi < KT) xs_sh[r][g0 + gi] = s;
   }
 }
 
-// Per-tile epilogue: the WG's waves' 16x16 partials meet in LDS.  Thread
-// tid < 256 owns (m = tid/16, n = tid%16) and returns the finished sum.
-__device__ __forceinline__ float reduce_tile_16x16(float (*red)[256], const float (&yv)[4], int wave, int nwaves,
-                                                   int q, int r) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][(4 * q + i) * 16 + r] = yv[i];
-  __syncthreads();
-  float v = 0.f;
-  if (threadIdx.x < 256)
-    for (int w2 = 0; w2 < nwaves; ++w2) v += red[w2][threadIdx.x];
-  return v;
+// M <= 16 chunk epilogue: the chunk's ntiles x 256 outputs, each the sum of
+// the waves' partials; thread tid walks outputs tid, tid + blockDim, ...
+template <class F>
+__device__ __forceinline__ void chunk_tile_sums(const float* red, int nwaves, int ntiles, F&& emit) {
+  // nwaves * 64 is the block size (blockDim.x itself would be a memory read here).
+  for (int o = threadIdx.x; o < ntiles * 256; o += nwaves * 64) {
+    const int c = o >> 8, e = o & 255;
+    float s = 0.f;
+    for (int w = 0; w < nwaves; ++w) s += red[(c * nwaves + w) * 256 + e];
+    emit(c, e >> 4, e & 15, s);  // (tile in chunk, m, n in tile, value)
+  }
 }
 
-template <int GPW, int MAXW, bool ARGMAX>
+template <int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemm_w4a16(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
-                 ArgBest* __restrict__ ws, int M, int N, int KT, int NT) {
+                 uint8_t* __restrict__ ws, const int32_t* __restrict__ row_ids, int32_t* __restrict__ out_idx,
+                 float* __restrict__ out_max, int M, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
-  const uint8_t* codes = blob;
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + (size_t)NT * KT * 1024);
-
-  __shared__ float xs_sh[16][65];
-  __shared__ float red[2][kMaxWaves][256];
+  const BlobView bv = int4_view(blob, KT, NT);
+  const int T = tiles_of_wg(NT);
 
   uint32_t xa[GPW][16];
-  load_x_pairs<GPW>(Xw + (size_t)r * KT * 64, r < M, g0, KT, q, xa);
+  load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
+  Int4Slot<GPW> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_int4_tile<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    // Issue each slot's loads in the same order the loop refills them.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Keep the whole prefetch issued before anything waits on the activations.
+  __builtin_amdgcn_sched_barrier(0);
+  mask_x_pairs<GPW>(r, M, g0, KT, xa);
+
+  __shared__ float xs_sh[16][65];
+  __shared__ float red[kChunkGemm * MAXW * 256];
   // Every (row, group) entry read below is written by the wave owning the group.
   x_group_sums_to_lds<GPW>(xa, g0, KT, q, r, xs_sh);
   __syncthreads();
-  float xsv[GPW][4];
+  f32x4_t cinit[GPW];  // -136 * sum_k X[m][k] over the group, for m = 4q + i
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xsv[gi][i] = g0 + gi < KT ? xs_sh[4 * q + i][g0 + gi] : 0.f;
+    for (int i = 0; i < 4; ++i) cinit[gi][i] = g0 + gi < KT ? -kInt4Bias * xs_sh[4 * q + i][g0 + gi] : 0.f;
+  const uint32_t magic = kInt4Magic;
 
+  // Running best per (query row, n slot): thread tid < 256 owns m = tid >> 4.
   float best_v = -FLT_MAX;
   int best_i = INT_MAX;
-  const int mo = threadIdx.x >> 4, no = threadIdx.x & 15;  // output owned by this thread (tid < 256)
-
-  uint4 cur[GPW], nxt[GPW];
-  uint16_t scur[GPW], snxt[GPW];
-  int rt = blockIdx.x;
-  if (rt < NT) load_int4_tile<GPW>(codes, scales, rt, g0, KT, lane, r, cur, scur);
-  for (int it = 0; rt < NT; rt += gridDim.x, ++it) {
-    const int rn = rt + gridDim.x;
-    if (rn < NT) load_int4_tile<GPW>(codes, scales, rn, g0, KT, lane, r, nxt, snxt);
-    float yv[4] = {0.f, 0.f, 0.f, 0.f};
+  int i0 = 0;
+  do {
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      const uint32_t w[4] = {cur[gi].x, cur[gi].y, cur[gi].z, cur[gi].w};
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      const int ci = i % kChunkGemm;
+      {
+        float yv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t b[4] = {int4_pair(w[t], 0), int4_pair(w[t], 1), int4_pair(w[t], 2), int4_pair(w[t], 3)};
-        c = mfma16x16x32(&xa[gi][4 * t], b, c);
-      }
-      const float s = bf16_to_f32(scur[gi]);
+        for (int gi = 0; gi < GPW; ++gi) {
+          const uint4 cw = ring[j].c[gi];
+          const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+          f32x4_t c = cinit[gi];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yv[i] = fmaf(s, fmaf(-kInt4Bias, xsv[gi][i], c[i]), yv[i]);
-    }
-    const float v = reduce_tile_16x16(red[it & 1], yv, wave, nwaves, q, r);
-    const int n = 16 * rt + no;
-    if (threadIdx.x < 256 && mo < M && n < N) {
-      if constexpr (ARGMAX) {
-        if (v > best_v) {
-          best_v = v;
-          best_i = n;
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t bq[4] = {int4_pair(w[t], 0, magic), int4_pair(w[t], 1, magic),
+                                    int4_pair(w[t], 2, magic), int4_pair(w[t], 3, magic)};
+            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+          }
+          const float s = bf16_to_f32(ring[j].s[gi]);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) yv[ii] = fmaf(s, c[ii], yv[ii]);
         }
-      } else {
-        Y[(size_t)mo * N + n] = f32_to_bf16_rne(v);
+        float* rp = red + (ci * nwaves + wave) * 256;
+        if (i < T)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) rp[(4 * q + ii) * 16 + r] = yv[ii];
+      }
+      load_int4_tile<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      if (i < T && (ci == kChunkGemm - 1 || i == T - 1)) {
+        __syncthreads();
+        const int first = i - ci;
+        chunk_tile_sums(red, nwaves, ci + 1, [&](int c, int m, int nn, float v) {
+          const int n = 16 * row_tile(first + c) + nn;
+          if (m < M && n < N) {
+            if constexpr (ARGMAX) {
+              // thread tid's outputs always share m = (tid >> 4) & 15 and come in increasing n
+              if (v > best_v) {
+                best_v = v;
+                best_i = n;
+              }
+            } else {
+              Y[(size_t)m * N + n] = f32_to_bf16_rne(v);
+            }
+          }
+        });
+        __syncthreads();
       }
     }
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      cur[gi] = nxt[gi];
-      scur[gi] = snxt[gi];
-    }
-  }
+    i0 += D;
+  } while (i0 < T);
   if constexpr (ARGMAX) {
-    if (threadIdx.x < 256) {
-      for (int off = 8; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(best_v, off);
-        const int oi = __shfl_xor(best_i, off);
-        if (better(ov, oi, best_v, best_i)) {
-          best_v = ov;
-          best_i = oi;
-        }
+    // Thread tid held outputs with m = (tid >> 4) & 15; combine the 16 n slots
+    // of a row within the wave, then the waves through LDS.
+    for (int off = 8; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(best_v, off);
+      const int oi = __shfl_xor(best_i, off);
+      if (better(ov, oi, best_v, best_i)) {
+        best_v = ov;
+        best_i = oi;
       }
-      if (no == 0 && mo < M) ws[(size_t)mo * gridDim.x + blockIdx.x] = ArgBest{best_v, best_i};
     }
+    __shared__ ArgBest part[MAXW * 4];
+    if ((lane & 15) == 0) part[wave * 4 + (lane >> 4)] = ArgBest{best_v, best_i};
+    __syncthreads();
+    float bvv = -FLT_MAX;
+    int bii = INT_MAX;
+    if ((int)threadIdx.x < M) {
+      // slot (wave, lane >> 4) holds m = (wave * 4 + (lane >> 4)) & 15
+      for (int sl = threadIdx.x; sl < nwaves * 4; sl += 16)
+        if (better(part[sl].v, part[sl].idx, bvv, bii)) {
+          bvv = part[sl].v;
+          bii = part[sl].idx;
+        }
+    }
+    argmax_complete(argmax_key(bvv, bii), (int)threadIdx.x < M && bii < N, threadIdx.x, ws, M, N, row_ids,
+                    out_idx, out_max);
   }
 }
 
-template <int GPW, int MAXW, int P>
+template <int GPW, int MAXW, int D, int P>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemm_binplane(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
                     int M, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
-  const int N16 = NT * 16;
-  const uint8_t* bits = blob;
-  const uint16_t* alpha = reinterpret_cast<const uint16_t*>(blob + (size_t)NT * KT * 256 * P);
+  const BlobView bv = sign_view(blob, KT, NT, P);
+  const int T = tiles_of_wg(NT);
 
-  __shared__ float red[2][kMaxWaves][256];
   uint32_t xa[GPW][16];
-  load_x_pairs<GPW>(Xw + (size_t)r * KT * 64, r < M, g0, KT, q, xa);
-  const int mo = threadIdx.x >> 4, no = threadIdx.x & 15;
-
-  uint32_t cur[GPW][P], nxt[GPW][P];
-  uint16_t acur[GPW][P], anxt[GPW][P];
-  int rt = blockIdx.x;
-  if (rt < NT) load_sign_tile<GPW, P>(bits, alpha, rt, g0, KT, N16, lane, r, cur, acur);
-  for (int it = 0; rt < NT; rt += gridDim.x, ++it) {
-    const int rn = rt + gridDim.x;
-    if (rn < NT) load_sign_tile<GPW, P>(bits, alpha, rn, g0, KT, N16, lane, r, nxt, anxt);
-    float yv[4] = {0.f, 0.f, 0.f, 0.f};
+  load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
+  SignSlot<GPW, P> ring[D];
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t b[4] = {sign_pair(cur[gi][p], 4 * t + 0), sign_pair(cur[gi][p], 4 * t + 1),
-                                 sign_pair(cur[gi][p], 4 * t + 2), sign_pair(cur[gi][p], 4 * t + 3)};
-          c = mfma16x16x32(&xa[gi][4 * t], b, c);
-        }
-        const float a = f16_to_f32(acur[gi][p]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yv[i] = fmaf(a, c[i], yv[i]);
-      }
-    const float v = reduce_tile_16x16(red[it & 1], yv, wave, nwaves, q, r);
-    const int n = 16 * rt + no;
-    if (threadIdx.x < 256 && mo < M && n < N) Y[(size_t)mo * N + n] = f32_to_bf16_rne(v);
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        cur[gi][p] = nxt[gi][p];
-        acur[gi][p] = anxt[gi][p];
-      }
+  for (int j = 0; j < D; ++j) {
+    load_sign_tile<GPW, P>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    // Issue each slot's loads in the same order the loop refills them.
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // Keep the whole prefetch issued before anything waits on the activations.
+  __builtin_amdgcn_sched_barrier(0);
+  mask_x_pairs<GPW>(r, M, g0, KT, xa);
+  const uint32_t one = kOnePair;
+
+  __shared__ float red[kChunkGemm * MAXW * 256];
+  int i0 = 0;
+  do {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      const int ci = i % kChunkGemm;
+      {
+        float yv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const uint32_t wp = ring[j].w[gi][p];
+            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, one), sign_pair(wp, 4 * t + 1, one),
+                                      sign_pair(wp, 4 * t + 2, one), sign_pair(wp, 4 * t + 3, one)};
+              c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+            }
+            const float a = f16_to_f32((uint16_t)ring[j].a[p][gi]);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) yv[ii] = fmaf(a, c[ii], yv[ii]);
+          }
+        float* rp = red + (ci * nwaves + wave) * 256;
+        if (i < T)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) rp[(4 * q + ii) * 16 + r] = yv[ii];
+      }
+      load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      if (i < T && (ci == kChunkGemm - 1 || i == T - 1)) {
+        __syncthreads();
+        const int first = i - ci;
+        chunk_tile_sums(red, nwaves, ci + 1, [&](int c, int m, int nn, float v) {
+          const int n = 16 * row_tile(first + c) + nn;
+          if (m < M && n < N) Y[(size_t)m * N + n] = f32_to_bf16_rne(v);
+        });
+        __syncthreads();
+      }
+    }
+    i0 += D;
+  } while (i0 < T);
 }
 
-// Combine the per-workgroup bests of lmhead_argmax: block m reduces row m.
-__global__ void __launch_bounds__(256)
-    k_argmax_finalize(const ArgBest* __restrict__ ws, int nwg, int N, const int32_t* __restrict__ row_ids,
-                      int32_t* __restrict__ out_idx, float* __restrict__ out_max) {
-  const int m = blockIdx.x;
-  float bv = -FLT_MAX;
-  int bi = INT_MAX;
-  for (int j = threadIdx.x; j < nwg; j += blockDim.x) {
-    const ArgBest e = ws[(size_t)m * nwg + j];
-    if (better(e.v, e.idx, bv, bi)) {
-      bv = e.v;
-      bi = e.idx;
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-  __shared__ ArgBest part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ArgBest{bv, bi};
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
-      if (better(part[w].v, part[w].idx, bv, bi)) {
-        bv = part[w].v;
-        bi = part[w].idx;
-      }
-    // No row compared greater than -FLT_MAX only if every logit was NaN.
-    const bool found = bi >= 0 && bi < N;
-    out_idx[m] = !found ? -1 : row_ids ? row_ids[bi] : bi;
-    out_max[m] = found ? bv : __builtin_nanf("");
-  }
-}
-
-// Streaming-read ceiling: 16-byte loads over `n16` chunks, one checksum per WG.
+// Streaming-read ceiling: non-temporal 16-byte loads, eight per thread in
+// flight, over `n16` chunks; one checksum per workgroup keeps the loads live.
 __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ src, size_t n16,
                                                      uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
   uint32_t acc = 0;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    v4u_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + i + u * stride));
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
     const uint4 a = src[i];
@@ -577,15 +853,6 @@ int device_cus(int* cus) {
   return SVQ_OK;
 }
 
-int wgs_per_cu() {
-  static const int v = [] {
-    const char* s = std::getenv("SVQ_WG_PER_CU");
-    const int x = s ? std::atoi(s) : 0;
-    return x >= 1 && x <= 8 ? x : 2;
-  }();
-  return v;
-}
-
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 int check_linear(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N, int64_t K,
@@ -598,6 +865,10 @@ int check_linear(const char* fn, const void* packed, const void* x, const void* 
     return svq::fail(SVQ_ERR_SHAPE, "%s: K=%lld must be a multiple of 128 in [128, %d]", fn, (long long)K, SVQ_MAX_K);
   if (M < 1 || M > SVQ_MAX_M) return svq::fail(SVQ_ERR_SHAPE, "%s: M=%d must be in 1..16", fn, M);
   if (P != 0 && (P < 1 || P > SVQ_MAX_P)) return svq::fail(SVQ_ERR_SHAPE, "%s: P=%d must be in 1..6", fn, P);
+  const int64_t N16 = (N + 15) / 16 * 16;
+  if (N16 * K / 2 >= ((int64_t)1 << 31) || (P != 0 && N16 * K / 8 * P >= ((int64_t)1 << 31)))
+    return svq::fail(SVQ_ERR_SHAPE, "%s: packed weights must be smaller than 2 GiB (N=%lld, K=%lld)", fn,
+                     (long long)N, (long long)K);
   if (misaligned(packed, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: packed weights must be 16-byte aligned", fn);
   if (misaligned(x, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: activations must be 16-byte aligned", fn);
   if (misaligned(y, 2)) return svq::fail(SVQ_ERR_ALIGN, "%s: output must be 2-byte aligned", fn);
@@ -605,21 +876,48 @@ int check_linear(const char* fn, const void* packed, const void* x, const void* 
 }
 
 struct Shape {
-  int KT, NT, gpw, waves, grid;
+  int KT, NT, gpw, waves, grid, depth;
 };
 
-// min_waves: the M <= 16 kernels finish a 16x16 output tile with 256
-// threads, so their workgroups always carry at least four waves.
-int plan(int64_t N, int64_t K, int min_waves, Shape* s) {
+int env_int(const char* name, int lo, int hi, int dflt) {
+  const char* s = std::getenv(name);
+  const int x = s ? std::atoi(s) : 0;
+  return x >= lo && x <= hi ? x : dflt;
+}
+
+// Launch shape.  A workgroup owns one 16-row tile at a time and splits K
+// across its waves (gpw groups each); the grid is one or a few workgroups per
+// CU walking the row tiles in grid-stride order; the ring depth is the number
+// of tiles whose loads each wave keeps in flight, at most the number of tiles
+// every workgroup owns (so the pipeline tail stays short).
+// wave_quantum: the M <= 16 kernels walk each 16x16 output tile with a
+// multiple of 256 threads (so a thread always meets the same query row), so
+// their workgroups carry a multiple of four waves.
+// Measured on MI355X (rocprofv3, decode/verify/head shapes at K = 4096): the
+// M = 1 mat-vecs run best at two workgroups per CU with a ring of <= 2 tiles,
+// the M <= 16 kernels at one workgroup per CU with a ring of <= 3 tiles.
+struct LaunchPref {
+  int wgs_per_cu, max_depth;
+};
+constexpr LaunchPref kPrefGemv = {2, 2};
+constexpr LaunchPref kPrefGemm = {1, 3};
+constexpr LaunchPref kPrefHeadM1 = {1, 2};
+constexpr LaunchPref kPrefHeadM16 = {1, 3};
+
+int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* s) {
   int cus = 0;
   if (int rc = device_cus(&cus)) return rc;
   s->KT = (int)(K / 128);
   s->NT = (int)((N + 15) / 16);
   s->gpw = s->KT <= 8 ? 1 : s->KT <= 16 ? 2 : 4;
   s->waves = (s->KT + s->gpw - 1) / s->gpw;
-  if (s->waves < min_waves) s->waves = min_waves;
-  const int want = cus * wgs_per_cu();
+  s->waves = (s->waves + wave_quantum - 1) / wave_quantum * wave_quantum;
+  // SVQ_WG_PER_CU / SVQ_PIPE_DEPTH override the preferences (for tuning runs).
+  const int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
   s->grid = s->NT < want ? s->NT : want;
+  const int tmin = s->NT / s->grid;
+  const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 4, pref.max_depth);
+  s->depth = tmin < 1 ? 1 : tmin > dmax ? dmax : tmin;
   return SVQ_OK;
 }
 
@@ -629,32 +927,44 @@ int launched(const char* fn) {
   return SVQ_OK;
 }
 
-#define SVQ_DISPATCH_GPW(sh, BODY)                         \
-  do {                                                     \
-    if ((sh).gpw == 1) {                                   \
-      constexpr int GPW = 1, MAXW = 8;                     \
-      BODY;                                                \
-    } else if ((sh).gpw == 2) {                            \
-      constexpr int GPW = 2, MAXW = 8;                     \
-      BODY;                                                \
-    } else if ((sh).waves <= 8) {                          \
-      constexpr int GPW = 4, MAXW = 8;                     \
-      BODY;                                                \
-    } else {                                               \
-      constexpr int GPW = 4, MAXW = 16;                    \
-      BODY;                                                \
-    }                                                      \
-  } while (0)
+template <int V>
+using ic = std::integral_constant<int, V>;
 
-#define SVQ_DISPATCH_P(Pv, BODY)        \
-  switch (Pv) {                         \
-    case 1: { constexpr int P = 1; BODY; } break; \
-    case 2: { constexpr int P = 2; BODY; } break; \
-    case 3: { constexpr int P = 3; BODY; } break; \
-    case 4: { constexpr int P = 4; BODY; } break; \
-    case 5: { constexpr int P = 5; BODY; } break; \
-    default: { constexpr int P = 6; BODY; } break; \
+// Calls launch(ic<GPW>, ic<MAXW>, ic<D>) for the shape's compile-time
+// parameters.  Depths above 2 are instantiated only for the 8-wave shapes.
+template <class L>
+void dispatch(const Shape& sh, L&& launch) {
+  auto depth = [&](auto G, auto W, auto DM) {
+    if constexpr (decltype(DM)::value >= 4)
+      if (sh.depth >= 4) return launch(G, W, ic<4>{});
+    if constexpr (decltype(DM)::value >= 3)
+      if (sh.depth == 3) return launch(G, W, ic<3>{});
+    if (sh.depth >= 2) return launch(G, W, ic<2>{});
+    launch(G, W, ic<1>{});
+  };
+  if (sh.gpw == 1)
+    depth(ic<1>{}, ic<8>{}, ic<2>{});
+  else if (sh.gpw == 2)
+    depth(ic<2>{}, ic<8>{}, ic<2>{});
+  else if (sh.waves <= 8)
+    depth(ic<4>{}, ic<8>{}, ic<4>{});
+  else
+    depth(ic<4>{}, ic<16>{}, ic<2>{});
+}
+
+template <class L>
+void dispatch_p(int P, L&& launch) {
+  switch (P) {
+    case 1: launch(ic<1>{}); break;
+    case 2: launch(ic<2>{}); break;
+    case 3: launch(ic<3>{}); break;
+    case 4: launch(ic<4>{}); break;
+    case 5: launch(ic<5>{}); break;
+    default: launch(ic<6>{}); break;
   }
+}
+
+#define SVQ_KARGS(G, W, D) decltype(G)::value, decltype(W)::value, decltype(D)::value
 
 }  // namespace
 
@@ -662,18 +972,21 @@ extern "C" {
 
 size_t svq_lmhead_workspace_bytes(int32_t M) {
   if (M < 1 || M > SVQ_MAX_M) return 0;
-  return (size_t)kLmheadMaxWg * (size_t)M * sizeof(ArgBest);
+  return (size_t)kWsBytes;
 }
 
 int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N, int64_t K, int32_t G,
                void* stream) {
   if (int rc = check_linear("gemv_w4a16", packed, x, y, 1, N, K, G, 0)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 1, &sh)) return rc;
+  if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
-  SVQ_DISPATCH_GPW(sh, hipLaunchKernelGGL((k_gemv_w4a16<GPW, MAXW, false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                                          st, packed, xw, y, (ArgBest*)nullptr, (int)N, sh.KT, sh.NT));
+  dispatch(sh, [&](auto G, auto W, auto D) {
+    hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                       packed, xw, y, (uint8_t*)nullptr, (const int32_t*)nullptr,
+                       (int32_t*)nullptr, (float*)nullptr, (int)N, sh.KT, sh.NT);
+  });
   return launched("gemv_w4a16");
 }
 
@@ -682,12 +995,15 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t
   if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemv_binplane: P=0 must be in 1..6");
   if (int rc = check_linear("gemv_binplane", packed, x, y, 1, N, K, G, P)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 1, &sh)) return rc;
+  if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
-  SVQ_DISPATCH_P(P, SVQ_DISPATCH_GPW(sh, hipLaunchKernelGGL((k_gemv_binplane<GPW, MAXW, P>), dim3(sh.grid),
-                                                            dim3(64 * sh.waves), 0, st, packed, xw, y, (int)N,
-                                                            sh.KT, sh.NT)));
+  dispatch_p(P, [&](auto Pc) {
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS(G, W, D), decltype(Pc)::value>), dim3(sh.grid),
+                         dim3(64 * sh.waves), 0, st, packed, xw, y, (int)N, sh.KT, sh.NT);
+    });
+  });
   return launched("gemv_binplane");
 }
 
@@ -695,11 +1011,14 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
                       int32_t G, void* stream) {
   if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 4, &sh)) return rc;
+  if (int rc = plan(N, K, 4, kPrefGemm, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  SVQ_DISPATCH_GPW(sh, hipLaunchKernelGGL((k_gemm_w4a16<GPW, MAXW, false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                                          st, packed, Xw, Y, (ArgBest*)nullptr, M, (int)N, sh.KT, sh.NT));
+  dispatch(sh, [&](auto G, auto W, auto D) {
+    hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                       packed, Xw, Y, (uint8_t*)nullptr, (const int32_t*)nullptr,
+                       (int32_t*)nullptr, (float*)nullptr, M, (int)N, sh.KT, sh.NT);
+  });
   return launched("gemm_smallm_w4a16");
 }
 
@@ -708,12 +1027,15 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
   if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemm_smallm_binplane: P=0 must be in 1..6");
   if (int rc = check_linear("gemm_smallm_binplane", packed, X, Y, M, N, K, G, P)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 4, &sh)) return rc;
+  if (int rc = plan(N, K, 4, kPrefGemm, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  SVQ_DISPATCH_P(P, SVQ_DISPATCH_GPW(sh, hipLaunchKernelGGL((k_gemm_binplane<GPW, MAXW, P>), dim3(sh.grid),
-                                                            dim3(64 * sh.waves), 0, st, packed, Xw, Y, M, (int)N,
-                                                            sh.KT, sh.NT)));
+  dispatch_p(P, [&](auto Pc) {
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS(G, W, D), decltype(Pc)::value>), dim3(sh.grid),
+                         dim3(64 * sh.waves), 0, st, packed, Xw, Y, M, (int)N, sh.KT, sh.NT);
+    });
+  });
   return launched("gemm_smallm_binplane");
 }
 
@@ -729,21 +1051,24 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N
                      svq_lmhead_workspace_bytes(M), workspace ? workspace_bytes : (size_t)0);
   if (misaligned(workspace, 16)) return svq::fail(SVQ_ERR_ALIGN, "lmhead_argmax: workspace must be 16-byte aligned");
   Shape sh;
-  if (int rc = plan(N, K, M == 1 ? 1 : 4, &sh)) return rc;
-  if (sh.grid > kLmheadMaxWg) sh.grid = kLmheadMaxWg;
+  if (int rc = plan(N, K, M == 1 ? 1 : 4, M == 1 ? kPrefHeadM1 : kPrefHeadM16, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  ArgBest* ws = reinterpret_cast<ArgBest*>(workspace);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   if (M == 1) {
-    SVQ_DISPATCH_GPW(sh, hipLaunchKernelGGL((k_gemv_w4a16<GPW, MAXW, true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                                            st, packed, Xw, (uint16_t*)nullptr, ws, (int)N, sh.KT, sh.NT));
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                         packed, Xw, (uint16_t*)nullptr, ws, row_ids, argmax, maxlogit, (int)N, sh.KT,
+                         sh.NT);
+    });
   } else {
-    SVQ_DISPATCH_GPW(sh, hipLaunchKernelGGL((k_gemm_w4a16<GPW, MAXW, true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                                            st, packed, Xw, (uint16_t*)nullptr, ws, M, (int)N, sh.KT, sh.NT));
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                         packed, Xw, (uint16_t*)nullptr, ws, row_ids, argmax, maxlogit, M, (int)N, sh.KT,
+                         sh.NT);
+    });
   }
-  if (int rc = launched("lmhead_argmax")) return rc;
-  hipLaunchKernelGGL(k_argmax_finalize, dim3(M), dim3(256), 0, st, ws, sh.grid, (int)N, row_ids, argmax, maxlogit);
-  return launched("lmhead_argmax(finalize)");
+  return launched("lmhead_argmax");
 }
 
 int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
@@ -753,7 +1078,8 @@ int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream)
   if (misaligned(src, 16) || misaligned(sink, 4)) return svq::fail(SVQ_ERR_ALIGN, "svq_stream_read: misaligned pointer");
   int cus = 0;
   if (int rc = device_cus(&cus)) return rc;
-  int grid = cus * 8;
+  // One workgroup per CU with eight loads per thread in flight measured best.
+  int grid = cus;
   if (grid > 4096) grid = 4096;
   hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      reinterpret_cast<const uint4*>(src), bytes / 16, sink);

@@ -22,5 +22,6 @@ __attribute__((format(printf, 2, 3))) inline int fail(int code, const char* fmt,
 }
 
 inline int64_t round16(int64_t n) { return (n + 15) / 16 * 16; }
+inline int64_t round4(int64_t n) { return (n + 3) / 4 * 4; }
 
 }  // namespace svq

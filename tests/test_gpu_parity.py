@@ -92,7 +92,7 @@ def run_lmhead(codes, scales, X, row_ids=None, blob=None):
         blob = dev(svq.pack_int4_grouped(codes, scales))
     idx = torch.full((M,), -1, dtype=torch.int32, device="cuda")
     mx = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
     svq.lmhead_argmax(blob, dev(X), M, N, K, idx, mx, ws,
                       row_ids=None if row_ids is None else dev(row_ids))
     torch.cuda.synchronize()
@@ -370,3 +370,22 @@ def test_lmhead_single_row_and_ragged_vocab():
             g = int(idx[m])
             assert 0 <= g < N
             assert Z[m, g] >= r["zmax"][m] - 2 * (REL * A[m].max() + ABS)
+
+
+def test_lmhead_workspace_counter_is_reusable():
+    # One zeroed workspace serves many calls of different M and N; it is
+    # all zero again after every call.
+    rng = np.random.default_rng(50)
+    ws = torch.zeros(svq.lmhead_workspace_bytes(16), dtype=torch.uint8, device="cuda")
+    for it in range(6):
+        M = (1, 16, 3, 1, 16, 7)[it]
+        N = (5000, 2000, 16, 70000, 40000, 999)[it]
+        case = synth.Case("t", "lmhead", M, N, 512)
+        codes, scales, X, rows = synth.make_lmhead(case, 100 + it)
+        blob = dev(svq.pack_int4_grouped(codes, scales))
+        idx = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+        mx = torch.zeros(M, dtype=torch.float32, device="cuda")
+        svq.lmhead_argmax(blob, dev(X), M, N, 512, idx, mx, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), rows.astype(np.int32)), it
+        assert int(ws.count_nonzero().item()) == 0, it
