@@ -149,9 +149,10 @@ def device_int4_blob(N: int, K: int, seed: int, G: int = GROUP, smin: float = 0.
 
     Uniform random code bytes give uniform nibbles, i.e. codes uniform in
     [-8, 7] whatever the byte layout; the scale section gets bf16 values
-    uniform in [smin, smax].  Needs N % 16 == 0 (no padding rows).
+    uniform in [smin, smax].  Needs N % 16 == 0 (no padding rows) and K/G a
+    multiple of 4 (no padded scale entries), so the sections are contiguous.
     """
-    assert N % 16 == 0 and K % G == 0
+    assert N % 16 == 0 and K % G == 0 and (K // G) % 4 == 0
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     code_bytes = N * K // 2
@@ -166,8 +167,9 @@ def device_int4_blob(N: int, K: int, seed: int, G: int = GROUP, smin: float = 0.
 def device_binplane_blob(N: int, K: int, P: int, seed: int, G: int = GROUP, a1=(0.01, 0.03),
                          ratio=(0.3, 0.6), device: str = "cuda"):
     """A packed sign-plane blob drawn on the device: Bernoulli(0.5) sign bits,
-    alpha_1 ~ U(a1), alpha_{p+1} = alpha_p * U(ratio), fp16.  N % 16 == 0."""
-    assert N % 16 == 0 and K % G == 0
+    alpha_1 ~ U(a1), alpha_{p+1} = alpha_p * U(ratio), fp16.  N % 16 == 0 and
+    (K/G) % 4 == 0, as for device_int4_blob."""
+    assert N % 16 == 0 and K % G == 0 and (K // G) % 4 == 0
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     sign_bytes = N * K // 8 * P
