@@ -80,25 +80,51 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// v_and_or_b32 with the mask in an SGPR and the OR constant in a VGPR: the
-// VOP3 encoding takes no literal, so the compiler would otherwise split it
-// into a literal AND and a literal OR.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(orv));
-  return d;
+// An SGPR holding the constant V, produced by a scalar move the compiler
+// cannot see through, so it is not folded back into a literal.
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_sgpr() {
+  uint32_t s;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(s) : "i"(V));
+  return s;
 }
 
-// bf16 pair (136 + c_even, 136 + c_odd) for pair i (k = 2i, 2i+1) of a code
-// dword; `magic` holds kInt4Magic in a VGPR.
-__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i, uint32_t magic) {
-  return and_or(w >> (4 * i), 0x000F000Fu, magic);
+// The same for a VGPR (one move at kernel start; only VALU instructions read
+// it, so no matrix-core hazard depends on this move).
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_vgpr() {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(V));
+  return v;
 }
 
-// bf16 pair (b_even, b_odd) in {-1, +1} for pair ip = 4t + i of a sign dword;
-// `one` holds kOnePair in a VGPR.
-__device__ __forceinline__ uint32_t sign_pair(uint32_t w, int ip, uint32_t one) {
-  return and_or(w << (15 - ip), 0x80008000u, one);
+// Pair decoders: one shift plus one v_and_or_b32 per bf16 pair.  The VOP3
+// encoding of v_and_or_b32 takes no literal and at most one SGPR, so the
+// mask lives in an SGPR and the OR value in a VGPR; with literals the
+// compiler would split the operation into an AND and an OR.
+struct PairDecode {
+  uint32_t mask, orv;
+};
+
+// Nibble pairs: each u = c + 8 becomes the bf16 value 128 + u.
+__device__ __forceinline__ PairDecode int4_decode() {
+  return PairDecode{opaque_sgpr<0x000F000Fu>(), opaque_vgpr<kInt4Magic>()};
+}
+
+// Sign pairs: a clear bit becomes +1, a set bit -1 (the bit lands in the
+// bf16 sign position).
+__device__ __forceinline__ PairDecode sign_decode() {
+  return PairDecode{opaque_sgpr<0x80008000u>(), opaque_vgpr<kOnePair>()};
+}
+
+// bf16 pair (136 + c_even, 136 + c_odd) for pair i (k = 2i, 2i+1) of a code dword.
+__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i, const PairDecode& d) {
+  return ((w >> (4 * i)) & d.mask) | d.orv;
+}
+
+// bf16 pair (b_even, b_odd) in {-1, +1} for pair ip = 4t + i of a sign dword.
+__device__ __forceinline__ uint32_t sign_pair(uint32_t w, int ip, const PairDecode& d) {
+  return ((w << (15 - ip)) & d.mask) | d.orv;
 }
 
 // Sum over the four lanes r, r+16, r+32, r+48 of a wave (the q index), via
@@ -235,34 +261,45 @@ __device__ __forceinline__ uint32_t ld_stream4(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAuxStream);
 }
 
+// GPW consecutive 16-bit scale entries, kept as the raw dwords one load
+// returns (entry gi in the low half of dword gi/2 when gi is even, in the
+// high half when odd) and unpacked at the point of use.
+template <int GPW>
+struct U16Run {
+  uint32_t d[(GPW + 1) / 2];
+
+  __device__ __forceinline__ float bf16(int gi) const {  // entry gi as a bf16 value
+    return __uint_as_float((gi & 1) ? (d[gi >> 1] & 0xFFFF0000u) : (d[gi >> 1] << 16));
+  }
+  __device__ __forceinline__ float f16(int gi) const {  // entry gi as an fp16 value
+    return f16_to_f32((uint16_t)((gi & 1) ? (d[gi >> 1] >> 16) : d[gi >> 1]));
+  }
+};
+
 template <int GPW>
 struct Int4Slot {
-  uint4 c[GPW];      // the lane's 16 code bytes of each group
-  uint32_t s[GPW];   // bf16 scale bits of (row r, group) in the low half
+  uint4 c[GPW];    // the lane's 16 code bytes of each group
+  U16Run<GPW> s;   // bf16 scales of (row r, groups g0 .. g0 + GPW - 1)
 };
 
 template <int GPW, int P>
 struct SignSlot {
   uint32_t w[GPW][P];  // the lane's sign dword of each (group, plane)
-  uint32_t a[P][GPW];  // fp16 alpha bits of (plane, row r, group) in the low half
+  U16Run<GPW> a[P];    // fp16 alphas of (plane, row r, groups g0 ..)
 };
 
-// GPW consecutive 16-bit values with one load (scale rows are padded to a
-// multiple of four entries, so the run is aligned to its own size).
+// One load of a run (scale rows are padded to a multiple of four entries,
+// so the run is aligned to its own size).
 template <int GPW>
-__device__ __forceinline__ void load_u16_run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&v)[GPW]) {
+__device__ __forceinline__ void load_u16_run(__amdgpu_buffer_rsrc_t r, uint32_t off, U16Run<GPW>& v) {
   if constexpr (GPW == 4) {
     const v2u_t t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    v[0] = t.x & 0xFFFFu;
-    v[1] = t.x >> 16;
-    v[2] = t.y & 0xFFFFu;
-    v[3] = t.y >> 16;
+    v.d[0] = t.x;
+    v.d[1] = t.y;
   } else if constexpr (GPW == 2) {
-    const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    v[0] = t & 0xFFFFu;
-    v[1] = t >> 16;
+    v.d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   } else {
-    v[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    v.d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
   }
 }
 
@@ -340,7 +377,7 @@ __device__ __forceinline__ int row_tile(int i) { return blockIdx.x + i * gridDim
 // carried by every decoded code.
 template <int GPW>
 __device__ __forceinline__ float w4a16_tile_partial(const Int4Slot<GPW>& sl, const uint32_t (&xp)[GPW][16],
-                                                    const float (&nxs)[GPW], uint32_t magic) {
+                                                    const float (&nxs)[GPW], const PairDecode& magic) {
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
@@ -350,14 +387,14 @@ __device__ __forceinline__ float w4a16_tile_partial(const Int4Slot<GPW>& sl, con
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc = dot2(int4_pair(w[t], i, magic), xp[gi][4 * t + i], acc);
-    part = fmaf(bf16_to_f32(sl.s[gi]), acc, part);
+    part = fmaf(sl.s.bf16(gi), acc, part);
   }
   return part;
 }
 
 template <int GPW, int P>
 __device__ __forceinline__ float binplane_tile_partial(const SignSlot<GPW, P>& sl, const uint32_t (&xp)[GPW][16],
-                                                       uint32_t one) {
+                                                       const PairDecode& one) {
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi)
@@ -366,29 +403,45 @@ __device__ __forceinline__ float binplane_tile_partial(const SignSlot<GPW, P>& s
       float acc = 0.f;
 #pragma unroll
       for (int ip = 0; ip < 16; ++ip) acc = dot2(sign_pair(sl.w[gi][p], ip, one), xp[gi][ip], acc);
-      part = fmaf(f16_to_f32((uint16_t)sl.a[p][gi]), acc, part);
+      part = fmaf(sl.a[p].f16(gi), acc, part);
     }
   return part;
 }
 
-// Per-tile partials wait in LDS and are combined once per chunk of C tiles,
-// so the waves of a workgroup meet at a barrier only once per chunk.
+// ---------------------------------------------------------------------------
+// Cross-wave combination.  The waves of a workgroup each own a slice of K,
+// so every output of a tile needs one partial from every wave.  Partials
+// wait in LDS and are combined once per chunk of C tiles, so the waves meet
+// at one barrier per chunk.  The staging area is double-buffered (chunk k
+// uses half k % 2): the barrier that ends chunk k + 1 also guarantees that
+// every thread has finished reading half k % 2 before chunk k + 2 writes
+// it.  A wave stages its partial at every loop step, also past the
+// workgroup's last tile (into a discard slot), so the partial is computed
+// before the next loads are issued rather than sunk into the branch that
+// consumes it.
 constexpr int kChunkGemv = 16;  // tiles per chunk, M = 1 kernels
-constexpr int kChunkGemm = 4;   // tiles per chunk, M <= 16 kernels
 
-// M = 1 chunk epilogue: the chunk's ntiles x 16 row sums, each over the
-// waves' partials; thread tid walks outputs tid, tid + blockDim, ... (so a
-// thread's outputs come in increasing row order).
-template <class F>
-__device__ __forceinline__ void chunk_row_sums(const float* red, int nwaves, int ntiles, F&& emit) {
-  // nwaves * 64 is the block size (blockDim.x itself would be a memory read here).
-  for (int o = threadIdx.x; o < ntiles * 16; o += nwaves * 64) {
-    const int c = o >> 4, rr = o & 15;
-    float s = 0.f;
-    for (int w = 0; w < nwaves; ++w) s += red[(c * nwaves + w) * 16 + rr];
-    emit(c, rr, s);  // (tile in chunk, row in tile, value)
+// Tiles per chunk of the M <= 16 kernels (bounded by LDS: 1 KiB per wave and tile).
+template <int MAXW>
+constexpr int chunk_gemm() { return MAXW <= 8 ? 4 : 2; }
+
+template <class V, int C, int MAXW, int L>
+struct ChunkStage {
+  V buf[2 * C + 1][MAXW][L];  // [half * C + tile in chunk][wave][lane]; the last row discards
+
+  __device__ __forceinline__ void put(int i, bool live, int wave, int lane, const V& v) {
+    const int k = live ? ((i / C) & 1) * C + i % C : 2 * C;
+    if (lane < L) buf[k][wave][lane] = v;
   }
-}
+
+  // Sum over the waves of tile c of the chunk that holds tile i.
+  __device__ __forceinline__ V sum(int i, int c, int nwaves, int l) const {
+    const int k = ((i / C) & 1) * C + c;
+    V s = buf[k][0][l];
+    for (int w = 1; w < nwaves; ++w) s += buf[k][w][l];
+    return s;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // lmhead_argmax completion.  A (logit, row) pair becomes one 64-bit key whose
@@ -404,6 +457,7 @@ __device__ __forceinline__ void chunk_row_sums(const float* red, int nwaves, int
 // coherence, and each step is issued only after the step before it has
 // returned, so no cache-wide fence is needed.  A max does not depend on the
 // order of its operands, so neither does the result.
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
 constexpr int kWsKeys = 0;        // M uint64 keys
 constexpr int kWsCounter = 128;   // uint32 completion counter
 constexpr int kWsBytes = 256;
@@ -420,8 +474,10 @@ __device__ __forceinline__ void argmax_complete(unsigned long long key, bool hol
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kWsKeys);
   unsigned* counter = reinterpret_cast<unsigned*>(ws + kWsCounter);
   if (holds_row) {
-    const unsigned long long prev = atomicMax(&keys[m], key);
-    asm volatile("" ::"v"(prev));  // a use of the return value waits until the max has been performed
+    atomicMax(&keys[m], key);
+    // Wait until the atomic has completed before the counter increment
+    // below can be issued (vmcnt(0); the other counters are left free).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   __syncthreads();
   __shared__ int last;
@@ -456,6 +512,8 @@ __global__ void __launch_bounds__(64 * MAXW)
 
   uint32_t xo[GPW];
   load_x_own<GPW>(xw, g0, KT, q, r, xo);
+  // The activation loads go out first: the first tile's work waits on them.
+  __builtin_amdgcn_sched_barrier(0);
   Int4Slot<GPW> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
@@ -465,15 +523,15 @@ __global__ void __launch_bounds__(64 * MAXW)
   }
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
+  __shared__ ChunkStage<float, kChunkGemv, MAXW, 16> stage;
   uint32_t xp[GPW][16];
   expand_x<GPW>(xo, g0, KT, xp);
   float nxs[GPW];
   lane_group_sums<GPW>(xp, nxs);
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) nxs[gi] *= -kInt4Bias;
-  const uint32_t magic = kInt4Magic;
+  const PairDecode magic = int4_decode();
 
-  __shared__ float red[kChunkGemv * MAXW * 16];
   float best_v = -FLT_MAX;
   int best_i = INT_MAX;
   // Every workgroup owns at least one tile (grid <= number of tiles).
@@ -482,20 +540,25 @@ __global__ void __launch_bounds__(64 * MAXW)
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const int ci = i % kChunkGemv;
       // Computed unconditionally (a tile past T holds zeros) so the loop body
-      // stays straight-line; only the staging write is predicated.
+      // stays straight-line.
       const float part = sum_over_q(w4a16_tile_partial<GPW>(ring[j], xp, nxs, magic));
-      if (q == 0 && i < T) red[(ci * nwaves + wave) * 16 + r] = part;
+      stage.put(i, i < T, wave, lane, part);
+      // Slot j is refilled only after its last use, so it keeps its registers.
+      __builtin_amdgcn_sched_barrier(0);
       load_int4_tile<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      const int ci = i % kChunkGemv;
       if (i < T && (ci == kChunkGemv - 1 || i == T - 1)) {
         __syncthreads();
         const int first = i - ci;
-        chunk_row_sums(red, nwaves, ci + 1, [&](int c, int rr, float v) {
-          const int n = 16 * row_tile(first + c) + rr;
+        // Output o = 16c + row of the chunk; a thread meets the same c in
+        // every chunk, so its rows arrive in increasing n.
+        for (int o = threadIdx.x; o < (ci + 1) * 16; o += nwaves * 64) {
+          const float v = stage.sum(i, o >> 4, nwaves, o & 15);
+          const int n = 16 * row_tile(first + (o >> 4)) + (o & 15);
           if (n < N) {
             if constexpr (ARGMAX) {
-              if (v > best_v) {  // a thread's rows arrive in increasing n
+              if (v > best_v) {
                 best_v = v;
                 best_i = n;
               }
@@ -503,14 +566,13 @@ __global__ void __launch_bounds__(64 * MAXW)
               y[n] = f32_to_bf16_rne(v);
             }
           }
-        });
-        __syncthreads();
+        }
       }
     }
     i0 += D;
   } while (i0 < T);
   if constexpr (ARGMAX) {
-    // Lowest index wins ties; each thread saw its rows in increasing order.
+    // Lowest index wins ties.
     __shared__ ArgBest part[MAXW];
     for (int off = 32; off > 0; off >>= 1) {
       const float ov = __shfl_xor(best_v, off);
@@ -546,6 +608,8 @@ __global__ void __launch_bounds__(64 * MAXW)
 
   uint32_t xo[GPW];
   load_x_own<GPW>(xw, g0, KT, q, r, xo);
+  // The activation loads go out first: the first tile's work waits on them.
+  __builtin_amdgcn_sched_barrier(0);
   SignSlot<GPW, P> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
@@ -555,28 +619,29 @@ __global__ void __launch_bounds__(64 * MAXW)
   }
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
+  __shared__ ChunkStage<float, kChunkGemv, MAXW, 16> stage;
   uint32_t xp[GPW][16];
   expand_x<GPW>(xo, g0, KT, xp);
-  const uint32_t one = kOnePair;
+  const PairDecode one = sign_decode();
 
-  __shared__ float red[kChunkGemv * MAXW * 16];
   int i0 = 0;
   do {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const int ci = i % kChunkGemv;
       const float part = sum_over_q(binplane_tile_partial<GPW, P>(ring[j], xp, one));
-      if (q == 0 && i < T) red[(ci * nwaves + wave) * 16 + r] = part;
+      stage.put(i, i < T, wave, lane, part);
+      // Slot j is refilled only after its last use, so it keeps its registers.
+      __builtin_amdgcn_sched_barrier(0);
       load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      const int ci = i % kChunkGemv;
       if (i < T && (ci == kChunkGemv - 1 || i == T - 1)) {
         __syncthreads();
         const int first = i - ci;
-        chunk_row_sums(red, nwaves, ci + 1, [&](int c, int rr, float v) {
-          const int n = 16 * row_tile(first + c) + rr;
-          if (n < N) y[n] = f32_to_bf16_rne(v);
-        });
-        __syncthreads();
+        for (int o = threadIdx.x; o < (ci + 1) * 16; o += nwaves * 64) {
+          const int n = 16 * row_tile(first + (o >> 4)) + (o & 15);
+          if (n < N) y[n] = f32_to_bf16_rne(stage.sum(i, o >> 4, nwaves, o & 15));
+        }
       }
     }
     i0 += D;
@@ -588,29 +653,86 @@ __global__ void __launch_bounds__(64 * MAXW)
 // A = X[m = r][k = 32t + 8q + 0..7] (lane q, r) and B = W^T[k][n = r] from the
 // tile's dword t; D lands as D[m = 4q + i][n = r], i = 0..3.
 
-// Group sums of X per (row m, group g) into LDS, computed by the owning wave.
+// Accumulator start per group: -136 * sum_k X[m][k] over the group for the
+// rows m = 4q + i (i = 0..3) whose outputs this lane's MFMA result holds.
+// Lane (q, r) sums its own 32 values of row r; sum_over_q completes row r's
+// group sum in every lane of that row; lane (q, r) then reads rows 4q + i
+// from lanes 4q + i (whose r is 4q + i).
 template <int GPW>
-__device__ __forceinline__ void x_group_sums_to_lds(const uint32_t (&xa)[GPW][16], int g0, int KT, int q, int r,
-                                                    float (*xs_sh)[65]) {
+__device__ __forceinline__ void x_row_group_init(const uint32_t (&xa)[GPW][16], int q, int g0, int KT,
+                                                 f32x4_t (&cinit)[GPW]) {
   float xs[GPW];
   lane_group_sums<GPW>(xa, xs);
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const float s = sum_over_q(xs[gi]);
-    if (q == 0 && g0 + gi < KT) xs_sh[r][g0 + gi] = s;
+    const float srow = sum_over_q(xs[gi]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = __shfl(srow, 4 * q + i);
+      cinit[gi][i] = g0 + gi < KT ? -kInt4Bias * v : 0.f;
+    }
   }
 }
 
-// M <= 16 chunk epilogue: the chunk's ntiles x 256 outputs, each the sum of
-// the waves' partials; thread tid walks outputs tid, tid + blockDim, ...
-template <class F>
-__device__ __forceinline__ void chunk_tile_sums(const float* red, int nwaves, int ntiles, F&& emit) {
-  // nwaves * 64 is the block size (blockDim.x itself would be a memory read here).
-  for (int o = threadIdx.x; o < ntiles * 256; o += nwaves * 64) {
-    const int c = o >> 8, e = o & 255;
-    float s = 0.f;
-    for (int w = 0; w < nwaves; ++w) s += red[(c * nwaves + w) * 256 + e];
-    emit(c, e >> 4, e & 15, s);  // (tile in chunk, m, n in tile, value)
+// Running greedy choice per query row m = 4q + ii of a lane (M <= 16 heads).
+struct RowBest4 {
+  float v[4];
+  int idx[4];
+};
+
+// Combines the lanes' and waves' running bests (lowest index wins ties) and
+// completes the launch's argmax.
+template <int MAXW>
+__device__ __forceinline__ void gemm_argmax_epilogue(RowBest4& b, int wave, int lane, int nwaves, uint8_t* ws,
+                                                     int M, int N, const int32_t* __restrict__ row_ids,
+                                                     int32_t* __restrict__ out_idx, float* __restrict__ out_max) {
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+    for (int off = 8; off > 0; off >>= 1) {  // over the 16 lanes of one q
+      const float ov = __shfl_xor(b.v[ii], off);
+      const int oi = __shfl_xor(b.idx[ii], off);
+      if (better(ov, oi, b.v[ii], b.idx[ii])) {
+        b.v[ii] = ov;
+        b.idx[ii] = oi;
+      }
+    }
+  __shared__ ArgBest fin[MAXW][16];  // [wave][query row]
+  if ((lane & 15) == 0)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) fin[wave][4 * (lane >> 4) + ii] = ArgBest{b.v[ii], b.idx[ii]};
+  __syncthreads();
+  float bvv = -FLT_MAX;
+  int bii = INT_MAX;
+  if ((int)threadIdx.x < M)
+    for (int w = 0; w < nwaves; ++w)
+      if (better(fin[w][threadIdx.x].v, fin[w][threadIdx.x].idx, bvv, bii)) {
+        bvv = fin[w][threadIdx.x].v;
+        bii = fin[w][threadIdx.x].idx;
+      }
+  argmax_complete(argmax_key(bvv, bii), (int)threadIdx.x < M && bii < N, threadIdx.x, ws, M, N, row_ids, out_idx,
+                  out_max);
+}
+
+// Emits a completed 16 x 16 output tile held as lane (q, r) -> rows 4q + ii,
+// column r of row tile rt.
+template <bool ARGMAX>
+__device__ __forceinline__ void gemm_emit(const float4& tot, int q, int r, int rt, int M, int N,
+                                          uint16_t* __restrict__ Y, RowBest4& best) {
+  const int n = 16 * rt + r;
+  const float v[4] = {tot.x, tot.y, tot.z, tot.w};
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int m = 4 * q + ii;
+    if (m < M && n < N) {
+      if constexpr (ARGMAX) {
+        if (v[ii] > best.v[ii]) {  // a lane's columns arrive in increasing n
+          best.v[ii] = v[ii];
+          best.idx[ii] = n;
+        }
+      } else {
+        Y[(size_t)m * N + n] = f32_to_bf16_rne(v[ii]);
+      }
+    }
   }
 }
 
@@ -627,6 +749,8 @@ __global__ void __launch_bounds__(64 * MAXW)
 
   uint32_t xa[GPW][16];
   load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
+  // The activation loads go out first: the first tile's work waits on them.
+  __builtin_amdgcn_sched_barrier(0);
   Int4Slot<GPW> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
@@ -636,101 +760,59 @@ __global__ void __launch_bounds__(64 * MAXW)
   }
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int C = chunk_gemm<MAXW>();
+  __shared__ ChunkStage<float4, C, MAXW, 64> stage;
   mask_x_pairs<GPW>(r, M, g0, KT, xa);
+  f32x4_t cinit[GPW];
+  x_row_group_init<GPW>(xa, q, g0, KT, cinit);
+  const PairDecode magic = int4_decode();
 
-  __shared__ float xs_sh[16][65];
-  __shared__ float red[kChunkGemm * MAXW * 256];
-  // Every (row, group) entry read below is written by the wave owning the group.
-  x_group_sums_to_lds<GPW>(xa, g0, KT, q, r, xs_sh);
-  __syncthreads();
-  f32x4_t cinit[GPW];  // -136 * sum_k X[m][k] over the group, for m = 4q + i
+  RowBest4 best;
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cinit[gi][i] = g0 + gi < KT ? -kInt4Bias * xs_sh[4 * q + i][g0 + gi] : 0.f;
-  const uint32_t magic = kInt4Magic;
-
-  // Running best per (query row, n slot): thread tid < 256 owns m = tid >> 4.
-  float best_v = -FLT_MAX;
-  int best_i = INT_MAX;
+  for (int ii = 0; ii < 4; ++ii) {
+    best.v[ii] = -FLT_MAX;
+    best.idx[ii] = INT_MAX;
+  }
   int i0 = 0;
   do {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const int ci = i % kChunkGemm;
-      {
-        float yv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) {
-          const uint4 cw = ring[j].c[gi];
-          const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-          f32x4_t c = cinit[gi];
+      for (int gi = 0; gi < GPW; ++gi) {
+        const uint4 cw = ring[j].c[gi];
+        const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+        f32x4_t c = cinit[gi];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t bq[4] = {int4_pair(w[t], 0, magic), int4_pair(w[t], 1, magic),
-                                    int4_pair(w[t], 2, magic), int4_pair(w[t], 3, magic)};
-            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
-          }
-          const float s = bf16_to_f32(ring[j].s[gi]);
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) yv[ii] = fmaf(s, c[ii], yv[ii]);
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t bq[4] = {int4_pair(w[t], 0, magic), int4_pair(w[t], 1, magic),
+                                  int4_pair(w[t], 2, magic), int4_pair(w[t], 3, magic)};
+          c = mfma16x16x32(&xa[gi][4 * t], bq, c);
         }
-        float* rp = red + (ci * nwaves + wave) * 256;
-        if (i < T)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) rp[(4 * q + ii) * 16 + r] = yv[ii];
+        const float sc = ring[j].s.bf16(gi);
+        yv.x = fmaf(sc, c[0], yv.x);
+        yv.y = fmaf(sc, c[1], yv.y);
+        yv.z = fmaf(sc, c[2], yv.z);
+        yv.w = fmaf(sc, c[3], yv.w);
       }
+      stage.put(i, i < T, wave, lane, yv);
+      // Slot j is refilled only after its last use, so it keeps its registers.
+      __builtin_amdgcn_sched_barrier(0);
       load_int4_tile<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
-      if (i < T && (ci == kChunkGemm - 1 || i == T - 1)) {
+      const int ci = i % C;
+      if (i < T && (ci == C - 1 || i == T - 1)) {
         __syncthreads();
         const int first = i - ci;
-        chunk_tile_sums(red, nwaves, ci + 1, [&](int c, int m, int nn, float v) {
-          const int n = 16 * row_tile(first + c) + nn;
-          if (m < M && n < N) {
-            if constexpr (ARGMAX) {
-              // thread tid's outputs always share m = (tid >> 4) & 15 and come in increasing n
-              if (v > best_v) {
-                best_v = v;
-                best_i = n;
-              }
-            } else {
-              Y[(size_t)m * N + n] = f32_to_bf16_rne(v);
-            }
-          }
-        });
-        __syncthreads();
+        // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
+        // same outputs of every tile, so its columns arrive in increasing n.
+        if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, best);
       }
     }
     i0 += D;
   } while (i0 < T);
-  if constexpr (ARGMAX) {
-    // Thread tid held outputs with m = (tid >> 4) & 15; combine the 16 n slots
-    // of a row within the wave, then the waves through LDS.
-    for (int off = 8; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(best_v, off);
-      const int oi = __shfl_xor(best_i, off);
-      if (better(ov, oi, best_v, best_i)) {
-        best_v = ov;
-        best_i = oi;
-      }
-    }
-    __shared__ ArgBest part[MAXW * 4];
-    if ((lane & 15) == 0) part[wave * 4 + (lane >> 4)] = ArgBest{best_v, best_i};
-    __syncthreads();
-    float bvv = -FLT_MAX;
-    int bii = INT_MAX;
-    if ((int)threadIdx.x < M) {
-      // slot (wave, lane >> 4) holds m = (wave * 4 + (lane >> 4)) & 15
-      for (int sl = threadIdx.x; sl < nwaves * 4; sl += 16)
-        if (better(part[sl].v, part[sl].idx, bvv, bii)) {
-          bvv = part[sl].v;
-          bii = part[sl].idx;
-        }
-    }
-    argmax_complete(argmax_key(bvv, bii), (int)threadIdx.x < M && bii < N, threadIdx.x, ws, M, N, row_ids,
-                    out_idx, out_max);
-  }
+  if constexpr (ARGMAX)
+    gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, row_ids, out_idx, out_max);
 }
 
 template <int GPW, int MAXW, int D, int P>
@@ -745,6 +827,8 @@ __global__ void __launch_bounds__(64 * MAXW)
 
   uint32_t xa[GPW][16];
   load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
+  // The activation loads go out first: the first tile's work waits on them.
+  __builtin_amdgcn_sched_barrier(0);
   SignSlot<GPW, P> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
@@ -754,48 +838,47 @@ __global__ void __launch_bounds__(64 * MAXW)
   }
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int C = chunk_gemm<MAXW>();
+  __shared__ ChunkStage<float4, C, MAXW, 64> stage;
   mask_x_pairs<GPW>(r, M, g0, KT, xa);
-  const uint32_t one = kOnePair;
+  const PairDecode one = sign_decode();
 
-  __shared__ float red[kChunkGemm * MAXW * 256];
+  RowBest4 unused;
   int i0 = 0;
   do {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const int ci = i % kChunkGemm;
-      {
-        float yv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int gi = 0; gi < GPW; ++gi)
+      for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
-          for (int p = 0; p < P; ++p) {
-            const uint32_t wp = ring[j].w[gi][p];
-            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < P; ++p) {
+          const uint32_t wp = ring[j].w[gi][p];
+          f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, one), sign_pair(wp, 4 * t + 1, one),
-                                      sign_pair(wp, 4 * t + 2, one), sign_pair(wp, 4 * t + 3, one)};
-              c = mfma16x16x32(&xa[gi][4 * t], bq, c);
-            }
-            const float a = f16_to_f32((uint16_t)ring[j].a[p][gi]);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) yv[ii] = fmaf(a, c[ii], yv[ii]);
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, one), sign_pair(wp, 4 * t + 1, one),
+                                    sign_pair(wp, 4 * t + 2, one), sign_pair(wp, 4 * t + 3, one)};
+            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
           }
-        float* rp = red + (ci * nwaves + wave) * 256;
-        if (i < T)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) rp[(4 * q + ii) * 16 + r] = yv[ii];
-      }
+          const float a = ring[j].a[p].f16(gi);
+          yv.x = fmaf(a, c[0], yv.x);
+          yv.y = fmaf(a, c[1], yv.y);
+          yv.z = fmaf(a, c[2], yv.z);
+          yv.w = fmaf(a, c[3], yv.w);
+        }
+      stage.put(i, i < T, wave, lane, yv);
+      // Slot j is refilled only after its last use, so it keeps its registers.
+      __builtin_amdgcn_sched_barrier(0);
       load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
-      if (i < T && (ci == kChunkGemm - 1 || i == T - 1)) {
+      const int ci = i % C;
+      if (i < T && (ci == C - 1 || i == T - 1)) {
         __syncthreads();
         const int first = i - ci;
-        chunk_tile_sums(red, nwaves, ci + 1, [&](int c, int m, int nn, float v) {
-          const int n = 16 * row_tile(first + c) + nn;
-          if (m < M && n < N) Y[(size_t)m * N + n] = f32_to_bf16_rne(v);
-        });
-        __syncthreads();
+        // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
+        // same outputs of every tile, so its columns arrive in increasing n.
+        if (wave <= ci) gemm_emit<false>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, unused);
       }
     }
     i0 += D;
