@@ -973,19 +973,23 @@ int env_int(const char* name, int lo, int hi, int dflt) {
 // CU walking the row tiles in grid-stride order; the ring depth is the number
 // of tiles whose loads each wave keeps in flight, at most the number of tiles
 // every workgroup owns (so the pipeline tail stays short).
-// wave_quantum: the M <= 16 kernels walk each 16x16 output tile with a
-// multiple of 256 threads (so a thread always meets the same query row), so
-// their workgroups carry a multiple of four waves.
-// Measured on MI355X (rocprofv3, decode/verify/head shapes at K = 4096): the
-// M = 1 mat-vecs run best at two workgroups per CU with a ring of <= 2 tiles,
-// the M <= 16 kernels at one workgroup per CU with a ring of <= 3 tiles.
+// wave_quantum: the M <= 16 kernels finish the tiles of a chunk one wave per
+// tile (up to four tiles), so their workgroups carry a multiple of four waves.
+// Measured on MI355X (rocprofv3 kernel traces of the decode, verify and head
+// shapes at K = 4096, sweeping both knobs): the M = 1 mat-vecs run best at
+// two workgroups per CU with a ring of <= 2 tiles, everything else at one
+// workgroup per CU; a ring of 2 tiles already keeps more bytes in flight
+// than the memory system's bandwidth-latency product, and deeper rings were
+// slower for the W4A16 kernels (the sign-plane verify kernel, with more
+// arithmetic per byte, gains a little from 3).
 struct LaunchPref {
   int wgs_per_cu, max_depth;
 };
 constexpr LaunchPref kPrefGemv = {2, 2};
-constexpr LaunchPref kPrefGemm = {1, 3};
+constexpr LaunchPref kPrefGemmW4 = {1, 2};
+constexpr LaunchPref kPrefGemmPlanes = {1, 3};
 constexpr LaunchPref kPrefHeadM1 = {1, 2};
-constexpr LaunchPref kPrefHeadM16 = {1, 3};
+constexpr LaunchPref kPrefHeadM16 = {1, 2};
 
 int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* s) {
   int cus = 0;
@@ -999,7 +1003,7 @@ int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* s) {
   const int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
   s->grid = s->NT < want ? s->NT : want;
   const int tmin = s->NT / s->grid;
-  const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 4, pref.max_depth);
+  const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 6, pref.max_depth);
   s->depth = tmin < 1 ? 1 : tmin > dmax ? dmax : tmin;
   return SVQ_OK;
 }
@@ -1018,8 +1022,12 @@ using ic = std::integral_constant<int, V>;
 template <class L>
 void dispatch(const Shape& sh, L&& launch) {
   auto depth = [&](auto G, auto W, auto DM) {
+    if constexpr (decltype(DM)::value >= 6)
+      if (sh.depth >= 6) return launch(G, W, ic<6>{});
+    if constexpr (decltype(DM)::value >= 5)
+      if (sh.depth == 5) return launch(G, W, ic<5>{});
     if constexpr (decltype(DM)::value >= 4)
-      if (sh.depth >= 4) return launch(G, W, ic<4>{});
+      if (sh.depth == 4) return launch(G, W, ic<4>{});
     if constexpr (decltype(DM)::value >= 3)
       if (sh.depth == 3) return launch(G, W, ic<3>{});
     if (sh.depth >= 2) return launch(G, W, ic<2>{});
@@ -1030,7 +1038,7 @@ void dispatch(const Shape& sh, L&& launch) {
   else if (sh.gpw == 2)
     depth(ic<2>{}, ic<8>{}, ic<2>{});
   else if (sh.waves <= 8)
-    depth(ic<4>{}, ic<8>{}, ic<4>{});
+    depth(ic<4>{}, ic<8>{}, ic<6>{});
   else
     depth(ic<4>{}, ic<16>{}, ic<2>{});
 }
@@ -1048,6 +1056,16 @@ void dispatch_p(int P, L&& launch) {
 }
 
 #define SVQ_KARGS(G, W, D) decltype(G)::value, decltype(W)::value, decltype(D)::value
+
+// Deepest ring the sign-plane kernels keep in registers without spilling:
+// a slot holds P sign dwords and P scale runs per group.
+template <int P>
+constexpr int max_depth_planes() { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
+#define SVQ_KARGS_P(G, W, D, Pc)                                                                        \
+  decltype(G)::value, decltype(W)::value,                                                              \
+      (decltype(D)::value < max_depth_planes<decltype(Pc)::value>() ? decltype(D)::value               \
+                                                                    : max_depth_planes<decltype(Pc)::value>()), \
+      decltype(Pc)::value
 
 }  // namespace
 
@@ -1083,7 +1101,7 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
   dispatch_p(P, [&](auto Pc) {
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS(G, W, D), decltype(Pc)::value>), dim3(sh.grid),
+      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc)>), dim3(sh.grid),
                          dim3(64 * sh.waves), 0, st, packed, xw, y, (int)N, sh.KT, sh.NT);
     });
   });
@@ -1094,7 +1112,7 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
                       int32_t G, void* stream) {
   if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 4, kPrefGemm, &sh)) return rc;
+  if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch(sh, [&](auto G, auto W, auto D) {
@@ -1110,12 +1128,12 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
   if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemm_smallm_binplane: P=0 must be in 1..6");
   if (int rc = check_linear("gemm_smallm_binplane", packed, X, Y, M, N, K, G, P)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 4, kPrefGemm, &sh)) return rc;
+  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch_p(P, [&](auto Pc) {
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS(G, W, D), decltype(Pc)::value>), dim3(sh.grid),
+      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc)>), dim3(sh.grid),
                          dim3(64 * sh.waves), 0, st, packed, Xw, Y, M, (int)N, sh.KT, sh.NT);
     });
   });
