@@ -198,12 +198,17 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M,
 
 /*
  * svq_stream_read -- DEVICE pointers, asynchronous on `stream`.
- * Measurement aid, not part of the method: reads `bytes` (a multiple of 16)
- * from `src` with 16-byte loads and writes one uint32 checksum per workgroup
- * into `sink` (>= 4096 * 4 bytes).  Gives the achievable streaming-read
- * ceiling and the counter calibration for the same launch shape.
+ * Measurement aid, not part of the method: reads `bytes` (a positive
+ * multiple of 16 below 2 GiB) from `src` with non-temporal 16-byte loads,
+ * eight per thread in flight, on wgs_per_cu workgroups of 256 threads per
+ * CU (0 means 1; at most 8), and writes one uint32 checksum per workgroup
+ * into `sink` (>= 8 * CUs * 4 bytes).  Gives the achievable streaming-read
+ * ceiling for a buffer of that size and the counter calibration.
+ * Errors: NULL, SHAPE (size, wgs_per_cu), ALIGN (src 16-byte, sink 4-byte),
+ * HIP.
  */
-int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+int svq_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                    int32_t wgs_per_cu, void* stream);
 
 #ifdef __cplusplus
 }

@@ -68,7 +68,7 @@ def load():
         "gemm_smallm_w4a16": ([V, V, V, I32, I64, I64, I32, V], ctypes.c_int),
         "gemm_smallm_binplane": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
         "lmhead_argmax": ([V, V, I32, I64, I64, I32, V, V, V, V, SZ, V], ctypes.c_int),
-        "svq_stream_read": ([V, SZ, V, V], ctypes.c_int),
+        "svq_stream_read": ([V, SZ, V, I32, V], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -188,5 +188,6 @@ def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def svq_stream_read(src, nbytes: int, sink, stream=None) -> None:
-    _check("svq_stream_read", load().svq_stream_read(_dev_ptr(src), nbytes, _dev_ptr(sink), _stream(stream)))
+def svq_stream_read(src, nbytes: int, sink, wgs_per_cu: int = 0, stream=None) -> None:
+    _check("svq_stream_read", load().svq_stream_read(_dev_ptr(src), nbytes, _dev_ptr(sink), wgs_per_cu,
+                                                     _stream(stream)))

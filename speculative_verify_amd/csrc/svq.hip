@@ -885,14 +885,16 @@ __global__ void __launch_bounds__(64 * MAXW)
   } while (i0 < T);
 }
 
-// Streaming-read ceiling: non-temporal 16-byte loads, eight per thread in
-// flight, over `n16` chunks; one checksum per workgroup keeps the loads live.
+// Streaming-read ceiling: every thread keeps U non-temporal 16-byte loads in
+// flight over a grid-stride walk of the buffer; the last partial round
+// issues its (guarded) loads together as well, so the probe streams any size
+// at full depth.  One checksum per workgroup keeps the loads live.
 __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ src, size_t n16,
                                                      uint32_t* __restrict__ sink) {
   constexpr int U = 8;
   uint32_t acc = 0;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     v4u_t v[U];
 #pragma unroll
@@ -900,9 +902,15 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ s
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  {
+    v4u_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = v4u_t{0u, 0u, 0u, 0u};
+      if (i + u * stride < n16) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + i + u * stride));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
   __shared__ uint32_t part[4];
@@ -1172,17 +1180,24 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N
   return launched("lmhead_argmax");
 }
 
-int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t wgs_per_cu, void* stream) {
   svq::clear_error();
   if (!src || !sink) return svq::fail(SVQ_ERR_NULL, "svq_stream_read: NULL pointer");
-  if (bytes == 0 || bytes % 16) return svq::fail(SVQ_ERR_SHAPE, "svq_stream_read: bytes must be a positive multiple of 16");
+  if (bytes == 0 || bytes % 16 || bytes >= ((size_t)1 << 31))
+    return svq::fail(SVQ_ERR_SHAPE, "svq_stream_read: bytes must be a positive multiple of 16 below 2 GiB");
+  if (wgs_per_cu < 0 || wgs_per_cu > 8)
+    return svq::fail(SVQ_ERR_SHAPE, "svq_stream_read: wgs_per_cu must be in 0..8 (got %d)", wgs_per_cu);
   if (misaligned(src, 16) || misaligned(sink, 4)) return svq::fail(SVQ_ERR_ALIGN, "svq_stream_read: misaligned pointer");
   int cus = 0;
   if (int rc = device_cus(&cus)) return rc;
-  // One workgroup per CU with eight loads per thread in flight measured best.
-  int grid = cus;
-  if (grid > 4096) grid = 4096;
-  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+  // Eight loads per thread in flight; wgs_per_cu workgroups per CU (0: one,
+  // which measured best for large buffers); fewer when the buffer is smaller
+  // than one full round.
+  const size_t per_wg = (size_t)256 * 16 * 8;
+  size_t grid = (bytes + per_wg - 1) / per_wg;
+  const size_t cap = (size_t)cus * (wgs_per_cu == 0 ? 1 : wgs_per_cu);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      reinterpret_cast<const uint4*>(src), bytes / 16, sink);
   return launched("svq_stream_read");
 }

@@ -60,7 +60,8 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, A, A, 8, None), -5),
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, None, A, 1 << 20, None), -1),
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, A + 2, A, A, A, 1 << 20, None), -3),
-    (lambda l: l.svq_stream_read(A, 100, A, None), -2),
+    (lambda l: l.svq_stream_read(A, 100, A, 0, None), -2),
+    (lambda l: l.svq_stream_read(A, 1024, A, 9, None), -2),
 ])
 def test_argument_validation(call, code):
     lib = svq.load()
