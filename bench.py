@@ -8,7 +8,9 @@ on its own freshly drawn weights:
   gemv_binplane         M=1  K=4096 N=12288 P=3    (decode, sign planes)
   gemm_smallm_w4a16     M=16 K=4096 N=4096, 12288  (verify block)
   gemm_smallm_binplane  M=16 K=4096 N=4096, 12288  (verify block, P=3)
-  lmhead_argmax         M=1, 16  K=4096 N=32768 (trimmed), 248320 (full)
+  lmhead_argmax         M=1  K=4096 N=32768 (trimmed), 248320 (full); M=16 N=32768
+  lmhead_verify_greedy  M=16 K=4096 N=248320 (the verify step's head with
+                        greedy acceptance of 15 drafted tokens fused)
 
 The metric is weight bytes streamed per second (packed weights + scales +
 activations + outputs, the algorithmic bytes of each call) over the whole
@@ -91,7 +93,7 @@ def build_step(svq, synth, torch):
 
     heads = {}
 
-    def head(M, N):
+    def head(M, N, verify=False):
         def make(blob=None):
             if blob is None:
                 blob = synth.device_int4_blob(N, K, nxt())
@@ -99,12 +101,18 @@ def build_step(svq, synth, torch):
             idx = torch.empty(M, dtype=torch.int32, device="cuda")
             mx = torch.empty(M, dtype=torch.float32, device="cuda")
             ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
-            return lambda: svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
+            if not verify:
+                return lambda: svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
+            draft = torch.randint(0, N, (M - 1,), dtype=torch.int32, device="cuda")
+            tau = torch.empty(1, dtype=torch.int32, device="cuda")
+            return lambda: svq.lmhead_verify_greedy(blob, X, M, N, K, draft, idx, mx, tau, ws)
 
         # The M = 1 and M = 16 heads of one vocabulary share one weight blob.
         if N not in heads:
             heads[N] = synth.device_int4_blob(N, K, nxt())
-        calls.append((f"lmhead_argmax_m{M}_n{N}", alg_bytes_head(M, N), make(heads[N]), make))
+        name = f"lmhead_verify_greedy_m{M}_n{N}" if verify else f"lmhead_argmax_m{M}_n{N}"
+        nbytes = alg_bytes_head(M, N) + (4 * (M - 1) + 4 if verify else 0)
+        calls.append((name, nbytes, make(heads[N]), make))
 
     # Order: the full head (524 MB) sits between uses of anything small, so no
     # call finds its weights in the last-level cache from the previous step.
@@ -116,8 +124,8 @@ def build_step(svq, synth, torch):
     lin("binplane", 16, 4096, 3)
     lin("binplane", 16, 12288, 3)
     head(1, 32768)
-    head(16, 248320)
-    head(16, 32768)
+    head(16, 248320, verify=True)  # the verify step: full vocabulary, greedy acceptance fused
+    head(16, 32768)                # a block drafter on the trimmed head
     return calls
 
 
@@ -311,7 +319,8 @@ def main():
         "config": {
             "workload": "decode+verify+lmhead step, K=4096, group 128: W4A16 GEMV M1 N12288; "
                         "binary-plane P3 GEMV M1 N12288; W4A16 and P3 verify GEMM M16 N4096/N12288; "
-                        "W4A16 LM head + argmax M1/M16 N32768 (trimmed) and N248320 (full)",
+                        "W4A16 LM head + argmax M1 N248320 (full) and M1/M16 N32768 (trimmed); "
+                        "verify head M16 N248320 with fused greedy acceptance",
             "step_bytes": step_bytes,
             "frac_hbm_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
@@ -331,7 +340,7 @@ def main():
         "verify_over_decode_time": {
             "w4a16_n12288": ratio("gemm_smallm_w4a16_m16_n12288", "gemv_w4a16_m1_n12288"),
             "binplane_n12288": ratio("gemm_smallm_binplane_p3_m16_n12288", "gemv_binplane_p3_m1_n12288"),
-            "lmhead_n248320": ratio("lmhead_argmax_m16_n248320", "lmhead_argmax_m1_n248320"),
+            "lmhead_n248320": ratio("lmhead_verify_greedy_m16_n248320", "lmhead_argmax_m1_n248320"),
         },
     }
     traffic = load_traffic(dom)

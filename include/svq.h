@@ -197,6 +197,46 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * Greedy acceptance of a verified block (DFlash summary sec. 4.1: a cycle
+ * drafts gamma tokens, the target checks them in one parallel pass and
+ * accepts tau in [1, gamma + 1] tokens; the report's sec. 2.2 for parallel
+ * verification).  The block holds M = gamma + 1 query rows
+ * [anchor, d_1, ..., d_{M-1}]; row j's greedy token t_j is the target's
+ * prediction for the position after row j, so d_{j+1} is accepted while every
+ * earlier draft was accepted and t_j == d_{j+1}.  With a the number of
+ * accepted drafts, tau = a + 1 and the tokens to emit are t_0 .. t_a (the
+ * accepted drafts followed by the target's own next token).  A row without a
+ * valid maximum (id -1) ends the accepted prefix.
+ */
+
+/*
+ * lmhead_verify_greedy -- DEVICE pointers, asynchronous on `stream`.
+ * lmhead_argmax over the block, then, in the same launch (the workgroup that
+ * completes the argmax), greedy acceptance:
+ *   draft_ids   [M-1] int32 token ids d_1 .. d_{M-1}, 4-byte aligned; may be
+ *               NULL when M == 1
+ *   accept_len  [1] int32: tau; argmax[0 .. tau-1] are the tokens to emit
+ * Other arguments, the workspace contract and errors as lmhead_argmax.
+ */
+int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M,
+                         int64_t N, int64_t K, int32_t G,
+                         const int32_t* row_ids, const int32_t* draft_ids,
+                         int32_t* argmax, float* maxlogit, int32_t* accept_len,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * verify_greedy -- DEVICE pointers, asynchronous on `stream`.
+ * Greedy acceptance alone, for target tokens produced elsewhere:
+ *   target_ids  [M] int32 t_0 .. t_{M-1}
+ *   draft_ids   [M-1] int32 d_1 .. d_{M-1} (may be NULL when M == 1)
+ *   accept_len  [1] int32: tau
+ * 1 <= M <= 16; pointers 4-byte aligned.
+ * Errors: NULL, SHAPE (M), ALIGN, HIP.
+ */
+int verify_greedy(const int32_t* target_ids, const int32_t* draft_ids,
+                  int32_t M, int32_t* accept_len, void* stream);
+
+/*
  * svq_stream_read -- DEVICE pointers, asynchronous on `stream`.
  * Measurement aid, not part of the method: reads `bytes` (a positive
  * multiple of 16 below 2 GiB) from `src` with non-temporal 16-byte loads,

@@ -70,6 +70,8 @@ def _load():
     lib.oracle_linear_binplane.restype = ctypes.c_int
     lib.oracle_argmax_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.oracle_argmax_w4a16.restype = ctypes.c_int
+    lib.oracle_verify_greedy.argtypes = [P, P, I64]
+    lib.oracle_verify_greedy.restype = ctypes.c_int
     lib.oracle_int4_blob_bytes.argtypes = [I64, I64]
     lib.oracle_int4_blob_bytes.restype = I64
     lib.oracle_binplane_blob_bytes.argtypes = [I64, I64, I64]
@@ -170,6 +172,16 @@ def argmax_w4a16(codes, scales, x, G: int = 128, row_ids=None):
     if rc:
         raise ValueError(f"oracle_argmax_w4a16 rc={rc}")
     return dict(out=out, idx=idx, zmax=zmax, amax=amax, zsecond=zsec)
+
+
+def verify_greedy(target, draft) -> int:
+    """tau for target tokens [M] and drafted tokens [M-1]."""
+    t = _c(np.atleast_1d(target), np.int32)
+    M = t.shape[0]
+    d = _c(np.atleast_1d(draft) if M > 1 else np.zeros(1, np.int32), np.int32)
+    if M > 1 and d.shape[0] != M - 1:
+        raise ValueError("draft must hold M - 1 tokens")
+    return int(_load().oracle_verify_greedy(_ptr(t), _ptr(d), M))
 
 
 def pack_int4(codes, scales) -> np.ndarray:

@@ -233,6 +233,27 @@ int oracle_argmax_w4a16(const int8_t* codes, const uint16_t* scales,
   return rc;
 }
 
+/*
+ * Greedy acceptance of a verified block (DFlash summary sec. 4.1: the draft
+ * proposes gamma tokens, the target verifies them in one parallel pass and
+ * tau in [1, gamma + 1] tokens are accepted per cycle; greedy decoding keeps
+ * the target's argmax).  The block has M = gamma + 1 rows: the anchor, then
+ * the drafted tokens d_1 .. d_{M-1} (draft[0 .. M-2]).  target[j] is the
+ * target's greedy token for the position after row j.  Walking the drafts in
+ * order, draft d_{j+1} is accepted when every earlier draft was accepted and
+ * it equals target[j]; tau counts the accepted drafts plus the one token the
+ * target contributes after them.  A target id of -1 (no valid maximum) is
+ * never equal to a draft, as drafted ids are token ids >= 0.
+ */
+int oracle_verify_greedy(const int32_t* target, const int32_t* draft, int64_t M) {
+  int64_t accepted = 0;
+  for (int64_t j = 0; j + 1 < M; ++j) {
+    if (target[j] < 0 || target[j] != draft[j]) break;
+    accepted += 1;
+  }
+  return (int)(accepted + 1);
+}
+
 /* ---- packed layouts, stated one element at a time (see header) ---- */
 
 static void or_dword(uint8_t* blob, int64_t byte_off, uint32_t v) {

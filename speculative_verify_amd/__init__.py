@@ -10,7 +10,8 @@ Functions (same names as the C ABI):
   pack_int4_grouped, unpack_int4_grouped, pack_binary_planes,
   unpack_binary_planes                       host numpy arrays
   gemv_w4a16, gemv_binplane, gemm_smallm_w4a16, gemm_smallm_binplane,
-  lmhead_argmax, svq_stream_read             torch CUDA tensors
+  lmhead_argmax, lmhead_verify_greedy, verify_greedy,
+  svq_stream_read                            torch CUDA tensors
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ __all__ = [
     "SvqError", "lib_path", "load", "int4_packed_bytes", "binplane_packed_bytes",
     "lmhead_workspace_bytes", "pack_int4_grouped", "unpack_int4_grouped",
     "pack_binary_planes", "unpack_binary_planes", "gemv_w4a16", "gemv_binplane",
-    "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "svq_stream_read",
+    "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_verify_greedy",
+    "verify_greedy", "svq_stream_read",
 ]
 
 GROUP = 128
@@ -68,6 +70,8 @@ def load():
         "gemm_smallm_w4a16": ([V, V, V, I32, I64, I64, I32, V], ctypes.c_int),
         "gemm_smallm_binplane": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
         "lmhead_argmax": ([V, V, I32, I64, I64, I32, V, V, V, V, SZ, V], ctypes.c_int),
+        "lmhead_verify_greedy": ([V, V, I32, I64, I64, I32, V, V, V, V, V, V, SZ, V], ctypes.c_int),
+        "verify_greedy": ([V, V, I32, V, V], ctypes.c_int),
         "svq_stream_read": ([V, SZ, V, I32, V], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -186,6 +190,20 @@ def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace
            load().lmhead_argmax(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, _dev_ptr(row_ids),
                                 _dev_ptr(argmax), _dev_ptr(maxlogit), _dev_ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def lmhead_verify_greedy(packed, X, M: int, N: int, K: int, draft_ids, argmax, maxlogit, accept_len,
+                         workspace, row_ids=None, G: int = GROUP, stream=None) -> None:
+    _check("lmhead_verify_greedy",
+           load().lmhead_verify_greedy(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, _dev_ptr(row_ids),
+                                       _dev_ptr(draft_ids), _dev_ptr(argmax), _dev_ptr(maxlogit),
+                                       _dev_ptr(accept_len), _dev_ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def verify_greedy(target_ids, draft_ids, M: int, accept_len, stream=None) -> None:
+    _check("verify_greedy", load().verify_greedy(_dev_ptr(target_ids), _dev_ptr(draft_ids), M,
+                                                 _dev_ptr(accept_len), _stream(stream)))
 
 
 def svq_stream_read(src, nbytes: int, sink, wgs_per_cu: int = 0, stream=None) -> None:

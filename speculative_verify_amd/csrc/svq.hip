@@ -468,9 +468,30 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
   return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)n);
 }
 
+// Where a head launch leaves its results (all device pointers; see svq.h).
+// draft and accept are set only by lmhead_verify_greedy.
+struct HeadOut {
+  const int32_t* row_ids;  // NULL or [N] row -> token id
+  int32_t* idx;            // [M] greedy token per query row
+  float* max;              // [M] its logit
+  const int32_t* draft;    // NULL or [M - 1] drafted tokens d_1 .. d_{M-1}
+  int32_t* accept;         // [1] tau, when draft is set
+};
+
+// Greedy acceptance of a verified block (DFlash summary sec. 4.1): query row
+// m of the block [anchor, d_1, ..., d_{M-1}] predicts the token after
+// position m, so d_{j+1} is accepted while every earlier draft was accepted
+// and t_j == d_{j+1}.  tau = accepted + 1: the accepted drafts plus the
+// target's own next token, i.e. t_0 .. t_{tau-1}.  A row without a valid
+// maximum (id -1) ends the accepted prefix.
+__device__ __forceinline__ int greedy_accept_len(const int32_t* t, const int32_t* __restrict__ draft, int M) {
+  int a = 0;
+  while (a < M - 1 && t[a] >= 0 && t[a] == draft[a]) ++a;
+  return a + 1;
+}
+
 __device__ __forceinline__ void argmax_complete(unsigned long long key, bool holds_row, int m, uint8_t* ws, int M,
-                                                int N, const int32_t* __restrict__ row_ids,
-                                                int32_t* __restrict__ out_idx, float* __restrict__ out_max) {
+                                                int N, const HeadOut& ho) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kWsKeys);
   unsigned* counter = reinterpret_cast<unsigned*>(ws + kWsCounter);
   if (holds_row) {
@@ -484,6 +505,7 @@ __device__ __forceinline__ void argmax_complete(unsigned long long key, bool hol
   if (threadIdx.x == 0) last = atomicAdd(counter, 1u) == gridDim.x - 1;
   __syncthreads();
   if (!last) return;
+  __shared__ int32_t ids[SVQ_MAX_M];
   if ((int)threadIdx.x < M) {
     const unsigned long long k = atomicExch(&keys[threadIdx.x], 0ull);
     const uint32_t o = (uint32_t)(k >> 32);
@@ -491,10 +513,16 @@ __device__ __forceinline__ void argmax_complete(unsigned long long key, bool hol
     // key 0 means no row compared above it: every logit of the row was NaN.
     const bool found = k != 0ull && n >= 0 && n < N;
     const uint32_t u = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
-    out_idx[threadIdx.x] = !found ? -1 : row_ids ? row_ids[n] : n;
-    out_max[threadIdx.x] = found ? __uint_as_float(u) : __builtin_nanf("");
+    const int32_t id = !found ? -1 : ho.row_ids ? ho.row_ids[n] : n;
+    ho.idx[threadIdx.x] = id;
+    ho.max[threadIdx.x] = found ? __uint_as_float(u) : __builtin_nanf("");
+    ids[threadIdx.x] = id;
   }
   if (threadIdx.x == 0) atomicExch(counter, 0u);
+  if (ho.accept) {
+    __syncthreads();  // the whole completing workgroup takes this branch
+    if (threadIdx.x == 0) ho.accept[0] = greedy_accept_len(ids, ho.draft, M);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -502,8 +530,7 @@ __device__ __forceinline__ void argmax_complete(unsigned long long key, bool hol
 template <int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemv_w4a16(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ xw, uint16_t* __restrict__ y,
-                 uint8_t* __restrict__ ws, const int32_t* __restrict__ row_ids, int32_t* __restrict__ out_idx,
-                 float* __restrict__ out_max, int N, int KT, int NT) {
+                 uint8_t* __restrict__ ws, HeadOut ho, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
@@ -590,8 +617,7 @@ __global__ void __launch_bounds__(64 * MAXW)
           best_v = part[w].v;
           best_i = part[w].idx;
         }
-    argmax_complete(argmax_key(best_v, best_i), threadIdx.x == 0 && best_i < N, 0, ws, 1, N, row_ids, out_idx,
-                    out_max);
+    argmax_complete(argmax_key(best_v, best_i), threadIdx.x == 0 && best_i < N, 0, ws, 1, N, ho);
   }
 }
 
@@ -684,8 +710,7 @@ struct RowBest4 {
 // completes the launch's argmax.
 template <int MAXW>
 __device__ __forceinline__ void gemm_argmax_epilogue(RowBest4& b, int wave, int lane, int nwaves, uint8_t* ws,
-                                                     int M, int N, const int32_t* __restrict__ row_ids,
-                                                     int32_t* __restrict__ out_idx, float* __restrict__ out_max) {
+                                                     int M, int N, const HeadOut& ho) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
     for (int off = 8; off > 0; off >>= 1) {  // over the 16 lanes of one q
@@ -709,8 +734,7 @@ __device__ __forceinline__ void gemm_argmax_epilogue(RowBest4& b, int wave, int 
         bvv = fin[w][threadIdx.x].v;
         bii = fin[w][threadIdx.x].idx;
       }
-  argmax_complete(argmax_key(bvv, bii), (int)threadIdx.x < M && bii < N, threadIdx.x, ws, M, N, row_ids, out_idx,
-                  out_max);
+  argmax_complete(argmax_key(bvv, bii), (int)threadIdx.x < M && bii < N, threadIdx.x, ws, M, N, ho);
 }
 
 // Emits a completed 16 x 16 output tile held as lane (q, r) -> rows 4q + ii,
@@ -739,8 +763,7 @@ __device__ __forceinline__ void gemm_emit(const float4& tot, int q, int r, int r
 template <int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemm_w4a16(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
-                 uint8_t* __restrict__ ws, const int32_t* __restrict__ row_ids, int32_t* __restrict__ out_idx,
-                 float* __restrict__ out_max, int M, int N, int KT, int NT) {
+                 uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
@@ -812,7 +835,7 @@ __global__ void __launch_bounds__(64 * MAXW)
     i0 += D;
   } while (i0 < T);
   if constexpr (ARGMAX)
-    gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, row_ids, out_idx, out_max);
+    gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
 
 template <int GPW, int MAXW, int D, int P>
@@ -1093,8 +1116,7 @@ int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
   dispatch(sh, [&](auto G, auto W, auto D) {
     hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                       packed, xw, y, (uint8_t*)nullptr, (const int32_t*)nullptr,
-                       (int32_t*)nullptr, (float*)nullptr, (int)N, sh.KT, sh.NT);
+                       packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N, sh.KT, sh.NT);
   });
   return launched("gemv_w4a16");
 }
@@ -1125,8 +1147,7 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch(sh, [&](auto G, auto W, auto D) {
     hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                       packed, Xw, Y, (uint8_t*)nullptr, (const int32_t*)nullptr,
-                       (int32_t*)nullptr, (float*)nullptr, M, (int)N, sh.KT, sh.NT);
+                       packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
   });
   return launched("gemm_smallm_w4a16");
 }
@@ -1148,17 +1169,21 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
   return launched("gemm_smallm_binplane");
 }
 
-int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
-                  const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace, size_t workspace_bytes,
-                  void* stream) {
-  if (int rc = check_linear("lmhead_argmax", packed, X, argmax, M, N, K, G, 0)) return rc;
-  if (!maxlogit) return svq::fail(SVQ_ERR_NULL, "lmhead_argmax: NULL maxlogit");
-  if (misaligned(argmax, 4) || misaligned(maxlogit, 4) || (row_ids && misaligned(row_ids, 4)))
-    return svq::fail(SVQ_ERR_ALIGN, "lmhead_argmax: argmax, maxlogit and row_ids must be 4-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by lmhead_argmax and lmhead_verify_greedy.
+int launch_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
+                int32_t G, const HeadOut& ho, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, 0)) return rc;
+  if (!ho.max) return svq::fail(SVQ_ERR_NULL, "%s: NULL maxlogit", fn);
+  if (misaligned(ho.idx, 4) || misaligned(ho.max, 4) || (ho.row_ids && misaligned(ho.row_ids, 4)))
+    return svq::fail(SVQ_ERR_ALIGN, "%s: argmax, maxlogit and row_ids must be 4-byte aligned", fn);
   if (!workspace || workspace_bytes < svq_lmhead_workspace_bytes(M))
-    return svq::fail(SVQ_ERR_WORKSPACE, "lmhead_argmax: workspace needs %zu bytes (got %zu)",
-                     svq_lmhead_workspace_bytes(M), workspace ? workspace_bytes : (size_t)0);
-  if (misaligned(workspace, 16)) return svq::fail(SVQ_ERR_ALIGN, "lmhead_argmax: workspace must be 16-byte aligned");
+    return svq::fail(SVQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, svq_lmhead_workspace_bytes(M),
+                     workspace ? workspace_bytes : (size_t)0);
+  if (misaligned(workspace, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
   Shape sh;
   if (int rc = plan(N, K, M == 1 ? 1 : 4, M == 1 ? kPrefHeadM1 : kPrefHeadM16, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1167,17 +1192,56 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N
   if (M == 1) {
     dispatch(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, row_ids, argmax, maxlogit, (int)N, sh.KT,
-                         sh.NT);
+                         packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
     });
   } else {
     dispatch(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, row_ids, argmax, maxlogit, M, (int)N, sh.KT,
-                         sh.NT);
+                         packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
     });
   }
-  return launched("lmhead_argmax");
+  return launched(fn);
+}
+
+__global__ void __launch_bounds__(64) k_verify_greedy(const int32_t* __restrict__ target,
+                                                      const int32_t* __restrict__ draft, int M,
+                                                      int32_t* __restrict__ accept) {
+  if (threadIdx.x == 0) accept[0] = greedy_accept_len(target, draft, M);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                  const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return launch_head("lmhead_argmax", packed, X, M, N, K, G, HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr},
+                     workspace, workspace_bytes, stream);
+}
+
+int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                         const int32_t* row_ids, const int32_t* draft_ids, int32_t* argmax, float* maxlogit,
+                         int32_t* accept_len, void* workspace, size_t workspace_bytes, void* stream) {
+  svq::clear_error();
+  if (!accept_len || (M > 1 && !draft_ids))
+    return svq::fail(SVQ_ERR_NULL, "lmhead_verify_greedy: NULL accept_len or draft_ids");
+  if (misaligned(accept_len, 4) || (draft_ids && misaligned(draft_ids, 4)))
+    return svq::fail(SVQ_ERR_ALIGN, "lmhead_verify_greedy: accept_len and draft_ids must be 4-byte aligned");
+  return launch_head("lmhead_verify_greedy", packed, X, M, N, K, G,
+                     HeadOut{row_ids, argmax, maxlogit, draft_ids, accept_len}, workspace, workspace_bytes, stream);
+}
+
+int verify_greedy(const int32_t* target_ids, const int32_t* draft_ids, int32_t M, int32_t* accept_len, void* stream) {
+  svq::clear_error();
+  if (!target_ids || !accept_len || (M > 1 && !draft_ids))
+    return svq::fail(SVQ_ERR_NULL, "verify_greedy: NULL pointer");
+  if (M < 1 || M > SVQ_MAX_M) return svq::fail(SVQ_ERR_SHAPE, "verify_greedy: M=%d must be in 1..16", M);
+  if (misaligned(target_ids, 4) || misaligned(accept_len, 4) || (draft_ids && misaligned(draft_ids, 4)))
+    return svq::fail(SVQ_ERR_ALIGN, "verify_greedy: pointers must be 4-byte aligned");
+  hipLaunchKernelGGL(k_verify_greedy, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), target_ids,
+                     draft_ids, M, accept_len);
+  return launched("verify_greedy");
 }
 
 int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t wgs_per_cu, void* stream) {

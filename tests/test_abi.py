@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["pack_int4_grouped", "pack_binary_planes", "gemv_w4a16", "gemv_binplane",
-                 "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "svq_last_error"]:
+                 "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_verify_greedy",
+                 "verify_greedy", "svq_last_error"]:
         assert want in names
 
 
@@ -60,6 +61,14 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, A, A, 8, None), -5),
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, None, A, 1 << 20, None), -1),
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, A + 2, A, A, A, 1 << 20, None), -3),
+    (lambda l: l.verify_greedy(None, A, 2, A, None), -1),
+    (lambda l: l.verify_greedy(A, None, 2, A, None), -1),
+    (lambda l: l.verify_greedy(A, A, 0, A, None), -2),
+    (lambda l: l.verify_greedy(A, A, 17, A, None), -2),
+    (lambda l: l.verify_greedy(A + 2, A, 2, A, None), -3),
+    (lambda l: l.lmhead_verify_greedy(A, A, 2, 16, 128, 128, None, A, A, A, None, A, 1 << 20, None), -1),
+    (lambda l: l.lmhead_verify_greedy(A, A, 2, 16, 128, 128, None, None, A, A, A, A, 1 << 20, None), -1),
+    (lambda l: l.lmhead_verify_greedy(A, A, 2, 16, 128, 128, None, A, A, A, A, None, 0, None), -5),
     (lambda l: l.svq_stream_read(A, 100, A, 0, None), -2),
     (lambda l: l.svq_stream_read(A, 1024, A, 9, None), -2),
 ])

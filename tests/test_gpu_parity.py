@@ -389,3 +389,52 @@ def test_lmhead_workspace_counter_is_reusable():
         torch.cuda.synchronize()
         assert np.array_equal(idx.cpu().numpy(), rows.astype(np.int32)), it
         assert int(ws.count_nonzero().item()) == 0, it
+
+
+# ---------------------------------------------------------------------------
+# Greedy acceptance of a verified block
+
+def test_verify_greedy_matches_oracle():
+    rng = np.random.default_rng(60)
+    cases = []
+    for M in range(1, 17):
+        for a in range(M):  # accepted drafts
+            t = rng.integers(0, 1000, M).astype(np.int32)
+            d = t[:-1].copy()
+            if a < M - 1:
+                d[a] = t[a] + 1
+            cases.append((t, d))
+    t = np.array([4, -1, 7], np.int32)
+    cases.append((t, np.array([4, 0], np.int32)))
+    tau = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for t, d in cases:
+        M = t.shape[0]
+        svq.verify_greedy(dev(t), dev(d) if M > 1 else None, M, tau)
+        torch.cuda.synchronize()
+        assert int(tau.item()) == oracle.verify_greedy(t, d), (t, d)
+
+
+@pytest.mark.parametrize("M,N", [(16, 4096), (5, 32768), (1, 2000)])
+def test_lmhead_verify_greedy_planted(M, N):
+    case = synth.Case("t", "lmhead", M, N, 1024)
+    codes, scales, X, rows = synth.make_lmhead(case, 70 + M)
+    rid = (5 + 3 * np.arange(N)).astype(np.int32)
+    t_ids = rid[rows].astype(np.int32)
+    blob = dev(svq.pack_int4_grouped(codes, scales))
+    ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    idx = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    mx = torch.zeros(M, dtype=torch.float32, device="cuda")
+    tau = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Xd, rd = dev(X), dev(rid)
+    for bad in list(range(M - 1)) + [None]:
+        d = t_ids[:-1].copy()
+        if bad is not None:
+            d[bad] += 1
+        svq.lmhead_verify_greedy(blob, Xd, M, N, 1024, dev(d) if M > 1 else None, idx, mx, tau, ws,
+                                 row_ids=rd)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), t_ids)
+        want = oracle.verify_greedy(t_ids, d)
+        assert want == (M if bad is None else bad + 1)
+        assert int(tau.item()) == want, bad
+        assert int(ws.count_nonzero().item()) == 0

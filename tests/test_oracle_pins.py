@@ -202,6 +202,43 @@ def test_argmax_agrees_with_first_occurrence_argmax_of_logits():
     assert np.array_equal(r["zmax"], y.max(axis=1))
 
 
+# ---- greedy acceptance ---------------------------------------------------------
+# Hand-worked cases of the acceptance rule (DFlash summary sec. 4.1): the block
+# is [anchor, d_1 .. d_{M-1}], target[j] predicts the token after row j, drafts
+# are accepted in order while target[j] == d_{j+1}, and tau = accepted + 1.
+VERIFY_CASES = [
+    # (target, draft, tau, why)
+    ([5], [], 1, "no drafts: only the target's own token"),
+    ([7, 8, 9, 4], [7, 8, 9], 4, "every draft accepted, plus the bonus token t_3"),
+    ([7, 8, 9, 4], [1, 8, 9], 1, "first draft rejected"),
+    ([7, 8, 9, 4], [7, 2, 9], 2, "second draft rejected"),
+    ([7, 8, 9, 4], [7, 8, 3], 3, "last draft rejected"),
+    ([1, 2, 3], [9, 2], 1, "a later match after a rejection does not count"),
+    ([-1, 5, 6], [0, 5], 1, "a row without a valid maximum ends the prefix"),
+    ([3, -1, 6], [3, 0], 2, "... also after accepted drafts"),
+    (list(range(16)), list(range(15)), 16, "full 16-row block accepted"),
+]
+
+
+@pytest.mark.parametrize("target,draft,tau,why", VERIFY_CASES)
+def test_verify_greedy_hand_cases(target, draft, tau, why):
+    assert oracle.verify_greedy(np.array(target), np.array(draft)) == tau, why
+
+
+def test_verify_greedy_on_planted_head_blocks():
+    # End to end: the planted rows fix the target tokens, so drafts copied from
+    # them are accepted up to the first planted mismatch.
+    case = synth.Case("t", "lmhead", 6, 200, 256)
+    codes, scales, x, rows = synth.make_lmhead(case, seed=14)
+    t = oracle.argmax_w4a16(codes, scales, x)["out"]
+    assert np.array_equal(t, rows.astype(np.int32))
+    for bad in range(case.M - 1):
+        draft = t[:-1].copy()
+        draft[bad] = (draft[bad] + 1) % case.N
+        assert oracle.verify_greedy(t, draft) == bad + 1
+    assert oracle.verify_greedy(t, t[:-1]) == case.M
+
+
 # ---- packed layouts -----------------------------------------------------------
 
 def test_int4_pack_matches_hand_worked_bytes():
