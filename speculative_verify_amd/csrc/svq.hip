@@ -98,6 +98,14 @@ __device__ __forceinline__ uint32_t opaque_vgpr() {
   return v;
 }
 
+// A copy of v the compiler cannot see through (its known bits are lost).  Only
+// VALU instructions read the result.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t v) {
+  uint32_t d;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(d) : "v"(v));
+  return d;
+}
+
 // Pair decoders: one shift plus one v_and_or_b32 per bf16 pair.  The VOP3
 // encoding of v_and_or_b32 takes no literal and at most one SGPR, so the
 // mask lives in an SGPR and the OR value in a VGPR; with literals the
@@ -621,6 +629,80 @@ __global__ void __launch_bounds__(64 * MAXW)
   }
 }
 
+// Sign-nibble lookup tables for the M = 1 sign-plane kernel.  In a sign
+// dword, the bits of k-block t form two nibbles: bits 4t..4t+3 hold the signs
+// of the lane's even k's (32t + 8q + 2i) and bits 16+4t..16+4t+3 those of its
+// odd k's (+1).  For every (group, t, parity) the table holds, for each of
+// the 16 nibble values v, the sum over i of (bit i of v set ? -x : +x) over
+// those four activations, so a plane's sum over 128 k is eight table reads
+// instead of 64 sign decodes and 64 multiply-adds.  Lane (q, r) builds entry
+// v = r of the tables of its own q (the 16 lanes of a row share their
+// activations), and every wave builds and reads only its own tables, so no
+// barrier is needed.  In a read, the 16 lanes of a row q address the 16
+// consecutive entries of one table and the four rows use disjoint 16-bank
+// ranges, so a read is free of bank conflicts.
+template <int GPW>
+struct SignLut {
+  float e[GPW][4][2][64];  // [group][t][parity][16 q + v]
+};
+
+template <int GPW>
+__device__ __forceinline__ void build_sign_lut(SignLut<GPW>& lut, const uint32_t (&xp)[GPW][16], int q, int r) {
+  const uint32_t f0 = (uint32_t)(r & 1) << 31, f1 = (uint32_t)((r >> 1) & 1) << 31;
+  const uint32_t f2 = (uint32_t)((r >> 2) & 1) << 31, f3 = (uint32_t)((r >> 3) & 1) << 31;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t* pr = &xp[gi][4 * t];
+      // even k's: the pairs' low halves; odd k's: the high halves.
+      const float e0 = __uint_as_float((pr[0] << 16) ^ f0) + __uint_as_float((pr[1] << 16) ^ f1) +
+                       __uint_as_float((pr[2] << 16) ^ f2) + __uint_as_float((pr[3] << 16) ^ f3);
+      const float e1 = __uint_as_float((pr[0] & 0xFFFF0000u) ^ f0) + __uint_as_float((pr[1] & 0xFFFF0000u) ^ f1) +
+                       __uint_as_float((pr[2] & 0xFFFF0000u) ^ f2) + __uint_as_float((pr[3] & 0xFFFF0000u) ^ f3);
+      lut.e[gi][t][0][16 * q + r] = e0;
+      lut.e[gi][t][1][16 * q + r] = e1;
+    }
+}
+
+// ((w >> shift) & 15) * 4: a nibble as the byte offset of a table entry.
+__device__ __forceinline__ uint32_t nibble_offset(uint32_t w, int shift) {
+  return shift >= 2 ? (w >> (shift - 2)) & 0x3Cu : (w << (2 - shift)) & 0x3Cu;
+}
+
+// Lane's partial for row r over its k sub-ranges of the wave's groups, all
+// planes: sum_p alpha_p * (eight table reads per group).  lane_off is the
+// byte offset of the lane's table row (wave's tables + 64 q); the nibble's
+// offset has disjoint bits, so one AND-OR forms each address and the
+// (group, t, parity) part is the read's constant offset.
+template <int GPW, int P>
+__device__ __forceinline__ float binplane_tile_partial_lut(const SignSlot<GPW, P>& sl, const SignLut<GPW>* luts,
+                                                           uint32_t lane_off) {
+  const char* base = reinterpret_cast<const char*>(luts);
+  float part = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t w = sl.w[gi][p];
+      float acc;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          const uint32_t off = (nibble_offset(w, 16 * par + 4 * t) | lane_off) + ((gi * 4 + t) * 2 + par) * 256;
+          const float v = *reinterpret_cast<const float*>(base + off);
+          acc = (t == 0 && par == 0) ? v : acc + v;
+        }
+      part = fmaf(sl.a[p].f16(gi), acc, part);
+    }
+  return part;
+}
+
+// Chunk length of the table kernel: the tables (8 KiB per wave at four groups)
+// plus the chunk staging must leave room for two workgroups per CU.
+constexpr int kChunkGemvLut = 14;
+
 // gemv_binplane (M = 1).
 template <int GPW, int MAXW, int D, int P>
 __global__ void __launch_bounds__(64 * MAXW)
@@ -645,23 +727,37 @@ __global__ void __launch_bounds__(64 * MAXW)
   }
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
-  __shared__ ChunkStage<float, kChunkGemv, MAXW, 16> stage;
+  // Up to eight waves the nibble tables fit beside the staging area; wider
+  // workgroups (K > 4096) decode every sign pair instead.
+  constexpr bool kLut = MAXW <= 8;
+  constexpr int C = kLut ? kChunkGemvLut : kChunkGemv;
+  __shared__ ChunkStage<float, C, MAXW, 16> stage;
+  __shared__ SignLut<kLut ? GPW : 1> luts[kLut ? MAXW : 1];
   uint32_t xp[GPW][16];
   expand_x<GPW>(xo, g0, KT, xp);
   const PairDecode one = sign_decode();
+  if constexpr (kLut) build_sign_lut<GPW>(luts[wave], xp, q, r);
+  // Opaque copy: the compiler would otherwise turn the OR of disjoint bits in
+  // every address into an ADD and lose the one-instruction AND-OR form.
+  const uint32_t lut_off =
+      opaque_copy((uint32_t)wave * (uint32_t)sizeof(SignLut<kLut ? GPW : 1>) | (uint32_t)(64 * q));
 
   int i0 = 0;
   do {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const float part = sum_over_q(binplane_tile_partial<GPW, P>(ring[j], xp, one));
+      float part;
+      if constexpr (kLut)
+        part = sum_over_q(binplane_tile_partial_lut<GPW, P>(ring[j], luts, lut_off));
+      else
+        part = sum_over_q(binplane_tile_partial<GPW, P>(ring[j], xp, one));
       stage.put(i, i < T, wave, lane, part);
       // Slot j is refilled only after its last use, so it keeps its registers.
       __builtin_amdgcn_sched_barrier(0);
       load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
-      const int ci = i % kChunkGemv;
-      if (i < T && (ci == kChunkGemv - 1 || i == T - 1)) {
+      const int ci = i % C;
+      if (i < T && (ci == C - 1 || i == T - 1)) {
         __syncthreads();
         const int first = i - ci;
         for (int o = threadIdx.x; o < (ci + 1) * 16; o += nwaves * 64) {
