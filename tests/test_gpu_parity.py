@@ -230,6 +230,23 @@ def test_gemm_m_sweep_and_rows_match_gemv(M):
         check_close(Yg[m], y1[0], a1[0], f"row {m}")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 200, 8192), (7, 96, 6144), (16, 33, 4224)])
+def test_gemm_wide_k(M, N, K):
+    # K above 4096 takes the 12- and 16-wave workgroups.
+    rng = np.random.default_rng(M + N + K)
+    codes, scales = synth.int4_weights(rng, N, K)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=3)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    check_close(run_gemm_w4a16(codes, scales, X), Y, A, f"gemm w4a16 M={M} N={N} K={K}")
+    Yb, Ab = oracle.linear_binplane(signs, alpha, X)
+    check_close(run_gemm_binplane(signs, alpha, X), Yb, Ab, f"gemm binplane M={M} N={N} K={K}")
+    case = synth.Case("t", "lmhead", M, N, K)
+    hc, hs, hX, rows = synth.make_lmhead(case, M + K)
+    idx, mx = run_lmhead(hc, hs, hX)
+    assert np.array_equal(idx, rows.astype(np.int32))
+
+
 def test_gemm_onehot_unit_scale_is_exact():
     # Row m of X is e_{k_m}; Y[m][n] = c[n][k_m] exactly (checks both MFMA operand layouts).
     N, K, M = 48, 256, 16
