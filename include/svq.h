@@ -197,6 +197,21 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * lmhead_argmax_binplane -- DEVICE pointers, asynchronous on `stream`.
+ * lmhead_argmax for a head stored as P sign planes (ShiftAddQwen README,
+ * Method/Format; the MTP study sec. 3.3 for the trimmed head):
+ *   z[m][n] = sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] * X[m][k]
+ * with the same outputs, workspace contract and tie rule as lmhead_argmax.
+ *   packed  binary-plane blob (layout above), 1 <= P <= 6
+ * Errors: as gemm_smallm_binplane, plus WORKSPACE.
+ */
+int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M,
+                           int64_t N, int64_t K, int32_t G, int32_t P,
+                           const int32_t* row_ids, int32_t* argmax,
+                           float* maxlogit, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Greedy acceptance of a verified block (DFlash summary sec. 4.1: a cycle
  * drafts gamma tokens, the target checks them in one parallel pass and
  * accepts tau in [1, gamma + 1] tokens; the report's sec. 2.2 for parallel

@@ -70,6 +70,8 @@ def _load():
     lib.oracle_linear_binplane.restype = ctypes.c_int
     lib.oracle_argmax_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.oracle_argmax_w4a16.restype = ctypes.c_int
+    lib.oracle_argmax_binplane.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]
+    lib.oracle_argmax_binplane.restype = ctypes.c_int
     lib.oracle_verify_greedy.argtypes = [P, P, I64]
     lib.oracle_verify_greedy.restype = ctypes.c_int
     lib.oracle_int4_blob_bytes.argtypes = [I64, I64]
@@ -171,6 +173,28 @@ def argmax_w4a16(codes, scales, x, G: int = 128, row_ids=None):
         _ptr(amax), _ptr(zsec))
     if rc:
         raise ValueError(f"oracle_argmax_w4a16 rc={rc}")
+    return dict(out=out, idx=idx, zmax=zmax, amax=amax, zsecond=zsec)
+
+
+def argmax_binplane(signs, alpha, x, G: int = 128, row_ids=None):
+    """dict(out, idx, zmax, amax, zsecond) for a sign-plane head."""
+    signs = _c(signs, np.int8)
+    alpha = _c(alpha, np.uint16)
+    x2 = _c(np.atleast_2d(x), np.uint16)
+    P, N, K = signs.shape
+    M = x2.shape[0]
+    rid = None if row_ids is None else _c(row_ids, np.int32)
+    out = np.empty(M, np.int32)
+    idx = np.empty(M, np.int32)
+    zmax = np.empty(M, np.float64)
+    amax = np.empty(M, np.float64)
+    zsec = np.empty(M, np.float64)
+    rc = _load().oracle_argmax_binplane(
+        _ptr(signs), _ptr(alpha), _ptr(x2), M, N, K, G, P,
+        None if rid is None else _ptr(rid), _ptr(out), _ptr(idx), _ptr(zmax),
+        _ptr(amax), _ptr(zsec))
+    if rc:
+        raise ValueError(f"oracle_argmax_binplane rc={rc}")
     return dict(out=out, idx=idx, zmax=zmax, amax=amax, zsecond=zsec)
 
 

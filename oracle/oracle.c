@@ -200,6 +200,25 @@ int oracle_linear_binplane(const int8_t* signs, const uint16_t* alpha,
  *   zsecond[m]= max over n != idx[m] of z[m][n]  (-inf when N == 1)
  * The logits are materialised here on purpose: this is the slow statement.
  */
+/* First-occurrence argmax of each row of logits z [M][N] (see above). */
+static void argmax_rows(const double* z, const double* a, int64_t M, int64_t N,
+                        const int32_t* row_ids, int32_t* out, int32_t* idx,
+                        double* zmax, double* amax, double* zsecond) {
+  for (int64_t m = 0; m < M; ++m) {
+    int64_t best = 0;
+    for (int64_t n = 1; n < N; ++n)
+      if (z[m * N + n] > z[m * N + best]) best = n;
+    double second = -INFINITY;
+    for (int64_t n = 0; n < N; ++n)
+      if (n != best && z[m * N + n] > second) second = z[m * N + n];
+    idx[m] = (int32_t)best;
+    out[m] = row_ids ? row_ids[best] : (int32_t)best;
+    zmax[m] = z[m * N + best];
+    amax[m] = a[m * N + best];
+    zsecond[m] = second;
+  }
+}
+
 int oracle_argmax_w4a16(const int8_t* codes, const uint16_t* scales,
                         const uint16_t* x, int64_t M, int64_t N, int64_t K,
                         int64_t G, const int32_t* row_ids, int32_t* out,
@@ -213,21 +232,30 @@ int oracle_argmax_w4a16(const int8_t* codes, const uint16_t* scales,
     return -1;
   }
   int rc = oracle_linear_w4a16(codes, scales, x, M, N, K, G, z, a);
-  if (rc == 0) {
-    for (int64_t m = 0; m < M; ++m) {
-      int64_t best = 0;
-      for (int64_t n = 1; n < N; ++n)
-        if (z[m * N + n] > z[m * N + best]) best = n;
-      double second = -INFINITY;
-      for (int64_t n = 0; n < N; ++n)
-        if (n != best && z[m * N + n] > second) second = z[m * N + n];
-      idx[m] = (int32_t)best;
-      out[m] = row_ids ? row_ids[best] : (int32_t)best;
-      zmax[m] = z[m * N + best];
-      amax[m] = a[m * N + best];
-      zsecond[m] = second;
-    }
+  if (rc == 0) argmax_rows(z, a, M, N, row_ids, out, idx, zmax, amax, zsecond);
+  free(z);
+  free(a);
+  return rc;
+}
+
+/*
+ * The same greedy decision for a head stored as P sign planes (ShiftAddQwen
+ * README, Method/Format): z[m][n] is oracle_linear_binplane's logit.
+ */
+int oracle_argmax_binplane(const int8_t* signs, const uint16_t* alpha,
+                           const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                           int64_t G, int64_t P, const int32_t* row_ids,
+                           int32_t* out, int32_t* idx, double* zmax,
+                           double* amax, double* zsecond) {
+  double* z = (double*)malloc((size_t)(M * N) * sizeof(double));
+  double* a = (double*)malloc((size_t)(M * N) * sizeof(double));
+  if (!z || !a) {
+    free(z);
+    free(a);
+    return -1;
   }
+  int rc = oracle_linear_binplane(signs, alpha, x, M, N, K, G, P, z, a);
+  if (rc == 0) argmax_rows(z, a, M, N, row_ids, out, idx, zmax, amax, zsecond);
   free(z);
   free(a);
   return rc;

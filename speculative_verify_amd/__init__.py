@@ -10,7 +10,7 @@ Functions (same names as the C ABI):
   pack_int4_grouped, unpack_int4_grouped, pack_binary_planes,
   unpack_binary_planes                       host numpy arrays
   gemv_w4a16, gemv_binplane, gemm_smallm_w4a16, gemm_smallm_binplane,
-  lmhead_argmax, lmhead_verify_greedy, verify_greedy,
+  lmhead_argmax, lmhead_argmax_binplane, lmhead_verify_greedy, verify_greedy,
   svq_stream_read                            torch CUDA tensors
 """
 from __future__ import annotations
@@ -24,7 +24,8 @@ __all__ = [
     "SvqError", "lib_path", "load", "int4_packed_bytes", "binplane_packed_bytes",
     "lmhead_workspace_bytes", "pack_int4_grouped", "unpack_int4_grouped",
     "pack_binary_planes", "unpack_binary_planes", "gemv_w4a16", "gemv_binplane",
-    "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_verify_greedy",
+    "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_argmax_binplane",
+    "lmhead_verify_greedy",
     "verify_greedy", "svq_stream_read",
 ]
 
@@ -71,6 +72,7 @@ def load():
         "gemm_smallm_binplane": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
         "lmhead_argmax": ([V, V, I32, I64, I64, I32, V, V, V, V, SZ, V], ctypes.c_int),
         "lmhead_verify_greedy": ([V, V, I32, I64, I64, I32, V, V, V, V, V, V, SZ, V], ctypes.c_int),
+        "lmhead_argmax_binplane": ([V, V, I32, I64, I64, I32, I32, V, V, V, V, SZ, V], ctypes.c_int),
         "verify_greedy": ([V, V, I32, V, V], ctypes.c_int),
         "svq_stream_read": ([V, SZ, V, I32, V], ctypes.c_int),
     }
@@ -190,6 +192,14 @@ def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace
            load().lmhead_argmax(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, _dev_ptr(row_ids),
                                 _dev_ptr(argmax), _dev_ptr(maxlogit), _dev_ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def lmhead_argmax_binplane(packed, X, M: int, N: int, K: int, P: int, argmax, maxlogit, workspace,
+                           row_ids=None, G: int = GROUP, stream=None) -> None:
+    _check("lmhead_argmax_binplane",
+           load().lmhead_argmax_binplane(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, P, _dev_ptr(row_ids),
+                                         _dev_ptr(argmax), _dev_ptr(maxlogit), _dev_ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def lmhead_verify_greedy(packed, X, M: int, N: int, K: int, draft_ids, argmax, maxlogit, accept_len,

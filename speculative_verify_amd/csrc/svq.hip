@@ -533,6 +533,31 @@ __device__ __forceinline__ void argmax_complete(unsigned long long key, bool hol
   }
 }
 
+// M = 1 heads: combines the threads' running bests (lowest index wins ties)
+// and completes the launch's argmax.
+template <int MAXW>
+__device__ __forceinline__ void gemv_argmax_epilogue(float best_v, int best_i, int wave, int lane, int nwaves,
+                                                     uint8_t* ws, int N, const HeadOut& ho) {
+  __shared__ ArgBest part[MAXW];
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(best_v, off);
+    const int oi = __shfl_xor(best_i, off);
+    if (better(ov, oi, best_v, best_i)) {
+      best_v = ov;
+      best_i = oi;
+    }
+  }
+  if (lane == 0) part[wave] = ArgBest{best_v, best_i};
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < nwaves; ++w)
+      if (better(part[w].v, part[w].idx, best_v, best_i)) {
+        best_v = part[w].v;
+        best_i = part[w].idx;
+      }
+  argmax_complete(argmax_key(best_v, best_i), threadIdx.x == 0 && best_i < N, 0, ws, 1, N, ho);
+}
+
 // ---------------------------------------------------------------------------
 // gemv_w4a16 / lmhead (M = 1).  ARGMAX selects the epilogue.
 template <int GPW, int MAXW, int D, bool ARGMAX>
@@ -606,27 +631,7 @@ __global__ void __launch_bounds__(64 * MAXW)
     }
     i0 += D;
   } while (i0 < T);
-  if constexpr (ARGMAX) {
-    // Lowest index wins ties.
-    __shared__ ArgBest part[MAXW];
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(best_v, off);
-      const int oi = __shfl_xor(best_i, off);
-      if (better(ov, oi, best_v, best_i)) {
-        best_v = ov;
-        best_i = oi;
-      }
-    }
-    if (lane == 0) part[wave] = ArgBest{best_v, best_i};
-    __syncthreads();
-    if (threadIdx.x == 0)
-      for (int w = 1; w < nwaves; ++w)
-        if (better(part[w].v, part[w].idx, best_v, best_i)) {
-          best_v = part[w].v;
-          best_i = part[w].idx;
-        }
-    argmax_complete(argmax_key(best_v, best_i), threadIdx.x == 0 && best_i < N, 0, ws, 1, N, ho);
-  }
+  if constexpr (ARGMAX) gemv_argmax_epilogue<MAXW>(best_v, best_i, wave, lane, nwaves, ws, N, ho);
 }
 
 // Sign-nibble lookup tables for the M = 1 sign-plane kernel.  In a sign
@@ -703,11 +708,11 @@ __device__ __forceinline__ float binplane_tile_partial_lut(const SignSlot<GPW, P
 // plus the chunk staging must leave room for two workgroups per CU.
 constexpr int kChunkGemvLut = 14;
 
-// gemv_binplane (M = 1).
-template <int GPW, int MAXW, int D, int P>
+// gemv_binplane / sign-plane head (M = 1).  ARGMAX selects the epilogue.
+template <int GPW, int MAXW, int D, int P, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemv_binplane(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ xw, uint16_t* __restrict__ y,
-                    int N, int KT, int NT) {
+                    uint8_t* __restrict__ ws, HeadOut ho, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
@@ -741,6 +746,8 @@ __global__ void __launch_bounds__(64 * MAXW)
   // every address into an ADD and lose the one-instruction AND-OR form.
   const uint32_t lut_off =
       opaque_copy((uint32_t)wave * (uint32_t)sizeof(SignLut<kLut ? GPW : 1>) | (uint32_t)(64 * q));
+  float best_v = -FLT_MAX;
+  int best_i = INT_MAX;
 
   int i0 = 0;
   do {
@@ -762,12 +769,23 @@ __global__ void __launch_bounds__(64 * MAXW)
         const int first = i - ci;
         for (int o = threadIdx.x; o < (ci + 1) * 16; o += nwaves * 64) {
           const int n = 16 * row_tile(first + (o >> 4)) + (o & 15);
-          if (n < N) y[n] = f32_to_bf16_rne(stage.sum(i, o >> 4, nwaves, o & 15));
+          if (n < N) {
+            const float v = stage.sum(i, o >> 4, nwaves, o & 15);
+            if constexpr (ARGMAX) {
+              if (v > best_v) {  // a thread's rows arrive in increasing n
+                best_v = v;
+                best_i = n;
+              }
+            } else {
+              y[n] = f32_to_bf16_rne(v);
+            }
+          }
         }
       }
     }
     i0 += D;
   } while (i0 < T);
+  if constexpr (ARGMAX) gemv_argmax_epilogue<MAXW>(best_v, best_i, wave, lane, nwaves, ws, N, ho);
 }
 
 // ---------------------------------------------------------------------------
@@ -934,10 +952,10 @@ __global__ void __launch_bounds__(64 * MAXW)
     gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
 
-template <int GPW, int MAXW, int D, int P>
+template <int GPW, int MAXW, int D, int P, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemm_binplane(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
-                    int M, int N, int KT, int NT) {
+                    uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
@@ -962,7 +980,12 @@ __global__ void __launch_bounds__(64 * MAXW)
   mask_x_pairs<GPW>(r, M, g0, KT, xa);
   const PairDecode one = sign_decode();
 
-  RowBest4 unused;
+  RowBest4 best;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    best.v[ii] = -FLT_MAX;
+    best.idx[ii] = INT_MAX;
+  }
   int i0 = 0;
   do {
 #pragma unroll
@@ -997,11 +1020,13 @@ __global__ void __launch_bounds__(64 * MAXW)
         const int first = i - ci;
         // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
         // same outputs of every tile, so its columns arrive in increasing n.
-        if (wave <= ci) gemm_emit<false>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, unused);
+        if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, best);
       }
     }
     i0 += D;
   } while (i0 < T);
+  if constexpr (ARGMAX)
+    gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
 
 // Streaming-read ceiling: every thread keeps U non-temporal 16-byte loads in
@@ -1227,8 +1252,9 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
   dispatch_p(P, [&](auto Pc) {
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc)>), dim3(sh.grid),
-                         dim3(64 * sh.waves), 0, st, packed, xw, y, (int)N, sh.KT, sh.NT);
+      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
+                         dim3(64 * sh.waves), 0, st, packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N,
+                         sh.KT, sh.NT);
     });
   });
   return launched("gemv_binplane");
@@ -1258,8 +1284,9 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch_p(P, [&](auto Pc) {
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc)>), dim3(sh.grid),
-                         dim3(64 * sh.waves), 0, st, packed, Xw, Y, M, (int)N, sh.KT, sh.NT);
+      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
+                         dim3(64 * sh.waves), 0, st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N,
+                         sh.KT, sh.NT);
     });
   });
   return launched("gemm_smallm_binplane");
@@ -1270,9 +1297,10 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
 namespace {
 
 // Validation and launch shared by lmhead_argmax and lmhead_verify_greedy.
+// P = 0: INT4 weights; P >= 1: P sign planes.
 int launch_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
-                int32_t G, const HeadOut& ho, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, 0)) return rc;
+                int32_t G, int32_t P, const HeadOut& ho, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, P)) return rc;
   if (!ho.max) return svq::fail(SVQ_ERR_NULL, "%s: NULL maxlogit", fn);
   if (misaligned(ho.idx, 4) || misaligned(ho.max, 4) || (ho.row_ids && misaligned(ho.row_ids, 4)))
     return svq::fail(SVQ_ERR_ALIGN, "%s: argmax, maxlogit and row_ids must be 4-byte aligned", fn);
@@ -1281,11 +1309,23 @@ int launch_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_
                      workspace ? workspace_bytes : (size_t)0);
   if (misaligned(workspace, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
   Shape sh;
-  if (int rc = plan(N, K, M == 1 ? 1 : 4, M == 1 ? kPrefHeadM1 : kPrefHeadM16, &sh)) return rc;
+  const LaunchPref pref = P ? (M == 1 ? kPrefHeadM1 : kPrefGemmPlanes) : (M == 1 ? kPrefHeadM1 : kPrefHeadM16);
+  if (int rc = plan(N, K, M == 1 ? 1 : 4, pref, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  if (M == 1) {
+  if (P) {
+    dispatch_p(P, [&](auto Pc) {
+      dispatch(sh, [&](auto G, auto W, auto D) {
+        if (M == 1)
+          hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves),
+                             0, st, packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
+        else
+          hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves),
+                             0, st, packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
+      });
+    });
+  } else if (M == 1) {
     dispatch(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
                          packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
@@ -1312,8 +1352,17 @@ extern "C" {
 int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
                   const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  return launch_head("lmhead_argmax", packed, X, M, N, K, G, HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr},
+  return launch_head("lmhead_argmax", packed, X, M, N, K, G, 0, HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr},
                      workspace, workspace_bytes, stream);
+}
+
+int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                           int32_t P, const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  svq::clear_error();
+  if (P < 1 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "lmhead_argmax_binplane: P=%d must be in 1..6", P);
+  return launch_head("lmhead_argmax_binplane", packed, X, M, N, K, G, P,
+                     HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr}, workspace, workspace_bytes, stream);
 }
 
 int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
@@ -1324,7 +1373,7 @@ int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M, in
     return svq::fail(SVQ_ERR_NULL, "lmhead_verify_greedy: NULL accept_len or draft_ids");
   if (misaligned(accept_len, 4) || (draft_ids && misaligned(draft_ids, 4)))
     return svq::fail(SVQ_ERR_ALIGN, "lmhead_verify_greedy: accept_len and draft_ids must be 4-byte aligned");
-  return launch_head("lmhead_verify_greedy", packed, X, M, N, K, G,
+  return launch_head("lmhead_verify_greedy", packed, X, M, N, K, G, 0,
                      HeadOut{row_ids, argmax, maxlogit, draft_ids, accept_len}, workspace, workspace_bytes, stream);
 }
 

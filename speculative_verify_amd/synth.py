@@ -91,6 +91,23 @@ def plant_rows(rng, codes: np.ndarray, scales: np.ndarray, x: np.ndarray,
     return rows
 
 
+def plant_rows_binplane(rng, signs: np.ndarray, alpha: np.ndarray, x: np.ndarray,
+                        factor: float = 3.0) -> np.ndarray:
+    """Sign-plane counterpart of plant_rows: for query m a distinct row r_m gets
+    b = +1 on every plane where x[m][k] has a clear sign bit and -1 where it is
+    set, and its plane scales become ``factor`` times the drawn ones (fp16).
+    Edits ``signs``/``alpha`` in place and returns the planted rows [M]."""
+    M = x.shape[0]
+    N = signs.shape[1]
+    rows = rng.choice(N, size=M, replace=False).astype(np.int64)
+    for m in range(M):
+        neg = (x[m] & 0x8000) != 0
+        signs[:, rows[m]] = np.where(neg, -1, 1).astype(np.int8)[None, :]
+        a = alpha[:, rows[m]].astype(np.uint16).view(np.float16).astype(np.float32)
+        alpha[:, rows[m]] = f32_to_f16_bits(factor * a)
+    return rows
+
+
 @dataclass(frozen=True)
 class Case:
     """One synthetic workload shape."""
@@ -141,6 +158,14 @@ def make_lmhead(case: Case, seed: int = 0):
     x = activations(rng, case.M, case.K)
     rows = plant_rows(rng, codes, scales, x)
     return codes, scales, x, rows
+
+
+def make_lmhead_binplane(case: Case, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    signs, alpha = binplane_weights(rng, case.N, case.K, case.P, case.G)
+    x = activations(rng, case.M, case.K)
+    rows = plant_rows_binplane(rng, signs, alpha, x)
+    return signs, alpha, x, rows
 
 
 def device_int4_blob(N: int, K: int, seed: int, G: int = GROUP, smin: float = 0.005,

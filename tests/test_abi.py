@@ -69,6 +69,9 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.lmhead_verify_greedy(A, A, 2, 16, 128, 128, None, A, A, A, None, A, 1 << 20, None), -1),
     (lambda l: l.lmhead_verify_greedy(A, A, 2, 16, 128, 128, None, None, A, A, A, A, 1 << 20, None), -1),
     (lambda l: l.lmhead_verify_greedy(A, A, 2, 16, 128, 128, None, A, A, A, A, None, 0, None), -5),
+    (lambda l: l.lmhead_argmax_binplane(A, A, 2, 16, 128, 128, 0, None, A, A, A, 1 << 20, None), -2),
+    (lambda l: l.lmhead_argmax_binplane(A, A, 2, 16, 128, 128, 7, None, A, A, A, 1 << 20, None), -2),
+    (lambda l: l.lmhead_argmax_binplane(A, A, 2, 16, 128, 128, 3, None, A, A, None, 0, None), -5),
     (lambda l: l.svq_stream_read(A, 100, A, 0, None), -2),
     (lambda l: l.svq_stream_read(A, 1024, A, 9, None), -2),
 ])

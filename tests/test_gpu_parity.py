@@ -455,3 +455,26 @@ def test_lmhead_verify_greedy_planted(M, N):
         assert want == (M if bad is None else bad + 1)
         assert int(tau.item()) == want, bad
         assert int(ws.count_nonzero().item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# Sign-plane head
+
+@pytest.mark.parametrize("M,N,K,P", [(1, 5000, 4096, 3), (16, 32768, 4096, 3), (5, 777, 1024, 2),
+                                     (16, 300, 6144, 4), (1, 64, 256, 1)])
+def test_lmhead_binplane_planted(M, N, K, P):
+    case = synth.Case("t", "lmhead", M, N, K, P=P)
+    signs, alpha, X, rows = synth.make_lmhead_binplane(case, 80 + M + P)
+    rid = (11 + 2 * np.arange(N)).astype(np.int32)
+    r = oracle.argmax_binplane(signs, alpha, X, row_ids=rid)
+    assert np.array_equal(r["idx"], rows.astype(np.int32))
+    blob = dev(svq.pack_binary_planes(signs, alpha))
+    idx = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    mx = torch.zeros(M, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    print(f"lmhead_argmax_binplane M={M} N={N} K={K} P={P}", flush=True)
+    svq.lmhead_argmax_binplane(blob, dev(X), M, N, K, P, idx, mx, ws, row_ids=dev(rid))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), r["out"])
+    check_close(mx.double().cpu().numpy(), r["zmax"], r["amax"], "binplane head max")
+    assert int(ws.count_nonzero().item()) == 0

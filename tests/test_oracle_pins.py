@@ -177,6 +177,21 @@ def test_argmax_finds_planted_rows_with_closed_form_logit():
         assert r["zsecond"][m] < r["zmax"][m]
 
 
+def test_binplane_argmax_finds_planted_rows_with_closed_form_logit():
+    case = synth.Case("t", "lmhead", 3, 250, 384, P=3)
+    signs, alpha, x, rows = synth.make_lmhead_binplane(case, seed=15)
+    r = oracle.argmax_binplane(signs, alpha, x)
+    assert np.array_equal(r["idx"], rows.astype(np.int32))
+    xv = oracle.bf16_values(x)
+    for m in range(case.M):
+        want = 0.0
+        for g in range(case.K // 128):
+            sx = np.abs(xv[m, g * 128:(g + 1) * 128]).sum()
+            want += sum(oracle.f16_values(alpha[p, rows[m], g:g + 1])[0] * sx for p in range(case.P))
+        assert r["zmax"][m] == pytest.approx(want, rel=1e-14)
+        assert r["zsecond"][m] < r["zmax"][m]
+
+
 def test_argmax_ties_go_to_lowest_index_and_row_ids_map():
     case = synth.Case("t", "lmhead", 2, 64, 256)
     codes, scales, x, rows = synth.make_lmhead(case, seed=12)
