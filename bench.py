@@ -363,16 +363,13 @@ def main():
 def load_traffic(kernel_name: str):
     """HBM bytes per launch of `kernel_name` from the committed counter summary,
     or None when the kernel source changed after the counters were taken."""
-    import hashlib
+    from speculative_verify_amd.build import device_source_digest
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "speculative_verify_amd", "csrc", "svq.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if t.get("svq_hip_sha256") != digest:
+    if t.get("device_source_sha256") != device_source_digest():
         return None
     return t.get("per_launch_bytes", {}).get(kernel_name)
 

@@ -1,4 +1,6 @@
-// svq.hip -- gfx950 (CDNA4) kernels behind the device entry points of svq.h.
+// kernels.h -- gfx950 (CDNA4) device code behind the entry points of svq.h:
+// helpers, tile loaders and the kernel templates, instantiated by the
+// translation units that launch them (svq_int4.hip, svq_planes.hip).
 //
 // What is computed (see svq.h for the full statements and citations):
 //   W4A16         y = sum_g s[n][g] * sum_{k in g} c[n][k] x[k]
@@ -26,26 +28,15 @@
 // shift and one AND-OR.  Neither s*c nor sum_p alpha_p b_p is ever rounded to
 // bf16; the scales are applied per group in fp32, and the output is rounded
 // to bf16 once, to nearest even.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <type_traits>
 #include <cfloat>
 #include <climits>
 #include <cstdint>
-#include <cstdlib>
 
 #include "svq.h"
-#include "svq_internal.h"
-
-namespace svq {
-char* error_buffer() {
-  static thread_local char buf[512];
-  return buf;
-}
-}  // namespace svq
-
-extern "C" const char* svq_last_error(void) { return svq::error_buffer(); }
 
 namespace {
 
@@ -1029,386 +1020,4 @@ __global__ void __launch_bounds__(64 * MAXW)
     gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
 
-// Streaming-read ceiling: every thread keeps U non-temporal 16-byte loads in
-// flight over a grid-stride walk of the buffer; the last partial round
-// issues its (guarded) loads together as well, so the probe streams any size
-// at full depth.  One checksum per workgroup keeps the loads live.
-__global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ src, size_t n16,
-                                                     uint32_t* __restrict__ sink) {
-  constexpr int U = 8;
-  uint32_t acc = 0;
-  const size_t stride = (size_t)gridDim.x * 256;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + (U - 1) * stride < n16; i += U * stride) {
-    v4u_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + i + u * stride));
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  {
-    v4u_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = v4u_t{0u, 0u, 0u, 0u};
-      if (i + u * stride < n16) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + i + u * stride));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
-  __shared__ uint32_t part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
-}
-
-// ---------------------------------------------------------------------------
-// Host side: validation, launch shapes, dispatch.
-
-std::atomic<int> g_cus[64];
-
-int device_cus(int* cus) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev >= 0 && dev < 64) {
-    const int c = g_cus[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *cus = c;
-      return SVQ_OK;
-    }
-  }
-  int v = 0;
-  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
-  if (v < 1) v = 1;
-  if (dev >= 0 && dev < 64) g_cus[dev].store(v, std::memory_order_relaxed);
-  *cus = v;
-  return SVQ_OK;
-}
-
-bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
-
-int check_linear(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N, int64_t K,
-                 int32_t G, int32_t P) {
-  svq::clear_error();
-  if (!packed || !x || !y) return svq::fail(SVQ_ERR_NULL, "%s: NULL pointer", fn);
-  if (N < 1 || N > (int64_t)INT_MAX - 16) return svq::fail(SVQ_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
-  if (G != SVQ_GROUP) return svq::fail(SVQ_ERR_SHAPE, "%s: group size must be 128 (got %d)", fn, G);
-  if (K < SVQ_GROUP || K % SVQ_GROUP || K > SVQ_MAX_K)
-    return svq::fail(SVQ_ERR_SHAPE, "%s: K=%lld must be a multiple of 128 in [128, %d]", fn, (long long)K, SVQ_MAX_K);
-  if (M < 1 || M > SVQ_MAX_M) return svq::fail(SVQ_ERR_SHAPE, "%s: M=%d must be in 1..16", fn, M);
-  if (P != 0 && (P < 1 || P > SVQ_MAX_P)) return svq::fail(SVQ_ERR_SHAPE, "%s: P=%d must be in 1..6", fn, P);
-  const int64_t N16 = (N + 15) / 16 * 16;
-  if (N16 * K / 2 >= ((int64_t)1 << 31) || (P != 0 && N16 * K / 8 * P >= ((int64_t)1 << 31)))
-    return svq::fail(SVQ_ERR_SHAPE, "%s: packed weights must be smaller than 2 GiB (N=%lld, K=%lld)", fn,
-                     (long long)N, (long long)K);
-  if (misaligned(packed, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: packed weights must be 16-byte aligned", fn);
-  if (misaligned(x, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: activations must be 16-byte aligned", fn);
-  if (misaligned(y, 2)) return svq::fail(SVQ_ERR_ALIGN, "%s: output must be 2-byte aligned", fn);
-  return SVQ_OK;
-}
-
-struct Shape {
-  int KT, NT, gpw, waves, grid, depth;
-};
-
-int env_int(const char* name, int lo, int hi, int dflt) {
-  const char* s = std::getenv(name);
-  const int x = s ? std::atoi(s) : 0;
-  return x >= lo && x <= hi ? x : dflt;
-}
-
-// Launch shape.  A workgroup owns one 16-row tile at a time and splits K
-// across its waves (gpw groups each); the grid is one or a few workgroups per
-// CU walking the row tiles in grid-stride order; the ring depth is the number
-// of tiles whose loads each wave keeps in flight, at most the number of tiles
-// every workgroup owns (so the pipeline tail stays short).
-// wave_quantum: the M <= 16 kernels finish the tiles of a chunk one wave per
-// tile (up to four tiles), so their workgroups carry a multiple of four waves.
-// Measured on MI355X (rocprofv3 kernel traces of the decode, verify and head
-// shapes at K = 4096, sweeping both knobs): the M = 1 mat-vecs run best at
-// two workgroups per CU with a ring of <= 2 tiles, everything else at one
-// workgroup per CU; a ring of 2 tiles already keeps more bytes in flight
-// than the memory system's bandwidth-latency product, and deeper rings were
-// slower for the W4A16 kernels (the sign-plane verify kernel, with more
-// arithmetic per byte, gains a little from 3).
-struct LaunchPref {
-  int wgs_per_cu, max_depth;
-};
-constexpr LaunchPref kPrefGemv = {2, 2};
-constexpr LaunchPref kPrefGemmW4 = {1, 2};
-constexpr LaunchPref kPrefGemmPlanes = {1, 3};
-constexpr LaunchPref kPrefHeadM1 = {1, 2};
-constexpr LaunchPref kPrefHeadM16 = {1, 2};
-
-int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* s) {
-  int cus = 0;
-  if (int rc = device_cus(&cus)) return rc;
-  s->KT = (int)(K / 128);
-  s->NT = (int)((N + 15) / 16);
-  s->gpw = s->KT <= 8 ? 1 : s->KT <= 16 ? 2 : 4;
-  s->waves = (s->KT + s->gpw - 1) / s->gpw;
-  s->waves = (s->waves + wave_quantum - 1) / wave_quantum * wave_quantum;
-  // SVQ_WG_PER_CU / SVQ_PIPE_DEPTH override the preferences (for tuning runs).
-  const int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
-  s->grid = s->NT < want ? s->NT : want;
-  const int tmin = s->NT / s->grid;
-  const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 6, pref.max_depth);
-  s->depth = tmin < 1 ? 1 : tmin > dmax ? dmax : tmin;
-  return SVQ_OK;
-}
-
-int launched(const char* fn) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-  return SVQ_OK;
-}
-
-template <int V>
-using ic = std::integral_constant<int, V>;
-
-// Calls launch(ic<GPW>, ic<MAXW>, ic<D>) for the shape's compile-time
-// parameters.  Depths above 2 are instantiated only for the 8-wave shapes.
-template <class L>
-void dispatch(const Shape& sh, L&& launch) {
-  auto depth = [&](auto G, auto W, auto DM) {
-    if constexpr (decltype(DM)::value >= 6)
-      if (sh.depth >= 6) return launch(G, W, ic<6>{});
-    if constexpr (decltype(DM)::value >= 5)
-      if (sh.depth == 5) return launch(G, W, ic<5>{});
-    if constexpr (decltype(DM)::value >= 4)
-      if (sh.depth == 4) return launch(G, W, ic<4>{});
-    if constexpr (decltype(DM)::value >= 3)
-      if (sh.depth == 3) return launch(G, W, ic<3>{});
-    if (sh.depth >= 2) return launch(G, W, ic<2>{});
-    launch(G, W, ic<1>{});
-  };
-  if (sh.gpw == 1)
-    depth(ic<1>{}, ic<8>{}, ic<2>{});
-  else if (sh.gpw == 2)
-    depth(ic<2>{}, ic<8>{}, ic<2>{});
-  else if (sh.waves <= 8)
-    depth(ic<4>{}, ic<8>{}, ic<6>{});
-  else
-    depth(ic<4>{}, ic<16>{}, ic<2>{});
-}
-
-template <class L>
-void dispatch_p(int P, L&& launch) {
-  switch (P) {
-    case 1: launch(ic<1>{}); break;
-    case 2: launch(ic<2>{}); break;
-    case 3: launch(ic<3>{}); break;
-    case 4: launch(ic<4>{}); break;
-    case 5: launch(ic<5>{}); break;
-    default: launch(ic<6>{}); break;
-  }
-}
-
-#define SVQ_KARGS(G, W, D) decltype(G)::value, decltype(W)::value, decltype(D)::value
-
-// Deepest ring the sign-plane kernels keep in registers without spilling:
-// a slot holds P sign dwords and P scale runs per group.
-template <int P>
-constexpr int max_depth_planes() { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
-#define SVQ_KARGS_P(G, W, D, Pc)                                                                        \
-  decltype(G)::value, decltype(W)::value,                                                              \
-      (decltype(D)::value < max_depth_planes<decltype(Pc)::value>() ? decltype(D)::value               \
-                                                                    : max_depth_planes<decltype(Pc)::value>()), \
-      decltype(Pc)::value
-
 }  // namespace
-
-extern "C" {
-
-size_t svq_lmhead_workspace_bytes(int32_t M) {
-  if (M < 1 || M > SVQ_MAX_M) return 0;
-  return (size_t)kWsBytes;
-}
-
-int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N, int64_t K, int32_t G,
-               void* stream) {
-  if (int rc = check_linear("gemv_w4a16", packed, x, y, 1, N, K, G, 0)) return rc;
-  Shape sh;
-  if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
-  dispatch(sh, [&](auto G, auto W, auto D) {
-    hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                       packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N, sh.KT, sh.NT);
-  });
-  return launched("gemv_w4a16");
-}
-
-int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N, int64_t K, int32_t G, int32_t P,
-                  void* stream) {
-  if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemv_binplane: P=0 must be in 1..6");
-  if (int rc = check_linear("gemv_binplane", packed, x, y, 1, N, K, G, P)) return rc;
-  Shape sh;
-  if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
-  dispatch_p(P, [&](auto Pc) {
-    dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
-                         dim3(64 * sh.waves), 0, st, packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N,
-                         sh.KT, sh.NT);
-    });
-  });
-  return launched("gemv_binplane");
-}
-
-int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
-                      int32_t G, void* stream) {
-  if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0)) return rc;
-  Shape sh;
-  if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  dispatch(sh, [&](auto G, auto W, auto D) {
-    hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                       packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
-  });
-  return launched("gemm_smallm_w4a16");
-}
-
-int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
-                         int32_t G, int32_t P, void* stream) {
-  if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemm_smallm_binplane: P=0 must be in 1..6");
-  if (int rc = check_linear("gemm_smallm_binplane", packed, X, Y, M, N, K, G, P)) return rc;
-  Shape sh;
-  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  dispatch_p(P, [&](auto Pc) {
-    dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
-                         dim3(64 * sh.waves), 0, st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N,
-                         sh.KT, sh.NT);
-    });
-  });
-  return launched("gemm_smallm_binplane");
-}
-
-}  // extern "C"
-
-namespace {
-
-// Validation and launch shared by lmhead_argmax and lmhead_verify_greedy.
-// P = 0: INT4 weights; P >= 1: P sign planes.
-int launch_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
-                int32_t G, int32_t P, const HeadOut& ho, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, P)) return rc;
-  if (!ho.max) return svq::fail(SVQ_ERR_NULL, "%s: NULL maxlogit", fn);
-  if (misaligned(ho.idx, 4) || misaligned(ho.max, 4) || (ho.row_ids && misaligned(ho.row_ids, 4)))
-    return svq::fail(SVQ_ERR_ALIGN, "%s: argmax, maxlogit and row_ids must be 4-byte aligned", fn);
-  if (!workspace || workspace_bytes < svq_lmhead_workspace_bytes(M))
-    return svq::fail(SVQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, svq_lmhead_workspace_bytes(M),
-                     workspace ? workspace_bytes : (size_t)0);
-  if (misaligned(workspace, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-  Shape sh;
-  const LaunchPref pref = P ? (M == 1 ? kPrefHeadM1 : kPrefGemmPlanes) : (M == 1 ? kPrefHeadM1 : kPrefHeadM16);
-  if (int rc = plan(N, K, M == 1 ? 1 : 4, pref, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  if (P) {
-    dispatch_p(P, [&](auto Pc) {
-      dispatch(sh, [&](auto G, auto W, auto D) {
-        if (M == 1)
-          hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves),
-                             0, st, packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
-        else
-          hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves),
-                             0, st, packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
-      });
-    });
-  } else if (M == 1) {
-    dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
-    });
-  } else {
-    dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
-    });
-  }
-  return launched(fn);
-}
-
-__global__ void __launch_bounds__(64) k_verify_greedy(const int32_t* __restrict__ target,
-                                                      const int32_t* __restrict__ draft, int M,
-                                                      int32_t* __restrict__ accept) {
-  if (threadIdx.x == 0) accept[0] = greedy_accept_len(target, draft, M);
-}
-
-}  // namespace
-
-extern "C" {
-
-int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
-                  const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace, size_t workspace_bytes,
-                  void* stream) {
-  return launch_head("lmhead_argmax", packed, X, M, N, K, G, 0, HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr},
-                     workspace, workspace_bytes, stream);
-}
-
-int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
-                           int32_t P, const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  svq::clear_error();
-  if (P < 1 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "lmhead_argmax_binplane: P=%d must be in 1..6", P);
-  return launch_head("lmhead_argmax_binplane", packed, X, M, N, K, G, P,
-                     HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr}, workspace, workspace_bytes, stream);
-}
-
-int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
-                         const int32_t* row_ids, const int32_t* draft_ids, int32_t* argmax, float* maxlogit,
-                         int32_t* accept_len, void* workspace, size_t workspace_bytes, void* stream) {
-  svq::clear_error();
-  if (!accept_len || (M > 1 && !draft_ids))
-    return svq::fail(SVQ_ERR_NULL, "lmhead_verify_greedy: NULL accept_len or draft_ids");
-  if (misaligned(accept_len, 4) || (draft_ids && misaligned(draft_ids, 4)))
-    return svq::fail(SVQ_ERR_ALIGN, "lmhead_verify_greedy: accept_len and draft_ids must be 4-byte aligned");
-  return launch_head("lmhead_verify_greedy", packed, X, M, N, K, G, 0,
-                     HeadOut{row_ids, argmax, maxlogit, draft_ids, accept_len}, workspace, workspace_bytes, stream);
-}
-
-int verify_greedy(const int32_t* target_ids, const int32_t* draft_ids, int32_t M, int32_t* accept_len, void* stream) {
-  svq::clear_error();
-  if (!target_ids || !accept_len || (M > 1 && !draft_ids))
-    return svq::fail(SVQ_ERR_NULL, "verify_greedy: NULL pointer");
-  if (M < 1 || M > SVQ_MAX_M) return svq::fail(SVQ_ERR_SHAPE, "verify_greedy: M=%d must be in 1..16", M);
-  if (misaligned(target_ids, 4) || misaligned(accept_len, 4) || (draft_ids && misaligned(draft_ids, 4)))
-    return svq::fail(SVQ_ERR_ALIGN, "verify_greedy: pointers must be 4-byte aligned");
-  hipLaunchKernelGGL(k_verify_greedy, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), target_ids,
-                     draft_ids, M, accept_len);
-  return launched("verify_greedy");
-}
-
-int svq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t wgs_per_cu, void* stream) {
-  svq::clear_error();
-  if (!src || !sink) return svq::fail(SVQ_ERR_NULL, "svq_stream_read: NULL pointer");
-  if (bytes == 0 || bytes % 16 || bytes >= ((size_t)1 << 31))
-    return svq::fail(SVQ_ERR_SHAPE, "svq_stream_read: bytes must be a positive multiple of 16 below 2 GiB");
-  if (wgs_per_cu < 0 || wgs_per_cu > 8)
-    return svq::fail(SVQ_ERR_SHAPE, "svq_stream_read: wgs_per_cu must be in 0..8 (got %d)", wgs_per_cu);
-  if (misaligned(src, 16) || misaligned(sink, 4)) return svq::fail(SVQ_ERR_ALIGN, "svq_stream_read: misaligned pointer");
-  int cus = 0;
-  if (int rc = device_cus(&cus)) return rc;
-  // Eight loads per thread in flight; wgs_per_cu workgroups per CU (0: one,
-  // which measured best for large buffers); fewer when the buffer is smaller
-  // than one full round.
-  const size_t per_wg = (size_t)256 * 16 * 8;
-  size_t grid = (bytes + per_wg - 1) / per_wg;
-  const size_t cap = (size_t)cus * (wgs_per_cu == 0 ? 1 : wgs_per_cu);
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                     reinterpret_cast<const uint4*>(src), bytes / 16, sink);
-  return launched("svq_stream_read");
-}
-
-}  // extern "C"

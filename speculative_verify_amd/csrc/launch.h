@@ -1,0 +1,185 @@
+// launch.h -- host-side helpers shared by the device entry points:
+// argument checks, launch shapes and compile-time dispatch.
+#pragma once
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <type_traits>
+
+#include "kernels.h"
+#include "svq.h"
+#include "svq_internal.h"
+
+namespace {
+
+inline std::atomic<int> g_cus[64];
+
+inline int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return SVQ_OK;
+    }
+  }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  if (v < 1) v = 1;
+  if (dev >= 0 && dev < 64) g_cus[dev].store(v, std::memory_order_relaxed);
+  *cus = v;
+  return SVQ_OK;
+}
+
+inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+inline int check_linear(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N, int64_t K,
+                 int32_t G, int32_t P) {
+  svq::clear_error();
+  if (!packed || !x || !y) return svq::fail(SVQ_ERR_NULL, "%s: NULL pointer", fn);
+  if (N < 1 || N > (int64_t)INT_MAX - 16) return svq::fail(SVQ_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (G != SVQ_GROUP) return svq::fail(SVQ_ERR_SHAPE, "%s: group size must be 128 (got %d)", fn, G);
+  if (K < SVQ_GROUP || K % SVQ_GROUP || K > SVQ_MAX_K)
+    return svq::fail(SVQ_ERR_SHAPE, "%s: K=%lld must be a multiple of 128 in [128, %d]", fn, (long long)K, SVQ_MAX_K);
+  if (M < 1 || M > SVQ_MAX_M) return svq::fail(SVQ_ERR_SHAPE, "%s: M=%d must be in 1..16", fn, M);
+  if (P != 0 && (P < 1 || P > SVQ_MAX_P)) return svq::fail(SVQ_ERR_SHAPE, "%s: P=%d must be in 1..6", fn, P);
+  const int64_t N16 = (N + 15) / 16 * 16;
+  if (N16 * K / 2 >= ((int64_t)1 << 31) || (P != 0 && N16 * K / 8 * P >= ((int64_t)1 << 31)))
+    return svq::fail(SVQ_ERR_SHAPE, "%s: packed weights must be smaller than 2 GiB (N=%lld, K=%lld)", fn,
+                     (long long)N, (long long)K);
+  if (misaligned(packed, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: packed weights must be 16-byte aligned", fn);
+  if (misaligned(x, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: activations must be 16-byte aligned", fn);
+  if (misaligned(y, 2)) return svq::fail(SVQ_ERR_ALIGN, "%s: output must be 2-byte aligned", fn);
+  return SVQ_OK;
+}
+
+struct Shape {
+  int KT, NT, gpw, waves, grid, depth;
+};
+
+inline int env_int(const char* name, int lo, int hi, int dflt) {
+  const char* s = std::getenv(name);
+  const int x = s ? std::atoi(s) : 0;
+  return x >= lo && x <= hi ? x : dflt;
+}
+
+// Launch shape.  A workgroup owns one 16-row tile at a time and splits K
+// across its waves (gpw groups each); the grid is one or a few workgroups per
+// CU walking the row tiles in grid-stride order; the ring depth is the number
+// of tiles whose loads each wave keeps in flight, at most the number of tiles
+// every workgroup owns (so the pipeline tail stays short).
+// wave_quantum: the M <= 16 kernels finish the tiles of a chunk one wave per
+// tile (up to four tiles), so their workgroups carry a multiple of four waves.
+// Measured on MI355X (rocprofv3 kernel traces of the decode, verify and head
+// shapes at K = 4096, sweeping both knobs): the M = 1 mat-vecs run best at
+// two workgroups per CU with a ring of <= 2 tiles, everything else at one
+// workgroup per CU; a ring of 2 tiles already keeps more bytes in flight
+// than the memory system's bandwidth-latency product, and deeper rings were
+// slower for the W4A16 kernels (the sign-plane verify kernel, with more
+// arithmetic per byte, gains a little from 3).
+struct LaunchPref {
+  int wgs_per_cu, max_depth;
+};
+constexpr LaunchPref kPrefGemv = {2, 2};
+constexpr LaunchPref kPrefGemmW4 = {1, 2};
+constexpr LaunchPref kPrefGemmPlanes = {1, 3};
+constexpr LaunchPref kPrefHeadM1 = {1, 2};
+constexpr LaunchPref kPrefHeadM16 = {1, 2};
+
+inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* s) {
+  int cus = 0;
+  if (int rc = device_cus(&cus)) return rc;
+  s->KT = (int)(K / 128);
+  s->NT = (int)((N + 15) / 16);
+  s->gpw = s->KT <= 8 ? 1 : s->KT <= 16 ? 2 : 4;
+  s->waves = (s->KT + s->gpw - 1) / s->gpw;
+  s->waves = (s->waves + wave_quantum - 1) / wave_quantum * wave_quantum;
+  // SVQ_WG_PER_CU / SVQ_PIPE_DEPTH override the preferences (for tuning runs).
+  const int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
+  s->grid = s->NT < want ? s->NT : want;
+  const int tmin = s->NT / s->grid;
+  const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 6, pref.max_depth);
+  s->depth = tmin < 1 ? 1 : tmin > dmax ? dmax : tmin;
+  return SVQ_OK;
+}
+
+inline int launched(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return SVQ_OK;
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Calls launch(ic<GPW>, ic<MAXW>, ic<D>) for the shape's compile-time
+// parameters.  Depths above 2 are instantiated only for the 8-wave shapes.
+template <class L>
+void dispatch(const Shape& sh, L&& launch) {
+  auto depth = [&](auto G, auto W, auto DM) {
+    if constexpr (decltype(DM)::value >= 6)
+      if (sh.depth >= 6) return launch(G, W, ic<6>{});
+    if constexpr (decltype(DM)::value >= 5)
+      if (sh.depth == 5) return launch(G, W, ic<5>{});
+    if constexpr (decltype(DM)::value >= 4)
+      if (sh.depth == 4) return launch(G, W, ic<4>{});
+    if constexpr (decltype(DM)::value >= 3)
+      if (sh.depth == 3) return launch(G, W, ic<3>{});
+    if (sh.depth >= 2) return launch(G, W, ic<2>{});
+    launch(G, W, ic<1>{});
+  };
+  if (sh.gpw == 1)
+    depth(ic<1>{}, ic<8>{}, ic<2>{});
+  else if (sh.gpw == 2)
+    depth(ic<2>{}, ic<8>{}, ic<2>{});
+  else if (sh.waves <= 8)
+    depth(ic<4>{}, ic<8>{}, ic<6>{});
+  else
+    depth(ic<4>{}, ic<16>{}, ic<2>{});
+}
+
+template <class L>
+void dispatch_p(int P, L&& launch) {
+  switch (P) {
+    case 1: launch(ic<1>{}); break;
+    case 2: launch(ic<2>{}); break;
+    case 3: launch(ic<3>{}); break;
+    case 4: launch(ic<4>{}); break;
+    case 5: launch(ic<5>{}); break;
+    default: launch(ic<6>{}); break;
+  }
+}
+
+#define SVQ_KARGS(G, W, D) decltype(G)::value, decltype(W)::value, decltype(D)::value
+
+// Deepest ring the sign-plane kernels keep in registers without spilling:
+// a slot holds P sign dwords and P scale runs per group.
+template <int P>
+constexpr int max_depth_planes() { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
+#define SVQ_KARGS_P(G, W, D, Pc)                                                                        \
+  decltype(G)::value, decltype(W)::value,                                                              \
+      (decltype(D)::value < max_depth_planes<decltype(Pc)::value>() ? decltype(D)::value               \
+                                                                    : max_depth_planes<decltype(Pc)::value>()), \
+      decltype(Pc)::value
+
+
+// Argument checks shared by the head entry points (P = 0: INT4 weights;
+// P >= 1: P sign planes).
+inline int check_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
+                      int32_t G, int32_t P, const HeadOut& ho, void* workspace, size_t workspace_bytes) {
+  if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, P)) return rc;
+  if (!ho.max) return svq::fail(SVQ_ERR_NULL, "%s: NULL maxlogit", fn);
+  if (misaligned(ho.idx, 4) || misaligned(ho.max, 4) || (ho.row_ids && misaligned(ho.row_ids, 4)))
+    return svq::fail(SVQ_ERR_ALIGN, "%s: argmax, maxlogit and row_ids must be 4-byte aligned", fn);
+  if (!workspace || workspace_bytes < svq_lmhead_workspace_bytes(M))
+    return svq::fail(SVQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, svq_lmhead_workspace_bytes(M),
+                     workspace ? workspace_bytes : (size_t)0);
+  if (misaligned(workspace, 16)) return svq::fail(SVQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return SVQ_OK;
+}
+
+}  // namespace

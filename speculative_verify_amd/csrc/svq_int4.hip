@@ -1,0 +1,91 @@
+// svq_int4.hip -- device entry points for W4A16 weights (symmetric INT4
+// codes, one bf16 scale per group of 128): decode mat-vec, small-M verify
+// mat-mul, and the LM head with fused argmax and greedy acceptance.
+//   y = sum_g s[n][g] * sum_{k in g} c[n][k] x[k]
+//   (Efficient Qwen Competition report, sec. 2.1 and 3.3)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "launch.h"
+#include "svq.h"
+#include "svq_internal.h"
+
+namespace {
+
+// Launch of the W4A16 head once its arguments are checked.
+int launch_head_w4a16(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
+                      int32_t G, const HeadOut& ho, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_head(fn, packed, X, M, N, K, G, 0, ho, workspace, workspace_bytes)) return rc;
+  Shape sh;
+  if (int rc = plan(N, K, M == 1 ? 1 : 4, M == 1 ? kPrefHeadM1 : kPrefHeadM16, &sh)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  if (M == 1) {
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                         packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
+    });
+  } else {
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                         packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
+    });
+  }
+  return launched(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N, int64_t K, int32_t G,
+               void* stream) {
+  if (int rc = check_linear("gemv_w4a16", packed, x, y, 1, N, K, G, 0)) return rc;
+  Shape sh;
+  if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
+  dispatch(sh, [&](auto G, auto W, auto D) {
+    hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                       packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N, sh.KT, sh.NT);
+  });
+  return launched("gemv_w4a16");
+}
+
+int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
+                      int32_t G, void* stream) {
+  if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0)) return rc;
+  Shape sh;
+  if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  dispatch(sh, [&](auto G, auto W, auto D) {
+    hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                       packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
+  });
+  return launched("gemm_smallm_w4a16");
+}
+
+int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                  const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return launch_head_w4a16("lmhead_argmax", packed, X, M, N, K, G, HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr},
+                     workspace, workspace_bytes, stream);
+}
+
+int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                         const int32_t* row_ids, const int32_t* draft_ids, int32_t* argmax, float* maxlogit,
+                         int32_t* accept_len, void* workspace, size_t workspace_bytes, void* stream) {
+  svq::clear_error();
+  if (!accept_len || (M > 1 && !draft_ids))
+    return svq::fail(SVQ_ERR_NULL, "lmhead_verify_greedy: NULL accept_len or draft_ids");
+  if (misaligned(accept_len, 4) || (draft_ids && misaligned(draft_ids, 4)))
+    return svq::fail(SVQ_ERR_ALIGN, "lmhead_verify_greedy: accept_len and draft_ids must be 4-byte aligned");
+  return launch_head_w4a16("lmhead_verify_greedy", packed, X, M, N, K, G,
+                           HeadOut{row_ids, argmax, maxlogit, draft_ids, accept_len}, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

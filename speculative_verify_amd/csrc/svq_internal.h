@@ -21,6 +21,13 @@ __attribute__((format(printf, 2, 3))) inline int fail(int code, const char* fmt,
   return code;
 }
 
+// One-token sign-plane LM head (arguments already checked): launches the
+// mat-vec kernel with fused argmax.  Defined with the mat-vec kernels so that
+// their instantiations stay in one translation unit.
+int launch_binplane_head_m1(const char* fn, const uint8_t* packed, const uint16_t* x, int64_t N, int64_t K,
+                            int32_t P, const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace,
+                            void* stream);
+
 inline int64_t round16(int64_t n) { return (n + 15) / 16 * 16; }
 inline int64_t round4(int64_t n) { return (n + 3) / 4 * 4; }
 

@@ -1,0 +1,60 @@
+// svq_planes_gemm.hip -- small-M device entry points for binary-plane
+// weights (P sign planes, one fp16 scale per plane, row and group of 128):
+// the verify mat-mul and the LM head with fused argmax, whose one-token case
+// launches the mat-vec kernel of svq_planes_gemv.hip.
+//   Y = X W^T with W[n][k] = sum_p alpha[p][n][k/128] * b[p][n][k]
+//   (ShiftAddQwen README, intro and "Method / Format")
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "launch.h"
+#include "svq.h"
+#include "svq_internal.h"
+
+extern "C" {
+
+int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
+                         int32_t G, int32_t P, void* stream) {
+  if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemm_smallm_binplane: P=0 must be in 1..6");
+  if (int rc = check_linear("gemm_smallm_binplane", packed, X, Y, M, N, K, G, P)) return rc;
+  Shape sh;
+  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  dispatch_p(P, [&](auto Pc) {
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
+                         dim3(64 * sh.waves), 0, st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N,
+                         sh.KT, sh.NT);
+    });
+  });
+  return launched("gemm_smallm_binplane");
+}
+
+int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                           int32_t P, const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  svq::clear_error();
+  if (P < 1 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "lmhead_argmax_binplane: P=%d must be in 1..6", P);
+  const char* fn = "lmhead_argmax_binplane";
+  const HeadOut ho{row_ids, argmax, maxlogit, nullptr, nullptr};
+  if (int rc = check_head(fn, packed, X, M, N, K, G, P, ho, workspace, workspace_bytes)) return rc;
+  if (M == 1)
+    return svq::launch_binplane_head_m1(fn, packed, X, N, K, P, row_ids, argmax, maxlogit, workspace, stream);
+  Shape sh;
+  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  dispatch_p(P, [&](auto Pc) {
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+                         st, packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
+    });
+  });
+  return launched(fn);
+}
+
+}  // extern "C"
