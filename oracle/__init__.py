@@ -13,9 +13,12 @@ activations) and returns fp64 results:
   frozen symmetric per-group scales, group 128 along the input dimension);
 * ``linear_binplane`` y = sum_g sum_p alpha[p,n,g] sum_{k in g} b[p,n,k] x[k]
   (ShiftAddQwen README, intro and "Format");
+* ``linear_sa``       the same sum with alpha[p,n,g] = d[n, g*G/256] * a[p,n,g]:
+  u8 scale codes per (plane, group) and one fp16 d per 256-weight
+  super-block (ShiftAddQwen README, "Method / Format", the sa* types);
 * ``argmax_w4a16``    greedy token = lowest index attaining the max logit
   (DFlash summary sec. 4.1; MTP study sec. 3.3 for the trimmed-head row map);
-* ``pack_int4`` / ``pack_binplane`` state the packed byte layouts element by
+* ``pack_int4`` / ``pack_binplane`` / ``pack_sa`` state the packed byte layouts element by
   element (the pages name the formats, the layout is this project's own).
 
 Each returned ``a`` array is sum_k |w[n,k] x[k]|, the scale of the stated
@@ -68,6 +71,12 @@ def _load():
     lib.oracle_linear_w4a16.restype = ctypes.c_int
     lib.oracle_linear_binplane.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P]
     lib.oracle_linear_binplane.restype = ctypes.c_int
+    lib.oracle_linear_sa.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, P]
+    lib.oracle_linear_sa.restype = ctypes.c_int
+    lib.oracle_sa_blob_bytes.argtypes = [I64, I64, I64, I64]
+    lib.oracle_sa_blob_bytes.restype = I64
+    lib.oracle_pack_sa.argtypes = [P, P, P, I64, I64, I64, I64, P]
+    lib.oracle_pack_sa.restype = ctypes.c_int
     lib.oracle_argmax_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.oracle_argmax_w4a16.restype = ctypes.c_int
     lib.oracle_argmax_binplane.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]
@@ -154,6 +163,25 @@ def linear_binplane(signs, alpha, x, G: int = 128):
     return y, a
 
 
+def linear_sa(signs, codes, d, x, G: int = 128):
+    """(y, a) fp64 [M][N] for signs [P][N][K] in {-1,+1}, u8 scale codes
+    [P][N][K/G], fp16 super-block scales d [N][K/256] (bits), x [M][K] bf16."""
+    signs = _c(signs, np.int8)
+    codes = _c(codes, np.uint8)
+    d = _c(d, np.uint16)
+    x2 = _c(np.atleast_2d(x), np.uint16)
+    P, N, K = signs.shape
+    M = x2.shape[0]
+    assert x2.shape[1] == K and codes.shape == (P, N, K // G) and d.shape == (N, K // 256)
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    rc = _load().oracle_linear_sa(_ptr(signs), _ptr(codes), _ptr(d), _ptr(x2), M, N, K, G, P,
+                                  _ptr(y), _ptr(a))
+    if rc:
+        raise ValueError(f"oracle_linear_sa rc={rc}")
+    return y, a
+
+
 def argmax_w4a16(codes, scales, x, G: int = 128, row_ids=None):
     """dict(out, idx, zmax, amax, zsecond), each of length M."""
     codes = _c(codes, np.int8)
@@ -231,4 +259,18 @@ def pack_binplane(signs, alpha) -> np.ndarray:
     rc = lib.oracle_pack_binplane(_ptr(signs), _ptr(alpha), N, K, P, _ptr(blob))
     if rc:
         raise ValueError(f"oracle_pack_binplane rc={rc}")
+    return blob
+
+
+def pack_sa(signs, codes, d, G: int = 128) -> np.ndarray:
+    """Packed sa blob (uint8) per the element-wise layout statement."""
+    signs = _c(signs, np.int8)
+    codes = _c(codes, np.uint8)
+    d = _c(d, np.uint16)
+    P, N, K = signs.shape
+    lib = _load()
+    blob = np.empty(int(lib.oracle_sa_blob_bytes(N, K, G, P)), np.uint8)
+    rc = lib.oracle_pack_sa(_ptr(signs), _ptr(codes), _ptr(d), N, K, G, P, _ptr(blob))
+    if rc:
+        raise ValueError(f"oracle_pack_sa rc={rc}")
     return blob

@@ -16,6 +16,11 @@
  *    sum of sign planes, w = sum_p alpha_p * b_p with b_p in {-1,+1} and one
  *    scale per (plane, group) along the input dimension; the mat-vec is a
  *    signed add per plane followed by one multiply per plane and group.
+ *  - ShiftAddQwen README, "Method / Format" (the sa* types): inside a
+ *    super-block of 256 weights of one row along the input dimension, each
+ *    sign plane has one unsigned 8-bit scale code a per group of G in
+ *    {64, 128, 256} weights, and the super-block has one fp16 scale d; the
+ *    plane's scale for that group is alpha = d * a.
  *  - DFlash summary, sec. 4.1 and the tech report sec. 2.2: the target
  *    verifies a drafted block in one parallel pass, and greedy (temperature 0)
  *    decoding takes the argmax of the target's logits.
@@ -49,6 +54,13 @@
  *     means b = -1.  Rows n >= N hold b = +1.
  *     Then fp16 alphas: alpha[p][n][g] at entry (p*N16 + n)*KT4 + g; entries
  *     g >= KT and padded rows are 0.
+ *   sa blob (P planes, group G in {64, 128, 256}, K a multiple of 256).
+ *     The sign section is the binary-plane blob's, byte for byte.
+ *     Then u8 codes: a[p][n][g] at byte (p*N16 + n)*CG + g of the code
+ *     section, CG = KT4*128/G (a row spans KT4 128-wide column tiles);
+ *     entries g >= K/G and padded rows are 0.
+ *     Then fp16 d: d[n][j] (super-block j = k/256) at entry n*KS2 + j of
+ *     the last section, KS2 = KT4/2; entries j >= K/256 and padded rows are 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -179,6 +191,51 @@ int oracle_linear_binplane(const int8_t* signs, const uint16_t* alpha,
           for (int64_t p = 0; p < P; ++p)
             w += oracle_f16_value(alpha[(p * N + n) * ng + g]) *
                  (double)signs[(p * N + n) * K + k];
+          total_abs += fabs(w * xv[m * K + k]);
+        }
+      }
+      y[m * N + n] = total;
+      a[m * N + n] = total_abs;
+    }
+  }
+  free(xv);
+  return 0;
+}
+
+/*
+ * sa* ShiftAdd layer (ShiftAddQwen README, "Method / Format"): the planes'
+ * scales are stored as alpha[p][n][g] = d[n][j] * a[p][n][g], j the
+ * super-block (256 weights) holding group g:
+ *   y[m][n] = sum_g sum_p d[n][g*G/256] * a[p][n][g] * ( sum_{k in g} b[p][n][k] * x[m][k] )
+ *   a_tol[m][n] = sum_k | w[n][k] * x[m][k] |,  w[n][k] = sum_p alpha[p][n][g(k)] b[p][n][k]
+ * signs [P][N][K] in {-1,+1}, codes [P][N][K/G] u8, d [N][K/256] fp16 bits.
+ * d * a is exact in fp64 (11 by 8 significant bits).  Requires K % 256 == 0
+ * and G dividing 256.
+ */
+int oracle_linear_sa(const int8_t* signs, const uint8_t* codes, const uint16_t* d,
+                     const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                     int64_t G, int64_t P, double* y, double* a) {
+  if (M < 1 || N < 1 || K < 256 || K % 256 || G < 1 || 256 % G || P < 1) return -1;
+  const int64_t ng = K / G, ns = K / 256;
+  double* xv = decode_bf16_array(x, M * K);
+  if (!xv) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t m = 0; m < M; ++m) {
+      double total = 0.0, total_abs = 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        const double dj = oracle_f16_value(d[n * ns + (g * G) / 256]);
+        for (int64_t p = 0; p < P; ++p) {
+          const double al = dj * (double)codes[(p * N + n) * ng + g];
+          double inner = 0.0;
+          for (int64_t k = g * G; k < (g + 1) * G; ++k)
+            inner += (double)signs[(p * N + n) * K + k] * xv[m * K + k];
+          total += al * inner;
+        }
+        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+          double w = 0.0;
+          for (int64_t p = 0; p < P; ++p)
+            w += dj * (double)codes[(p * N + n) * ng + g] * (double)signs[(p * N + n) * K + k];
           total_abs += fabs(w * xv[m * K + k]);
         }
       }
@@ -326,11 +383,11 @@ int64_t oracle_binplane_blob_bytes(int64_t N, int64_t K, int64_t P) {
   return N16 * (K / 8) * P + P * N16 * KT4 * 2;
 }
 
-int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
-                         int64_t K, int64_t P, uint8_t* blob) {
-  if (N < 1 || K < 128 || K % 128 || P < 1) return -1;
-  const int64_t N16 = (N + 15) / 16 * 16, KT = K / 128, ng = K / 128;
-  memset(blob, 0, (size_t)oracle_binplane_blob_bytes(N, K, P));
+/* Sign section shared by the binary-plane and sa blobs: returns -2 on a
+ * sign outside {-1, +1}.  The blob must be zeroed. */
+static int put_sign_planes(const int8_t* signs, int64_t N, int64_t K, int64_t P,
+                           uint8_t* blob) {
+  const int64_t N16 = (N + 15) / 16 * 16, KT = K / 128;
   for (int64_t p = 0; p < P; ++p)
     for (int64_t n = 0; n < N16; ++n)
       for (int64_t k = 0; k < K; ++k) {
@@ -345,6 +402,15 @@ int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
                                 : 4 * (int)t + (int)(j / 2);
         or_dword(blob, off, 1u << bit);
       }
+  return 0;
+}
+
+int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
+                         int64_t K, int64_t P, uint8_t* blob) {
+  if (N < 1 || K < 128 || K % 128 || P < 1) return -1;
+  const int64_t N16 = (N + 15) / 16 * 16, KT = K / 128, ng = K / 128;
+  memset(blob, 0, (size_t)oracle_binplane_blob_bytes(N, K, P));
+  if (put_sign_planes(signs, N, K, P, blob)) return -2;
   const int64_t aoff = (N16 / 16) * KT * 256 * P, KT4 = (KT + 3) / 4 * 4;
   for (int64_t p = 0; p < P; ++p)
     for (int64_t n = 0; n < N16; ++n)
@@ -354,5 +420,31 @@ int oracle_pack_binplane(const int8_t* signs, const uint16_t* alpha, int64_t N,
         blob[aoff + 2 * e] = (uint8_t)(a & 0xff);
         blob[aoff + 2 * e + 1] = (uint8_t)(a >> 8);
       }
+  return 0;
+}
+
+int64_t oracle_sa_blob_bytes(int64_t N, int64_t K, int64_t G, int64_t P) {
+  const int64_t N16 = (N + 15) / 16 * 16, KT4 = (K / 128 + 3) / 4 * 4;
+  return N16 * (K / 8) * P + P * N16 * (KT4 * 128 / G) + N16 * (KT4 / 2) * 2;
+}
+
+int oracle_pack_sa(const int8_t* signs, const uint8_t* codes, const uint16_t* d,
+                   int64_t N, int64_t K, int64_t G, int64_t P, uint8_t* blob) {
+  if (N < 1 || K < 256 || K % 256 || (G != 64 && G != 128 && G != 256) || P < 1) return -1;
+  const int64_t N16 = (N + 15) / 16 * 16, KT4 = (K / 128 + 3) / 4 * 4;
+  const int64_t ng = K / G, ns = K / 256, CG = KT4 * 128 / G, KS2 = KT4 / 2;
+  memset(blob, 0, (size_t)oracle_sa_blob_bytes(N, K, G, P));
+  if (put_sign_planes(signs, N, K, P, blob)) return -2;
+  const int64_t coff = N16 * (K / 8) * P, doff = coff + P * N16 * CG;
+  for (int64_t p = 0; p < P; ++p)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t g = 0; g < ng; ++g)
+        blob[coff + (p * N16 + n) * CG + g] = codes[(p * N + n) * ng + g];
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < ns; ++j) {
+      const uint16_t v = d[n * ns + j];
+      blob[doff + 2 * (n * KS2 + j)] = (uint8_t)(v & 0xff);
+      blob[doff + 2 * (n * KS2 + j) + 1] = (uint8_t)(v >> 8);
+    }
   return 0;
 }

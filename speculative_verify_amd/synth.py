@@ -10,7 +10,10 @@ Draw order for every case (numpy ``default_rng(seed)``, PCG64):
      -- or sign bits ``integers(0, 2)`` per (plane, row, k), b = 1 - 2*bit;
   2. scales ``uniform(0.005, 0.02)`` per (row, group) rounded to bf16 (RNE)
      -- or alpha_1 ``uniform(0.01, 0.03)``, alpha_{p+1} = alpha_p *
-     ``uniform(0.3, 0.6)`` per (row, group), each rounded to fp16 (RNE);
+     ``uniform(0.3, 0.6)`` per (row, group), each rounded to fp16 (RNE)
+     -- or, for the sa* storage, u8 scale codes a_1 ``integers(128, 256)``,
+     a_{p+1} = floor(a_p * ``uniform(0.3, 0.6)``) per (row, group), then
+     one fp16 d ``uniform(6e-5, 2e-4)`` per (row, 256-weight super-block);
   3. activations ``standard_normal`` (float32) rounded to bf16 (RNE);
   4. planted head rows, if asked for: M distinct rows, uniform in [0, N).
 
@@ -67,6 +70,23 @@ def binplane_weights(rng, N: int, K: int, P: int = 3, G: int = GROUP,
     return signs, f32_to_f16_bits(alpha)
 
 
+def sa_weights(rng, N: int, K: int, P: int = 3, G: int = GROUP, a1=(128, 256),
+               ratio=(0.3, 0.6), d_range=(6e-5, 2e-4)):
+    """signs int8 [P][N][K] in {-1,+1}; u8 scale codes [P][N][K/G]; fp16 bits
+    d [N][K/256].  Plane p+1's codes are plane p's times U(ratio), floored."""
+    assert K % 256 == 0 and 256 % G == 0
+    bits = rng.integers(0, 2, size=(P, N, K), dtype=np.int8)
+    signs = (1 - 2 * bits).astype(np.int8)
+    del bits
+    ng = K // G
+    codes = np.empty((P, N, ng), np.uint8)
+    codes[0] = rng.integers(a1[0], a1[1], size=(N, ng))
+    for p in range(1, P):
+        codes[p] = np.floor(codes[p - 1] * rng.uniform(ratio[0], ratio[1], size=(N, ng)))
+    d = f32_to_f16_bits(rng.uniform(d_range[0], d_range[1], size=(N, K // 256)).astype(np.float32))
+    return signs, codes, d
+
+
 def activations(rng, M: int, K: int) -> np.ndarray:
     """bf16 bits [M][K], x ~ N(0, 1)."""
     return f32_to_bf16_bits(rng.standard_normal(size=(M, K), dtype=np.float32))
@@ -112,7 +132,7 @@ def plant_rows_binplane(rng, signs: np.ndarray, alpha: np.ndarray, x: np.ndarray
 class Case:
     """One synthetic workload shape."""
     name: str
-    kind: str          # "w4a16" | "binplane" | "lmhead"
+    kind: str          # "w4a16" | "binplane" | "sa" | "lmhead"
     M: int
     N: int
     K: int
@@ -150,6 +170,13 @@ def make_binplane(case: Case, seed: int = 0):
     signs, alpha = binplane_weights(rng, case.N, case.K, case.P, case.G)
     x = activations(rng, case.M, case.K)
     return signs, alpha, x
+
+
+def make_sa(case: Case, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    signs, codes, d = sa_weights(rng, case.N, case.K, case.P, case.G)
+    x = activations(rng, case.M, case.K)
+    return signs, codes, d, x
 
 
 def make_lmhead(case: Case, seed: int = 0):

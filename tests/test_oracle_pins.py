@@ -160,6 +160,141 @@ def test_three_planes_reproduce_odd_int4_codes():
     assert np.allclose(ab, a4, rtol=1e-14, atol=0)
 
 
+# ---- sa* storage: u8 scale codes times one fp16 d per 256-weight super-block ----
+
+def sa_alpha_exact(codes, d, G):
+    """fp16 alpha[p][n][g] = d[n][g*G/256] * a[p][n][g], asserted exact in fp16
+    (the pins below pick d so that it is)."""
+    P, N, ng = codes.shape
+    dv = oracle.f16_values(d)
+    al = np.empty((P, N, ng), np.float64)
+    for g in range(ng):
+        al[:, :, g] = dv[None, :, (g * G) // 256] * codes[:, :, g].astype(np.float64)
+    bits = synth.f32_to_f16_bits(al.astype(np.float32))
+    assert np.array_equal(oracle.f16_values(bits), al)
+    return bits
+
+
+def exact_d(rng, N, K):
+    """fp16 d values 2^e * (1 + j/4): times any u8 code they stay exact in fp16."""
+    e = rng.integers(-14, -9, size=(N, K // 256))
+    j = rng.integers(0, 4, size=(N, K // 256))
+    return synth.f32_to_f16_bits((np.ldexp(1.0, e) * (1 + j / 4)).astype(np.float32))
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+def test_sa_equals_plane_layer_with_alpha_d_times_code(G):
+    rng = np.random.default_rng(20 + G)
+    M, N, K, P = 3, 11, 768, 4
+    signs, codes, _ = synth.sa_weights(rng, N, K, P, G)
+    codes[:, 0, 0] = 0  # a zero code drops its plane's group
+    codes[:, 1, :] = 255
+    d = exact_d(rng, N, K)
+    x = synth.activations(rng, M, K)
+    y, a = oracle.linear_sa(signs, codes, d, x, G=G)
+    yb, ab = oracle.linear_binplane(signs, sa_alpha_exact(codes, d, G), x, G=G)
+    assert np.array_equal(y, yb)
+    assert np.array_equal(a, ab)
+
+
+def test_sa_hand_worked_example():
+    signs = np.ones((2, 1, 512), np.int8)
+    signs[0, 0, [0, 200, 300]] = -1
+    signs[1, 0, [129, 511]] = -1
+    codes = np.array([[[1, 2, 3, 255, 4, 0, 9, 10]], [[16, 0, 128, 7, 1, 1, 1, 1]]], np.uint8)
+    d = np.array([[0x3C00, 0xC000]], np.uint16)  # fp16 1.0, -2.0
+    x = np.full((1, 512), BF16_ONE, np.uint16)
+    y, _ = oracle.linear_sa(signs, codes, d, x, G=64)
+    assert y[0, 0] == 22164.0
+    assert oracle.pack_sa(signs, codes, d, G=64).tobytes() == read_golden_bytes("sa_n1_k512_p2_g64.txt")
+
+
+def test_sa_three_planes_with_codes_4_2_1_reproduce_odd_int4():
+    # c = 4 b1 + 2 b2 + b3 for odd c, so codes (4, 2, 1) under d = s give s * c.
+    rng = np.random.default_rng(27)
+    M, N, K = 2, 13, 512
+    codes4 = (2 * rng.integers(-4, 4, size=(N, K)) + 1).astype(np.int8)
+    _, s_sb = synth.int4_weights(rng, N, K, G=256)      # one bf16 scale per super-block
+    scales = np.repeat(s_sb, 2, axis=1)                   # the same scale on both 128-groups
+    d = synth.f32_to_f16_bits(synth.bf16_bits_to_f32(s_sb))
+    assert np.array_equal(oracle.f16_values(d), oracle.bf16_values(s_sb))
+    sa_codes = np.empty((3, N, K // 128), np.uint8)
+    sa_codes[0], sa_codes[1], sa_codes[2] = 4, 2, 1
+    x = synth.activations(rng, M, K)
+    y4, a4 = oracle.linear_w4a16(codes4, scales, x)
+    ys, as_ = oracle.linear_sa(planes_from_odd_codes(codes4), sa_codes, d, x, G=128)
+    assert np.allclose(ys, y4, rtol=0, atol=1e-13 * a4.max())
+    assert np.allclose(as_, a4, rtol=1e-14, atol=0)
+
+
+def test_sa_group_size_reductions():
+    # Equal codes on the two halves of a group make G = 64 the G = 128 layer,
+    # and equal codes on a super-block's two groups make G = 128 the G = 256 one.
+    rng = np.random.default_rng(28)
+    M, N, K, P = 2, 9, 1024, 3
+    signs, c256, d = synth.sa_weights(rng, N, K, P, G=256)
+    x = synth.activations(rng, M, K)
+    y256, a256 = oracle.linear_sa(signs, c256, d, x, G=256)
+    c128 = np.repeat(c256, 2, axis=2)
+    y128, a128 = oracle.linear_sa(signs, c128, d, x, G=128)
+    y64, a64 = oracle.linear_sa(signs, np.repeat(c128, 2, axis=2), d, x, G=64)
+    for yy, aa in ((y128, a128), (y64, a64)):
+        assert np.allclose(yy, y256, rtol=0, atol=1e-13 * a256.max())
+        assert np.allclose(aa, a256, rtol=1e-13, atol=0)
+    # ... and different codes on the halves change the result
+    c64 = np.repeat(c128, 2, axis=2)
+    c64[0, :, 1] = c64[0, :, 1] // 2
+    y64b, _ = oracle.linear_sa(signs, c64, d, x, G=64)
+    assert not np.allclose(y64b, y256, rtol=0, atol=1e-6 * a256.max())
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+def test_sa_brute_force_dense_matmul(G):
+    rng = np.random.default_rng(30 + G)
+    M, N, K, P = 4, 7, 512, 5
+    signs, codes, d = synth.sa_weights(rng, N, K, P, G)
+    x = synth.activations(rng, M, K)
+    dv = ALL16.view(np.float16).astype(np.float64)[d]          # numpy's own fp16 decode
+    xv = x.astype(np.uint32) << 16
+    xv = xv.view(np.float32).astype(np.float64)
+    k = np.arange(K)
+    W = np.zeros((N, K))
+    for p in range(P):
+        W += dv[:, k // 256] * codes[p][:, k // G].astype(np.float64) * signs[p].astype(np.float64)
+    want = xv @ W.T
+    y, a = oracle.linear_sa(signs, codes, d, x, G=G)
+    assert np.allclose(y, want, rtol=0, atol=1e-12 * a.max())
+    assert np.allclose(a, np.abs(xv) @ np.abs(W).T, rtol=1e-12, atol=0)
+
+
+def test_sa_pack_places_every_code_and_d_in_its_own_slot():
+    N, K, P, G = 18, 512, 2, 64
+    signs = np.ones((P, N, K), np.int8)
+    sign_bytes = 32 * (K // 8) * P
+    codes = np.zeros((P, N, K // G), np.uint8)
+    d = np.zeros((N, K // 256), np.uint16)
+    assert not np.any(oracle.pack_sa(signs, codes, d, G=G))
+    seen = set()
+    for p in range(P):
+        for n in range(N):
+            for g in range(K // G):
+                c = codes.copy()
+                c[p, n, g] = 0xA5
+                nz = np.flatnonzero(oracle.pack_sa(signs, c, d, G=G))
+                assert len(nz) == 1 and nz[0] >= sign_bytes
+                seen.add(int(nz[0]))
+    for n in range(N):
+        for j in range(K // 256):
+            dd = d.copy()
+            dd[n, j] = 0x1234
+            blob = oracle.pack_sa(signs, codes, dd, G=G)
+            nz = np.flatnonzero(blob)
+            assert len(nz) == 2 and nz[1] == nz[0] + 1 and nz[0] % 2 == 0
+            assert blob[nz[0]] == 0x34 and blob[nz[1]] == 0x12
+            seen.add(int(nz[0]))
+    assert len(seen) == P * N * (K // G) + N * (K // 256)
+
+
 # ---- greedy argmax -----------------------------------------------------------
 
 def test_argmax_finds_planted_rows_with_closed_form_logit():
