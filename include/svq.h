@@ -10,6 +10,10 @@
  *   Binary planes: y[m][n] = sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] * x[m][k]
  *           b in {-1, +1}, alpha fp16, one scale per (plane, row, group).
  *           (ShiftAddQwen README, intro and "Method / Format".)
+ *   sa* storage of the same sum: alpha[p][n][g] = d[n][j] * a[p][n][g] with
+ *           a u8 scale code per (plane, row, group of G in {64, 128, 256})
+ *           and one fp16 d per (row, super-block j of 256 weights along k).
+ *           (ShiftAddQwen README, "Method / Format", the sa{2..6} types.)
  *   Greedy verify head: argmax over the W4A16 logits of a (possibly
  *           vocabulary-trimmed) head, lowest index on ties, optionally mapped
  *           through a row -> token-id table.  (DFlash summary sec. 4.1 and the
@@ -19,7 +23,8 @@
  * Conventions for every call:
  *   - bf16 and fp16 values travel as uint16_t bit patterns.
  *   - Shapes: W is [N][K] (row n = output feature), x/X is [M][K] row-major,
- *     y/Y is [M][N] row-major.  K % 128 == 0, G == 128.
+ *     y/Y is [M][N] row-major.  K % 128 == 0, G == 128 (sa calls: K % 256
+ *     == 0, G in {64, 128, 256}).
  *   - Return 0 (SVQ_OK) on success or a negative SVQ_ERR_* code.  On error
  *     nothing is written and svq_last_error() returns a message for the
  *     calling thread.  No C++ exception crosses this boundary.
@@ -55,6 +60,15 @@
  *     alphas: right after the signs, i.e. at byte N16 * K / 8 * P: fp16
  *       alpha[p][n][g] at entry (p*N16 + n)*KT4 + g.  Entries g >= KT and
  *       padding rows are 0.
+ *   sa blob with P planes and group G (K % 256 == 0):
+ *     signs: exactly the binary-plane blob's sign section.
+ *     codes: right after the signs (byte N16 * K / 8 * P): u8 a[p][n][g] at
+ *       byte (p*N16 + n)*CG + g, CG = KT4 * 128 / G (a row of codes spans
+ *       KT4 column tiles, so a wave's run of codes is one aligned load).
+ *       Entries g >= K/G and padding rows are 0.
+ *     d: right after the codes: fp16 d[n][j] (super-block j covers
+ *       k in [256j, 256j + 256)) at entry n*KS2 + j, KS2 = KT4 / 2.  Entries
+ *       j >= K/256 and padding rows are 0.
  */
 #ifndef SVQ_H
 #define SVQ_H
@@ -89,6 +103,10 @@ size_t svq_int4_packed_bytes(int64_t N, int64_t K, int32_t G);
 
 /* Bytes of a packed binary-plane blob: N16*K/8*P + P*N16*KT4*2.  0 for bad sizes. */
 size_t svq_binplane_packed_bytes(int64_t N, int64_t K, int32_t G, int32_t P);
+
+/* Bytes of a packed sa blob: N16*K/8*P + P*N16*CG + N16*KS2*2.  0 for bad
+ * sizes (K % 256, G not in {64, 128, 256}, P outside 2..6). */
+size_t svq_sa_packed_bytes(int64_t N, int64_t K, int32_t G, int32_t P);
 
 /* Workspace bytes that lmhead_argmax needs for M query rows. */
 size_t svq_lmhead_workspace_bytes(int32_t M);
@@ -130,6 +148,27 @@ int unpack_binary_planes(const uint8_t* packed, int64_t N, int64_t K, int32_t G,
                          int32_t P, int8_t* signs, uint16_t* alpha_f16);
 
 /*
+ * pack_sa -- HOST pointers, synchronous, CPU only.
+ * Stores P sign planes with their u8 scale codes and fp16 super-block scales
+ * in the sa blob layout above (ShiftAddQwen README, "Method / Format": the
+ * sa{P}[_128|_256] types keep, per super-block of 256 weights along the
+ * input dimension, the P sign planes, one u8 scale code per plane and group
+ * of G weights and one fp16 scale d, with alpha = d * a).
+ *   signs   [P][N][K] int8, each -1 or +1
+ *   codes   [P][N][K/G] uint8 scale codes a
+ *   d_f16   [N][K/256] fp16 bits
+ *   packed  svq_sa_packed_bytes(N, K, G, P) bytes, written in full
+ * Errors: NULL, SHAPE (P outside 2..6, N < 1, K % 256, G not in
+ * {64, 128, 256}), RANGE (a sign other than +-1).
+ */
+int pack_sa(const int8_t* signs, const uint8_t* codes, const uint16_t* d_f16,
+            int64_t N, int64_t K, int32_t G, int32_t P, uint8_t* packed);
+
+/* Inverse of pack_sa (HOST, for tests and inspection). */
+int unpack_sa(const uint8_t* packed, int64_t N, int64_t K, int32_t G, int32_t P,
+              int8_t* signs, uint8_t* codes, uint16_t* d_f16);
+
+/*
  * gemv_w4a16 -- DEVICE pointers, asynchronous on `stream`.
  * One decode step of a W4A16 linear layer (report sec. 2.1, 3.3):
  *   y[n] = bf16_rne( sum_g s[n][g] * sum_{k in g} c[n][k] * x[k] ),
@@ -169,6 +208,29 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
 int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                          int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,
                          void* stream);
+
+/*
+ * gemv_sa -- DEVICE pointers, asynchronous on `stream`.
+ * One decode step of an sa* layer (ShiftAddQwen README, "Method / Format"):
+ *   y[n] = bf16_rne( sum_j d[n][j] * sum_{g in j} sum_p a[p][n][g] * sum_{k in g} b[p][n][k] * x[k] ),
+ * j over the 256-weight super-blocks, accumulated in fp32 and scaled by d
+ * once per super-block.
+ *   packed  sa blob, 16-byte aligned; x [K] bf16, 16-byte aligned; y [N] bf16
+ * Errors: NULL, SHAPE (N < 1, K % 256, K > SVQ_MAX_K, G not in {64, 128, 256},
+ * P outside 2..6), ALIGN, HIP.
+ */
+int gemv_sa(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
+            int64_t K, int32_t G, int32_t P, void* stream);
+
+/*
+ * gemm_smallm_sa -- DEVICE pointers, asynchronous on `stream`.
+ * Y[m][n] = the sa* result for row m of X, M in 1..16 (the verify pass over
+ * a drafted block, as gemm_smallm_w4a16).  Errors: as gemv_sa, plus SHAPE
+ * for M outside 1..16.
+ */
+int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
+                   int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,
+                   void* stream);
 
 /*
  * lmhead_argmax -- DEVICE pointers, asynchronous on `stream`.

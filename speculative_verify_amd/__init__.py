@@ -8,8 +8,9 @@ raises -- there is no fallback path.
 
 Functions (same names as the C ABI):
   pack_int4_grouped, unpack_int4_grouped, pack_binary_planes,
-  unpack_binary_planes                       host numpy arrays
-  gemv_w4a16, gemv_binplane, gemm_smallm_w4a16, gemm_smallm_binplane,
+  unpack_binary_planes, pack_sa, unpack_sa   host numpy arrays
+  gemv_w4a16, gemv_binplane, gemv_sa, gemm_smallm_w4a16,
+  gemm_smallm_binplane, gemm_smallm_sa,
   lmhead_argmax, lmhead_argmax_binplane, lmhead_verify_greedy, verify_greedy,
   svq_stream_read                            torch CUDA tensors
 """
@@ -22,9 +23,9 @@ import numpy as np
 
 __all__ = [
     "SvqError", "lib_path", "load", "int4_packed_bytes", "binplane_packed_bytes",
-    "lmhead_workspace_bytes", "pack_int4_grouped", "unpack_int4_grouped",
-    "pack_binary_planes", "unpack_binary_planes", "gemv_w4a16", "gemv_binplane",
-    "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_argmax_binplane",
+    "sa_packed_bytes", "lmhead_workspace_bytes", "pack_int4_grouped", "unpack_int4_grouped",
+    "pack_binary_planes", "unpack_binary_planes", "pack_sa", "unpack_sa", "gemv_w4a16",
+    "gemv_binplane", "gemv_sa", "gemm_smallm_w4a16", "gemm_smallm_binplane", "gemm_smallm_sa", "lmhead_argmax", "lmhead_argmax_binplane",
     "lmhead_verify_greedy",
     "verify_greedy", "svq_stream_read",
 ]
@@ -61,12 +62,17 @@ def load():
         "svq_last_error": ([], ctypes.c_char_p),
         "svq_int4_packed_bytes": ([I64, I64, I32], SZ),
         "svq_binplane_packed_bytes": ([I64, I64, I32, I32], SZ),
+        "svq_sa_packed_bytes": ([I64, I64, I32, I32], SZ),
         "svq_lmhead_workspace_bytes": ([I32], SZ),
         "pack_int4_grouped": ([V, V, I64, I64, I32, V], ctypes.c_int),
         "unpack_int4_grouped": ([V, I64, I64, I32, V, V], ctypes.c_int),
         "pack_binary_planes": ([V, V, I64, I64, I32, I32, V], ctypes.c_int),
         "unpack_binary_planes": ([V, I64, I64, I32, I32, V, V], ctypes.c_int),
+        "pack_sa": ([V, V, V, I64, I64, I32, I32, V], ctypes.c_int),
+        "unpack_sa": ([V, I64, I64, I32, I32, V, V, V], ctypes.c_int),
         "gemv_w4a16": ([V, V, V, I64, I64, I32, V], ctypes.c_int),
+        "gemv_sa": ([V, V, V, I64, I64, I32, I32, V], ctypes.c_int),
+        "gemm_smallm_sa": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
         "gemv_binplane": ([V, V, V, I64, I64, I32, I32, V], ctypes.c_int),
         "gemm_smallm_w4a16": ([V, V, V, I32, I64, I64, I32, V], ctypes.c_int),
         "gemm_smallm_binplane": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
@@ -121,6 +127,10 @@ def binplane_packed_bytes(N: int, K: int, P: int, G: int = GROUP) -> int:
     return int(load().svq_binplane_packed_bytes(N, K, G, P))
 
 
+def sa_packed_bytes(N: int, K: int, P: int, G: int = GROUP) -> int:
+    return int(load().svq_sa_packed_bytes(N, K, G, P))
+
+
 def lmhead_workspace_bytes(M: int) -> int:
     return int(load().svq_lmhead_workspace_bytes(M))
 
@@ -164,6 +174,25 @@ def unpack_binary_planes(packed: np.ndarray, N: int, K: int, P: int, G: int = GR
     return signs, alpha
 
 
+def pack_sa(signs: np.ndarray, codes: np.ndarray, d_f16: np.ndarray, G: int = GROUP) -> np.ndarray:
+    signs = np.ascontiguousarray(signs, np.int8)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    d = np.ascontiguousarray(d_f16, np.uint16)
+    P, N, K = signs.shape
+    out = np.empty(max(sa_packed_bytes(N, K, P, G), 1), np.uint8)
+    _check("pack_sa", load().pack_sa(_np_ptr(signs), _np_ptr(codes), _np_ptr(d), N, K, G, P, _np_ptr(out)))
+    return out
+
+
+def unpack_sa(packed: np.ndarray, N: int, K: int, P: int, G: int = GROUP):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    signs = np.empty((P, N, K), np.int8)
+    codes = np.empty((P, N, K // G), np.uint8)
+    d = np.empty((N, K // 256), np.uint16)
+    _check("unpack_sa", load().unpack_sa(_np_ptr(packed), N, K, G, P, _np_ptr(signs), _np_ptr(codes), _np_ptr(d)))
+    return signs, codes, d
+
+
 # ---- device calls (torch tensors; bf16/fp16 values as int16/uint16 bits or bf16) --
 
 def gemv_w4a16(packed, x, y, N: int, K: int, G: int = GROUP, stream=None) -> None:
@@ -184,6 +213,15 @@ def gemm_smallm_binplane(packed, X, Y, M: int, N: int, K: int, P: int, G: int = 
     _check("gemm_smallm_binplane",
            load().gemm_smallm_binplane(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, P,
                                        _stream(stream)))
+
+
+def gemv_sa(packed, x, y, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
+    _check("gemv_sa", load().gemv_sa(_dev_ptr(packed), _dev_ptr(x), _dev_ptr(y), N, K, G, P, _stream(stream)))
+
+
+def gemm_smallm_sa(packed, X, Y, M: int, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
+    _check("gemm_smallm_sa",
+           load().gemm_smallm_sa(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, P, _stream(stream)))
 
 
 def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace,

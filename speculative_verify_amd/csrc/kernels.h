@@ -1,12 +1,16 @@
 // kernels.h -- gfx950 (CDNA4) device code behind the entry points of svq.h:
 // helpers, tile loaders and the kernel templates, instantiated by the
-// translation units that launch them (svq_int4.hip, svq_planes.hip).
+// translation units that launch them (svq_int4.hip, svq_planes_*.hip,
+// svq_sa_*.hip).
 //
 // What is computed (see svq.h for the full statements and citations):
 //   W4A16         y = sum_g s[n][g] * sum_{k in g} c[n][k] x[k]
 //                 (Efficient Qwen Competition report, sec. 2.1 and 3.3)
 //   binary planes y = sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] x[k]
 //                 (ShiftAddQwen README, intro and "Method / Format")
+//   sa* storage   the same with alpha[p][n][g] = d[n][j] * a[p][n][g]: u8 codes
+//                 a, one fp16 d per 256-weight super-block j (same page,
+//                 "Method / Format")
 //   greedy head   argmax over W4A16 logits, lowest index on ties
 //                 (DFlash summary sec. 4.1; small-vocabulary MTP study sec. 3.3)
 //
@@ -363,6 +367,84 @@ __device__ __forceinline__ void load_sign_tile(SignSlot<GPW, P>& sl, const BlobV
   }
 }
 
+// sa* tiles.  The sign dwords are the plane blob's; a lane also reads, per
+// plane, the run of u8 codes of its row over the wave's GPW column tiles
+// (2, 1 or 1/2 codes per column tile for G = 64, 128, 256) and the fp16 d of
+// the one or two super-blocks those tiles cover, each run with one load.
+template <int GPW, int G>
+constexpr int sa_code_bytes() { return GPW * 128 / G > 0 ? GPW * 128 / G : 1; }
+
+template <int GPW, int P, int G>
+struct SaSlot {
+  uint32_t w[GPW][P];                                // sign dword of each (column tile, plane)
+  uint32_t a[P][(sa_code_bytes<GPW, G>() + 3) / 4];  // raw code bytes of (plane, row r, the wave's groups)
+  uint32_t d;                                        // raw fp16 d of the wave's super-blocks
+
+  // Code of plane p for column tile gi, 32-wide k block t.  The wave's first
+  // column tile g0 is a multiple of GPW, so its super-blocks and groups start
+  // at the run's first byte.
+  __device__ __forceinline__ uint32_t code(int p, int gi, int t) const {
+    const int ci = G == 64 ? 2 * gi + (t >> 1) : G == 128 ? gi : gi >> 1;
+    return (a[p][ci >> 2] >> (8 * (ci & 3))) & 0xFFu;
+  }
+  // d of the super-block holding column tile gi.
+  __device__ __forceinline__ float dscale(int gi) const {
+    return f16_to_f32((uint16_t)(d >> (16 * (gi >> 1))));
+  }
+};
+
+template <int BYTES>
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* v) {
+  if constexpr (BYTES == 8) {
+    const v2u_t t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else if constexpr (BYTES == 4) {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (BYTES == 2) {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+  }
+}
+
+struct SaView {
+  __amdgpu_buffer_rsrc_t w, a, d;
+  int KT, KT4, NT;
+};
+
+template <int G>
+__device__ __forceinline__ SaView sa_view(const uint8_t* blob, int KT, int NT, int P) {
+  SaView v;
+  v.KT = KT;
+  v.KT4 = (KT + 3) & ~3;
+  v.NT = NT;
+  const uint32_t wbytes = (uint32_t)NT * (uint32_t)KT * 256u * (uint32_t)P;
+  const uint32_t abytes = (uint32_t)P * (uint32_t)NT * 16u * (uint32_t)(v.KT4 * 128 / G);
+  v.w = make_rsrc(blob, wbytes);
+  v.a = make_rsrc(blob + wbytes, abytes);
+  v.d = make_rsrc(blob + wbytes + abytes, (uint32_t)NT * 16u * (uint32_t)(v.KT4 / 2) * 2u);
+  return v;
+}
+
+template <int GPW, int P, int G>
+__device__ __forceinline__ void load_sa_tile(SaSlot<GPW, P, G>& sl, const SaView& b, int rt, bool live, int g0,
+                                             int lane, int r) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = g0 + gi;
+    const uint32_t off = ((uint32_t)(rt * b.KT + g) * 256u * P + 4u * lane) | oob_bit(live && g < b.KT);
+#pragma unroll
+    for (int p = 0; p < P; ++p) sl.w[gi][p] = ld_stream4(b.w, off + 256u * p);
+  }
+  const int N16 = b.NT * 16, CG = b.KT4 * 128 / G, row = 16 * rt + r;
+  const uint32_t oob = oob_bit(live && g0 < b.KT4);
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    load_run<sa_code_bytes<GPW, G>()>(b.a, ((uint32_t)((p * N16 + row) * CG + g0 * 128 / G)) | oob, sl.a[p]);
+  load_run<GPW >= 4 ? 4 : 2>(b.d, ((uint32_t)(row * (b.KT4 / 2) + g0 / 2) * 2u) | oob, &sl.d);
+}
+
 // Number of row tiles this workgroup owns in the grid-stride order.
 __device__ __forceinline__ int tiles_of_wg(int NT) { return (NT - 1 - (int)blockIdx.x) / (int)gridDim.x + 1; }
 
@@ -404,6 +486,46 @@ __device__ __forceinline__ float binplane_tile_partial(const SignSlot<GPW, P>& s
       for (int ip = 0; ip < 16; ++ip) acc = dot2(sign_pair(sl.w[gi][p], ip, one), xp[gi][ip], acc);
       part = fmaf(sl.a[p].f16(gi), acc, part);
     }
+  return part;
+}
+
+// bf16 pair (a, a) of a u8 scale code; exact, since a <= 255 has at most
+// eight significant bits.
+__device__ __forceinline__ uint32_t code_pair(uint32_t a) {
+  const uint32_t h = __float_as_uint((float)a) >> 16;
+  return h | (h << 16);
+}
+
+// bf16 pair (a * b_even, a * b_odd) for pair ip = 4t + i of a sign dword: the
+// +-1 decode with the code pair in place of (1, 1).
+__device__ __forceinline__ uint32_t scaled_sign_pair(uint32_t w, int ip, uint32_t mask, uint32_t apair) {
+  return ((w << (15 - ip)) & mask) | apair;
+}
+
+// sa* lane partial with the weights decoded to a * b pairs: every plane and
+// group of a super-block adds exact products a * b * x into one fp32 sum,
+// which the super-block's d scales once.
+template <int GPW, int P, int G>
+__device__ __forceinline__ float sa_tile_partial(const SaSlot<GPW, P, G>& sl, const uint32_t (&xp)[GPW][16],
+                                                 const PairDecode& one) {
+  constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
+  float part = 0.f;
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb) {
+    float acc = 0.f;
+#pragma unroll
+    for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t ap = code_pair(sl.code(p, gi, t));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc = dot2(scaled_sign_pair(sl.w[gi][p], 4 * t + i, one.mask, ap), xp[gi][4 * t + i], acc);
+        }
+    part = fmaf(sl.dscale(2 * sb), acc, part);
+  }
   return part;
 }
 
@@ -695,29 +817,188 @@ __device__ __forceinline__ float binplane_tile_partial_lut(const SignSlot<GPW, P
   return part;
 }
 
+// sa* counterpart: per plane the two halves of a column tile (k blocks 0-1
+// and 2-3) are summed apart, so that at G = 64 each takes its own code; the
+// codes weight the table sums and d scales each super-block once.
+template <int GPW, int P, int G>
+__device__ __forceinline__ float sa_tile_partial_lut(const SaSlot<GPW, P, G>& sl, const SignLut<GPW>* luts,
+                                                     uint32_t lane_off) {
+  const char* base = reinterpret_cast<const char*>(luts);
+  constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
+  float part = 0.f;
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb) {
+    float acc = 0.f;
+#pragma unroll
+    for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint32_t w = sl.w[gi][p];
+        float h[2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int par = 0; par < 2; ++par) {
+            const uint32_t off = (nibble_offset(w, 16 * par + 4 * t) | lane_off) + ((gi * 4 + t) * 2 + par) * 256;
+            const float v = *reinterpret_cast<const float*>(base + off);
+            h[t >> 1] = ((t & 1) == 0 && par == 0) ? v : h[t >> 1] + v;
+          }
+        if constexpr (G == 64) {
+          acc = fmaf((float)sl.code(p, gi, 0), h[0], acc);
+          acc = fmaf((float)sl.code(p, gi, 2), h[1], acc);
+        } else {
+          acc = fmaf((float)sl.code(p, gi, 0), h[0] + h[1], acc);
+        }
+      }
+    part = fmaf(sl.dscale(2 * sb), acc, part);
+  }
+  return part;
+}
+
+// ---------------------------------------------------------------------------
+// Sign-plane storages.  Both share the sign section and the two kernels
+// below; a format names its tile registers (Slot), its buffer views, the
+// loads of one tile and the tile's arithmetic: the M = 1 lane partial (from
+// the nibble tables or from decoded pairs) and the M <= 16 MFMA tile.
+
+// fp16 alpha per (plane, row, group of 128).
+template <int P_>
+struct PlaneFmt {
+  static constexpr int P = P_;
+  template <int GPW>
+  using Slot = SignSlot<GPW, P>;
+  using View = BlobView;
+
+  static __device__ __forceinline__ View view(const uint8_t* blob, int KT, int NT) {
+    return sign_view(blob, KT, NT, P);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ void load(Slot<GPW>& sl, const View& b, int rt, bool live, int g0, int lane,
+                                              int r) {
+    load_sign_tile<GPW, P>(sl, b, rt, live, g0, lane, r);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ float partial_lut(const Slot<GPW>& sl, const SignLut<GPW>* luts,
+                                                      uint32_t lane_off) {
+    return binplane_tile_partial_lut<GPW, P>(sl, luts, lane_off);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ float partial(const Slot<GPW>& sl, const uint32_t (&xp)[GPW][16],
+                                                  const PairDecode& one) {
+    return binplane_tile_partial<GPW, P>(sl, xp, one);
+  }
+  // One accumulator chain per (column tile, plane), scaled by its alpha.
+  template <int GPW>
+  static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
+                                               const PairDecode& one) {
+    float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint32_t wp = sl.w[gi][p];
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, one), sign_pair(wp, 4 * t + 1, one),
+                                  sign_pair(wp, 4 * t + 2, one), sign_pair(wp, 4 * t + 3, one)};
+          c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+        }
+        const float a = sl.a[p].f16(gi);
+        yv.x = fmaf(a, c[0], yv.x);
+        yv.y = fmaf(a, c[1], yv.y);
+        yv.z = fmaf(a, c[2], yv.z);
+        yv.w = fmaf(a, c[3], yv.w);
+      }
+    return yv;
+  }
+};
+
+// sa*: u8 codes per (plane, row, group of G) and one fp16 d per (row,
+// super-block).  In the MFMA tile, B holds a * b exactly, so all planes and
+// groups of a super-block accumulate in one chain that d scales once.
+template <int P_, int G>
+struct SaFmt {
+  static constexpr int P = P_;
+  template <int GPW>
+  using Slot = SaSlot<GPW, P, G>;
+  using View = SaView;
+
+  static __device__ __forceinline__ View view(const uint8_t* blob, int KT, int NT) {
+    return sa_view<G>(blob, KT, NT, P);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ void load(Slot<GPW>& sl, const View& b, int rt, bool live, int g0, int lane,
+                                              int r) {
+    load_sa_tile<GPW, P, G>(sl, b, rt, live, g0, lane, r);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ float partial_lut(const Slot<GPW>& sl, const SignLut<GPW>* luts,
+                                                      uint32_t lane_off) {
+    return sa_tile_partial_lut<GPW, P, G>(sl, luts, lane_off);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ float partial(const Slot<GPW>& sl, const uint32_t (&xp)[GPW][16],
+                                                  const PairDecode& one) {
+    return sa_tile_partial<GPW, P, G>(sl, xp, one);
+  }
+  template <int GPW>
+  static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
+                                               const PairDecode& one) {
+    constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
+    float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const uint32_t wp = sl.w[gi][p];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t ap = code_pair(sl.code(p, gi, t));
+            const uint32_t bq[4] = {scaled_sign_pair(wp, 4 * t + 0, one.mask, ap),
+                                    scaled_sign_pair(wp, 4 * t + 1, one.mask, ap),
+                                    scaled_sign_pair(wp, 4 * t + 2, one.mask, ap),
+                                    scaled_sign_pair(wp, 4 * t + 3, one.mask, ap)};
+            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+          }
+        }
+      const float d = sl.dscale(2 * sb);
+      yv.x = fmaf(d, c[0], yv.x);
+      yv.y = fmaf(d, c[1], yv.y);
+      yv.z = fmaf(d, c[2], yv.z);
+      yv.w = fmaf(d, c[3], yv.w);
+    }
+    return yv;
+  }
+};
+
 // Chunk length of the table kernel: the tables (8 KiB per wave at four groups)
 // plus the chunk staging must leave room for two workgroups per CU.
 constexpr int kChunkGemvLut = 14;
 
-// gemv_binplane / sign-plane head (M = 1).  ARGMAX selects the epilogue.
-template <int GPW, int MAXW, int D, int P, bool ARGMAX>
+// Sign-plane mat-vec and head (M = 1) for storage format F.  ARGMAX selects
+// the epilogue.
+template <class F, int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
-    k_gemv_binplane(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ xw, uint16_t* __restrict__ y,
+    k_gemv_planes(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ xw, uint16_t* __restrict__ y,
                     uint8_t* __restrict__ ws, HeadOut ho, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
-  const BlobView bv = sign_view(blob, KT, NT, P);
+  const typename F::View bv = F::view(blob, KT, NT);
   const int T = tiles_of_wg(NT);
 
   uint32_t xo[GPW];
   load_x_own<GPW>(xw, g0, KT, q, r, xo);
   // The activation loads go out first: the first tile's work waits on them.
   __builtin_amdgcn_sched_barrier(0);
-  SignSlot<GPW, P> ring[D];
+  typename F::template Slot<GPW> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    load_sign_tile<GPW, P>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    F::template load<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
     // Issue each slot's loads in the same order the loop refills them.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -747,13 +1028,13 @@ __global__ void __launch_bounds__(64 * MAXW)
       const int i = i0 + j;
       float part;
       if constexpr (kLut)
-        part = sum_over_q(binplane_tile_partial_lut<GPW, P>(ring[j], luts, lut_off));
+        part = sum_over_q(F::template partial_lut<GPW>(ring[j], luts, lut_off));
       else
-        part = sum_over_q(binplane_tile_partial<GPW, P>(ring[j], xp, one));
+        part = sum_over_q(F::template partial<GPW>(ring[j], xp, one));
       stage.put(i, i < T, wave, lane, part);
       // Slot j is refilled only after its last use, so it keeps its registers.
       __builtin_amdgcn_sched_barrier(0);
-      load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
       const int ci = i % C;
       if (i < T && (ci == C - 1 || i == T - 1)) {
         __syncthreads();
@@ -943,24 +1224,25 @@ __global__ void __launch_bounds__(64 * MAXW)
     gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
 
-template <int GPW, int MAXW, int D, int P, bool ARGMAX>
+// Sign-plane verify mat-mul and head (M <= 16) for storage format F.
+template <class F, int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
-    k_gemm_binplane(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
+    k_gemm_planes(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
                     uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
-  const BlobView bv = sign_view(blob, KT, NT, P);
+  const typename F::View bv = F::view(blob, KT, NT);
   const int T = tiles_of_wg(NT);
 
   uint32_t xa[GPW][16];
   load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
   // The activation loads go out first: the first tile's work waits on them.
   __builtin_amdgcn_sched_barrier(0);
-  SignSlot<GPW, P> ring[D];
+  typename F::template Slot<GPW> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    load_sign_tile<GPW, P>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    F::template load<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
     // Issue each slot's loads in the same order the loop refills them.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -982,29 +1264,11 @@ __global__ void __launch_bounds__(64 * MAXW)
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const uint32_t wp = ring[j].w[gi][p];
-          f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, one), sign_pair(wp, 4 * t + 1, one),
-                                    sign_pair(wp, 4 * t + 2, one), sign_pair(wp, 4 * t + 3, one)};
-            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
-          }
-          const float a = ring[j].a[p].f16(gi);
-          yv.x = fmaf(a, c[0], yv.x);
-          yv.y = fmaf(a, c[1], yv.y);
-          yv.z = fmaf(a, c[2], yv.z);
-          yv.w = fmaf(a, c[3], yv.w);
-        }
+      const float4 yv = F::template mma<GPW>(ring[j], xa, one);
       stage.put(i, i < T, wave, lane, yv);
       // Slot j is refilled only after its last use, so it keeps its registers.
       __builtin_amdgcn_sched_barrier(0);
-      load_sign_tile<GPW, P>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
       const int ci = i % C;
       if (i < T && (ci == C - 1 || i == T - 1)) {
         __syncthreads();

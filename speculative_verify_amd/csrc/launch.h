@@ -117,18 +117,20 @@ template <int V>
 using ic = std::integral_constant<int, V>;
 
 // Calls launch(ic<GPW>, ic<MAXW>, ic<D>) for the shape's compile-time
-// parameters.  Depths above 2 are instantiated only for the 8-wave shapes.
-template <class L>
+// parameters.  Depths above 2 are instantiated only for the 8-wave shapes,
+// and none above MAXD (a shallower ring is launched instead).
+template <int MAXD = 6, class L>
 void dispatch(const Shape& sh, L&& launch) {
   auto depth = [&](auto G, auto W, auto DM) {
-    if constexpr (decltype(DM)::value >= 6)
+    constexpr int dm = decltype(DM)::value < MAXD ? decltype(DM)::value : MAXD;
+    if constexpr (dm >= 6)
       if (sh.depth >= 6) return launch(G, W, ic<6>{});
-    if constexpr (decltype(DM)::value >= 5)
-      if (sh.depth == 5) return launch(G, W, ic<5>{});
-    if constexpr (decltype(DM)::value >= 4)
-      if (sh.depth == 4) return launch(G, W, ic<4>{});
-    if constexpr (decltype(DM)::value >= 3)
-      if (sh.depth == 3) return launch(G, W, ic<3>{});
+    if constexpr (dm >= 5)
+      if (sh.depth >= 5) return launch(G, W, ic<5>{});
+    if constexpr (dm >= 4)
+      if (sh.depth >= 4) return launch(G, W, ic<4>{});
+    if constexpr (dm >= 3)
+      if (sh.depth >= 3) return launch(G, W, ic<3>{});
     if (sh.depth >= 2) return launch(G, W, ic<2>{});
     launch(G, W, ic<1>{});
   };
@@ -154,18 +156,40 @@ void dispatch_p(int P, L&& launch) {
   }
 }
 
+// Calls launch(ic<G>) for a group size of the sa* storage (64, 128 or 256).
+template <class L>
+void dispatch_group(int G, L&& launch) {
+  switch (G) {
+    case 64: launch(ic<64>{}); break;
+    case 128: launch(ic<128>{}); break;
+    default: launch(ic<256>{}); break;
+  }
+}
+
 #define SVQ_KARGS(G, W, D) decltype(G)::value, decltype(W)::value, decltype(D)::value
 
 // Deepest ring the sign-plane kernels keep in registers without spilling:
 // a slot holds P sign dwords and P scale runs per group.
-template <int P>
-constexpr int max_depth_planes() { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
-#define SVQ_KARGS_P(G, W, D, Pc)                                                                        \
-  decltype(G)::value, decltype(W)::value,                                                              \
-      (decltype(D)::value < max_depth_planes<decltype(Pc)::value>() ? decltype(D)::value               \
-                                                                    : max_depth_planes<decltype(Pc)::value>()), \
-      decltype(Pc)::value
+constexpr int max_depth_planes(int P) { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
+// Template arguments of the sign-plane kernels for format F.
+#define SVQ_KARGS_F(F, G, W, D)                                                                     \
+  F, decltype(G)::value, decltype(W)::value,                                                       \
+      (decltype(D)::value < max_depth_planes(F::P) ? decltype(D)::value : max_depth_planes(F::P))
 
+// The sa* kernels keep rings of at most three tiles (the plane kernels'
+// measured best; deeper rings are not instantiated for them).
+constexpr int kMaxDepthSa = 3;
+
+// Argument checks of the sa* entry points; the rest as check_linear.
+inline int check_sa(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N,
+                    int64_t K, int32_t G, int32_t P) {
+  svq::clear_error();
+  if (G != 64 && G != 128 && G != 256)
+    return svq::fail(SVQ_ERR_SHAPE, "%s: group size must be 64, 128 or 256 (got %d)", fn, G);
+  if (K % 256) return svq::fail(SVQ_ERR_SHAPE, "%s: K=%lld must be a multiple of 256", fn, (long long)K);
+  if (P < 2 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "%s: P=%d must be in 2..6", fn, P);
+  return check_linear(fn, packed, x, y, M, N, K, SVQ_GROUP, P);
+}
 
 // Argument checks shared by the head entry points (P = 0: INT4 weights;
 // P >= 1: P sign planes).

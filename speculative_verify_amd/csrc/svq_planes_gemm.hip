@@ -24,8 +24,9 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch_p(P, [&](auto Pc) {
+    using F = PlaneFmt<decltype(Pc)::value>;
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
+      hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid),
                          dim3(64 * sh.waves), 0, st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N,
                          sh.KT, sh.NT);
     });
@@ -49,8 +50,9 @@ int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, 
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   dispatch_p(P, [&](auto Pc) {
+    using F = PlaneFmt<decltype(Pc)::value>;
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemm_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+      hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
                          st, packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
     });
   });

@@ -24,8 +24,9 @@ int launch_binplane_head_m1(const char* fn, const uint8_t* packed, const uint16_
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const HeadOut ho{row_ids, argmax, maxlogit, nullptr, nullptr};
   dispatch_p(P, [&](auto Pc) {
+    using F = PlaneFmt<decltype(Pc)::value>;
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+      hipLaunchKernelGGL((k_gemv_planes<SVQ_KARGS_F(F, G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
                          st, packed, xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
     });
   });
@@ -45,8 +46,9 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
   dispatch_p(P, [&](auto Pc) {
+    using F = PlaneFmt<decltype(Pc)::value>;
     dispatch(sh, [&](auto G, auto W, auto D) {
-      hipLaunchKernelGGL((k_gemv_binplane<SVQ_KARGS_P(G, W, D, Pc), false>), dim3(sh.grid),
+      hipLaunchKernelGGL((k_gemv_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid),
                          dim3(64 * sh.waves), 0, st, packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N,
                          sh.KT, sh.NT);
     });

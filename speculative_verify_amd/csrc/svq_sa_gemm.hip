@@ -1,0 +1,37 @@
+// svq_sa_gemm.hip -- small-M device entry point for the sa* storage of sign
+// planes (ShiftAddQwen README, "Method / Format"): the verify mat-mul over a
+// drafted block of M <= 16 rows, on 16x16x32 bf16 MFMA with B = a * b exact.
+//   Y = X W^T with W[n][k] = d[n][k/256] * sum_p a[p][n][k/G] * b[p][n][k]
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "launch.h"
+#include "svq.h"
+#include "svq_internal.h"
+
+extern "C" {
+
+int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
+                   int32_t G, int32_t P, void* stream) {
+  if (int rc = check_sa("gemm_smallm_sa", packed, X, Y, M, N, K, G, P)) return rc;
+  Shape sh;
+  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  dispatch_group(G, [&](auto Gc) {
+    dispatch_p(P, [&](auto Pc) {
+      if constexpr (decltype(Pc)::value >= 2) {
+        using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
+        dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
+          hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+                             st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
+        });
+      }
+    });
+  });
+  return launched("gemm_smallm_sa");
+}
+
+}  // extern "C"

@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["pack_int4_grouped", "pack_binary_planes", "gemv_w4a16", "gemv_binplane",
                  "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_verify_greedy",
-                 "verify_greedy", "svq_last_error"]:
+                 "verify_greedy", "svq_last_error", "pack_sa", "gemv_sa", "gemm_smallm_sa"]:
         assert want in names
 
 
@@ -38,6 +38,10 @@ def test_sizes():
     assert svq.int4_packed_bytes(248320, 4096) == 508559360 + 15892480
     assert svq.int4_packed_bytes(32768, 4096) == 69206016 - 2097152 + 2097152  # 67108864 + 2097152
     assert svq.lmhead_workspace_bytes(16) >= 16 * 8 and svq.lmhead_workspace_bytes(17) == 0
+    # sa at P = 3: signs + 3 code bytes per (row, 128 weights) + one fp16 d per (row, 256 weights)
+    assert svq.sa_packed_bytes(12288, 4096, 3, 128) == 18874368 + 3 * 12288 * 32 + 12288 * 16 * 2
+    assert svq.sa_packed_bytes(12288, 4096, 3, 64) == 18874368 + 3 * 12288 * 64 + 12288 * 16 * 2
+    assert svq.sa_packed_bytes(12288, 4096, 3, 256) == 18874368 + 3 * 12288 * 16 + 12288 * 16 * 2
 
 
 A = 0x100000  # an aligned address that is never dereferenced: validation fails first
@@ -72,6 +76,16 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.lmhead_argmax_binplane(A, A, 2, 16, 128, 128, 0, None, A, A, A, 1 << 20, None), -2),
     (lambda l: l.lmhead_argmax_binplane(A, A, 2, 16, 128, 128, 7, None, A, A, A, 1 << 20, None), -2),
     (lambda l: l.lmhead_argmax_binplane(A, A, 2, 16, 128, 128, 3, None, A, A, None, 0, None), -5),
+    (lambda l: l.gemv_sa(None, A, A, 16, 256, 128, 3, None), -1),
+    (lambda l: l.gemv_sa(A, A, A, 16, 384, 128, 3, None), -2),
+    (lambda l: l.gemv_sa(A, A, A, 16, 256, 32, 3, None), -2),
+    (lambda l: l.gemv_sa(A, A, A, 16, 256, 128, 1, None), -2),
+    (lambda l: l.gemv_sa(A, A, A, 16, 256, 128, 7, None), -2),
+    (lambda l: l.gemv_sa(A, A, A, 16, 256 * 33, 128, 3, None), -2),
+    (lambda l: l.gemv_sa(A + 8, A, A, 16, 256, 128, 3, None), -3),
+    (lambda l: l.gemm_smallm_sa(A, A, A, 17, 16, 256, 64, 2, None), -2),
+    (lambda l: l.gemm_smallm_sa(A, A, A, 4, 16, 256, 512, 2, None), -2),
+    (lambda l: l.gemm_smallm_sa(A, A + 2, A, 4, 16, 256, 256, 2, None), -3),
     (lambda l: l.svq_stream_read(A, 100, A, 0, None), -2),
     (lambda l: l.svq_stream_read(A, 1024, A, 9, None), -2),
 ])

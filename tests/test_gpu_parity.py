@@ -85,6 +85,25 @@ def run_gemm_binplane(signs, alpha, X):
     return bf16_host(Y)
 
 
+def run_gemv_sa(signs, codes, d, x, G):
+    P, N, K = signs.shape
+    blob = dev(svq.pack_sa(signs, codes, d, G=G))
+    y = torch.empty(N, dtype=torch.int16, device="cuda")
+    svq.gemv_sa(blob, dev(x), y, N, K, P, G=G)
+    torch.cuda.synchronize()
+    return bf16_host(y)
+
+
+def run_gemm_sa(signs, codes, d, X, G):
+    P, N, K = signs.shape
+    M = X.shape[0]
+    blob = dev(svq.pack_sa(signs, codes, d, G=G))
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    svq.gemm_smallm_sa(blob, dev(X), Y, M, N, K, P, G=G)
+    torch.cuda.synchronize()
+    return bf16_host(Y)
+
+
 def run_lmhead(codes, scales, X, row_ids=None, blob=None):
     N, K = codes.shape
     M = X.shape[0]
@@ -269,6 +288,113 @@ def test_gemm_onehot_unit_scale_is_exact():
 
 
 # ---------------------------------------------------------------------------
+# sa* storage (u8 scale codes per plane and group, fp16 d per super-block)
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+def test_gemv_sa_decode_shape(G):
+    case = synth.Case(f"decode_sa_p3_g{G}", "sa", 1, 12288, 4096, P=3, G=G)
+    signs, codes, d, x = synth.make_sa(case, 0)
+    y, a = oracle.linear_sa(signs, codes, d, x, G=G)
+    print(f"gemv_sa {case.name}", flush=True)
+    check_close(run_gemv_sa(signs, codes, d, x, G), y[0], a[0], case.name)
+
+
+@pytest.mark.parametrize("N,K,P,G", [(1, 256, 2, 64), (23, 512, 3, 128), (300, 768, 4, 256), (129, 1024, 5, 64),
+                                     (77, 2048, 6, 128), (1500, 4096, 3, 256), (45, 6144, 3, 64),
+                                     (33, 8192, 2, 128), (64, 4352, 6, 256)])
+def test_gemv_sa_ragged(N, K, P, G):
+    rng = np.random.default_rng(N + K + P + G)
+    signs, codes, d = synth.sa_weights(rng, N, K, P, G)
+    x = synth.activations(rng, 1, K)
+    y, a = oracle.linear_sa(signs, codes, d, x, G=G)
+    check_close(run_gemv_sa(signs, codes, d, x, G), y[0], a[0], f"N={N} K={K} P={P} G={G}")
+
+
+@pytest.mark.parametrize("N,G", [(4096, 128), (12288, 128), (4096, 64), (4096, 256)])
+def test_gemm_sa_verify_shapes(N, G):
+    case = synth.Case(f"verify_sa_p3_m16_n{N}_g{G}", "sa", 16, N, 4096, P=3, G=G)
+    signs, codes, d, X = synth.make_sa(case, 0)
+    Y, A = oracle.linear_sa(signs, codes, d, X, G=G)
+    print(f"gemm_smallm_sa {case.name}", flush=True)
+    check_close(run_gemm_sa(signs, codes, d, X, G), Y, A, case.name)
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_gemm_sa_m_sweep_and_rows_match_gemv(M):
+    G = (64, 128, 256)[M % 3]
+    P = 2 + M % 5
+    rng = np.random.default_rng(200 + M)
+    N, K = 150, 768
+    signs, codes, d = synth.sa_weights(rng, N, K, P, G)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_sa(signs, codes, d, X, G=G)
+    Yg = run_gemm_sa(signs, codes, d, X, G)
+    check_close(Yg, Y, A, f"gemm sa M={M} P={P} G={G}")
+    y0 = run_gemv_sa(signs, codes, d, X[:1], G)
+    check_close(y0, Y[0], A[0], f"gemv sa row 0 P={P} G={G}")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(16, 200, 8192, 64), (7, 96, 6144, 128), (16, 33, 4352, 256)])
+def test_gemm_sa_wide_k(M, N, K, G):
+    rng = np.random.default_rng(M + N + K + G)
+    signs, codes, d = synth.sa_weights(rng, N, K, 3, G)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_sa(signs, codes, d, X, G=G)
+    check_close(run_gemm_sa(signs, codes, d, X, G), Y, A, f"gemm sa M={M} N={N} K={K} G={G}")
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+def test_sa_onehot_with_unit_d_is_exact(G):
+    # d = 1 and codes <= 40 over three planes: y = sum_p a_p b_p is an integer of
+    # magnitude <= 120, exact in bf16, for x = e_k at every k of two super-blocks
+    # (mat-vec), and for 16 different k per launch (mat-mul).
+    N, K, P = 40, 512, 3
+    rng = np.random.default_rng(11 + G)
+    signs, _, _ = synth.sa_weights(rng, N, K, P, G)
+    codes = rng.integers(0, 41, size=(P, N, K // G)).astype(np.uint8)
+    d = np.full((N, K // 256), 0x3C00, np.uint16)
+    blob = dev(svq.pack_sa(signs, codes, d, G=G))
+    k = np.arange(K)
+    want = sum(codes[p][:, k // G].astype(np.int64) * signs[p].astype(np.int64) for p in range(P))
+    y = torch.empty(N, dtype=torch.int16, device="cuda")
+    for kk in range(K):
+        x = np.zeros((1, K), np.uint16)
+        x[0, kk] = 0x3F80
+        svq.gemv_sa(blob, dev(x), y, N, K, P, G=G)
+        assert np.array_equal(bf16_host(y), want[:, kk].astype(np.float64)), kk
+    M = 16
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    for base in range(0, K, M):
+        ks = [(base + 7 * m) % K for m in range(M)]
+        X = np.zeros((M, K), np.uint16)
+        X[np.arange(M), ks] = 0x3F80
+        svq.gemm_smallm_sa(blob, dev(X), Y, M, N, K, P, G=G)
+        assert np.array_equal(bf16_host(Y), want[:, ks].T.astype(np.float64)), base
+
+
+def test_sa_codes_4_2_1_match_int4_on_odd_codes():
+    # With codes (4, 2, 1) and d = the super-block's INT4 scale, the three sign
+    # planes of an odd code c carry s * c: both sa kernels meet the bound
+    # against the W4A16 oracle.
+    rng = np.random.default_rng(12)
+    N, K = 300, 1024
+    codes4 = (2 * rng.integers(-4, 4, size=(N, K)) + 1).astype(np.int8)
+    _, s_sb = synth.int4_weights(rng, N, K, G=256)
+    scales = np.repeat(s_sb, 2, axis=1)
+    d = synth.f32_to_f16_bits(synth.bf16_bits_to_f32(s_sb))
+    c = codes4.astype(np.int64)
+    b1 = np.where(c > 0, 1, -1)
+    b2 = np.where(c - 4 * b1 > 0, 1, -1)
+    signs = np.stack([b1, b2, c - 4 * b1 - 2 * b2]).astype(np.int8)
+    sa_codes = np.empty((3, N, K // 64), np.uint8)
+    sa_codes[0], sa_codes[1], sa_codes[2] = 4, 2, 1
+    X = synth.activations(rng, 16, K)
+    Y, A = oracle.linear_w4a16(codes4, scales, X)
+    check_close(run_gemv_sa(signs, sa_codes, d, X[:1], 64), Y[0], A[0], "sa gemv")
+    check_close(run_gemm_sa(signs, sa_codes, d, X, 64), Y, A, "sa gemm")
+
+
+# ---------------------------------------------------------------------------
 # Output rounding and accumulation quality
 
 def bf16_rne_candidates(v: np.ndarray, slack: np.ndarray):
@@ -284,7 +410,8 @@ def bf16_rne_candidates(v: np.ndarray, slack: np.ndarray):
     return pick, lo, hi, either
 
 
-@pytest.mark.parametrize("kind", ["w4a16_gemv", "w4a16_gemm", "binplane_gemv", "binplane_gemm"])
+@pytest.mark.parametrize("kind", ["w4a16_gemv", "w4a16_gemm", "binplane_gemv", "binplane_gemm", "sa_gemv",
+                                  "sa_gemm"])
 def test_sign_coherent_outputs_are_correctly_rounded(kind):
     # x > 0 and every weight positive: |y| = sum |w x|.  The result must be the
     # bf16 round-to-nearest-even of the exact sum (either neighbour only when the
@@ -299,12 +426,18 @@ def test_sign_coherent_outputs_are_correctly_rounded(kind):
         Y, A = oracle.linear_w4a16(codes, scales, X)
         got = run_gemv_w4a16(codes, scales, X[:1])[None] if kind.endswith("gemv") else \
             run_gemm_w4a16(codes, scales, X)
-    else:
+    elif kind.startswith("binplane"):
         signs = np.ones((3, N, K), np.int8)
         _, alpha = synth.binplane_weights(rng, N, K, P=3)
         Y, A = oracle.linear_binplane(signs, alpha, X)
         got = run_gemv_binplane(signs, alpha, X[:1])[None] if kind.endswith("gemv") else \
             run_gemm_binplane(signs, alpha, X)
+    else:
+        _, codes, d = synth.sa_weights(rng, N, K, 3, 64)
+        signs = np.ones((3, N, K), np.int8)
+        Y, A = oracle.linear_sa(signs, codes, d, X, G=64)
+        got = run_gemv_sa(signs, codes, d, X[:1], 64)[None] if kind.endswith("gemv") else \
+            run_gemm_sa(signs, codes, d, X, 64)
     Y = Y[: got.shape[0]]
     pick, lo, hi, either = bf16_rne_candidates(Y, 4e-5 * Y)
     ok = (got == pick) | (either & ((got == lo) | (got == hi)))

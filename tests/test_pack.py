@@ -32,6 +32,36 @@ def test_binplane_pack_bit_exact_vs_oracle(N, K, P):
     assert np.array_equal(s2, signs) and np.array_equal(a2, alpha)
 
 
+@pytest.mark.parametrize("N,K,P,G", [(1, 256, 2, 64), (16, 256, 3, 128), (19, 512, 2, 256), (33, 768, 6, 64),
+                                     (40, 1024, 5, 128), (17, 512, 4, 256), (64, 256, 3, 64)])
+def test_sa_pack_bit_exact_vs_oracle(N, K, P, G):
+    rng = np.random.default_rng(N * 1000 + K + P + G)
+    signs, codes, d = synth.sa_weights(rng, N, K, P, G)
+    blob = svq.pack_sa(signs, codes, d, G=G)
+    assert blob.nbytes == svq.sa_packed_bytes(N, K, P, G)
+    assert np.array_equal(blob, oracle.pack_sa(signs, codes, d, G=G))
+    s2, c2, d2 = svq.unpack_sa(blob, N, K, P, G=G)
+    assert np.array_equal(s2, signs) and np.array_equal(c2, codes) and np.array_equal(d2, d)
+
+
+def test_sa_pack_rejects_bad_arguments():
+    lib = svq.load()
+    buf = np.zeros(1 << 16, np.uint8)
+    s = np.ones((2, 1, 512), np.int8)
+    c = np.zeros((2, 1, 8), np.uint8)
+    d = np.zeros((1, 2), np.uint16)
+    assert lib.pack_sa(s.ctypes.data, c.ctypes.data, d.ctypes.data, 1, 384, 128, 2, buf.ctypes.data) == -2
+    assert lib.pack_sa(s.ctypes.data, c.ctypes.data, d.ctypes.data, 1, 512, 32, 2, buf.ctypes.data) == -2
+    assert lib.pack_sa(s.ctypes.data, c.ctypes.data, d.ctypes.data, 1, 512, 64, 1, buf.ctypes.data) == -2
+    assert lib.pack_sa(s.ctypes.data, c.ctypes.data, d.ctypes.data, 1, 512, 64, 7, buf.ctypes.data) == -2
+    assert lib.pack_sa(s.ctypes.data, None, d.ctypes.data, 1, 512, 64, 2, buf.ctypes.data) == -1
+    s[1, 0, 300] = 2
+    with pytest.raises(svq.SvqError) as e:
+        svq.pack_sa(s, c, d, G=64)
+    assert e.value.code == -4 and "p=1, n=0, k=300" in str(e.value)
+    assert svq.sa_packed_bytes(1, 384, 2, 128) == 0 and svq.sa_packed_bytes(1, 512, 1, 128) == 0
+
+
 def test_golden_blobs():
     codes = ((np.arange(128) % 16) - 8).astype(np.int8)[None, :]
     blob = svq.pack_int4_grouped(codes, np.array([[0x3F80]], np.uint16))
@@ -41,6 +71,12 @@ def test_golden_blobs():
     signs[1, 0, 64] = -1
     blob = svq.pack_binary_planes(signs, np.array([[[0x3C00]], [[0x3800]]], np.uint16))
     assert blob.tobytes() == read_golden_bytes("binplane_n1_k128_p2.txt")
+    signs = np.ones((2, 1, 512), np.int8)
+    signs[0, 0, [0, 200, 300]] = -1
+    signs[1, 0, [129, 511]] = -1
+    codes = np.array([[[1, 2, 3, 255, 4, 0, 9, 10]], [[16, 0, 128, 7, 1, 1, 1, 1]]], np.uint8)
+    blob = svq.pack_sa(signs, codes, np.array([[0x3C00, 0xC000]], np.uint16), G=64)
+    assert blob.tobytes() == read_golden_bytes("sa_n1_k512_p2_g64.txt")
 
 
 def test_every_code_value_at_every_tile_position_round_trips():
