@@ -17,6 +17,11 @@ activations + outputs, the algorithmic bytes of each call) over the whole
 step.  Each step reads ~1.3 GB of distinct weights, far more than the 256 MB
 last-level cache, so every call streams its weights from HBM.
 
+Also timed, each call on its own but outside the step (so the step and its
+`value` keep their definition): the sa* storage of sign planes (u8 scale
+codes per plane and group, one fp16 d per 256-weight super-block) for
+decode and verify, P=3, groups of 64 and 128.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one
 GPU's share.
 """
@@ -44,6 +49,12 @@ def alg_bytes_linear(kind: str, M: int, N: int, P: int = 0) -> int:
     else:
         w = N * K // 8 * P + P * N * (K // G) * 2
     return w + M * K * 2 + M * N * 2
+
+
+def alg_bytes_sa(M: int, N: int, P: int, Gs: int) -> int:
+    """sa* call: sign planes + one code byte per (plane, row, group) + fp16 d
+    per (row, 256 weights) + X in + Y out."""
+    return N * K // 8 * P + P * N * (K // Gs) + N * (K // 256) * 2 + M * K * 2 + M * N * 2
 
 
 def alg_bytes_head(M: int, N: int) -> int:
@@ -126,6 +137,33 @@ def build_step(svq, synth, torch):
     head(1, 32768)
     head(16, 248320, verify=True)  # the verify step: full vocabulary, greedy acceptance fused
     head(16, 32768)                # a block drafter on the trimmed head
+    return calls
+
+
+def build_extra(svq, synth, torch):
+    """The sa* calls, in build_step's format (timed alone, not in the step)."""
+    calls = []
+    seed = [500]
+
+    def sa(M, N, P, Gs):
+        def make():
+            seed[0] += 1
+            blob = synth.device_sa_blob(N, K, P, Gs, seed[0])
+            seed[0] += 1
+            X = synth.device_activations(M, K, seed[0]).view(torch.int16)
+            Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+            if M == 1:
+                return lambda: svq.gemv_sa(blob, X, Y, N, K, P, G=Gs)
+            return lambda: svq.gemm_smallm_sa(blob, X, Y, M, N, K, P, G=Gs)
+
+        name = (f"gemv_sa_p{P}_g{Gs}_m1_n{N}" if M == 1 else f"gemm_smallm_sa_p{P}_g{Gs}_m{M}_n{N}")
+        calls.append((name, alg_bytes_sa(M, N, P, Gs), make(), make))
+
+    sa(1, 12288, 3, 128)
+    sa(16, 4096, 3, 128)
+    sa(16, 12288, 3, 128)
+    sa(1, 12288, 3, 64)
+    sa(16, 12288, 3, 64)
     return calls
 
 
@@ -249,6 +287,7 @@ def main():
     torch.cuda.set_device(0)
     svq.load()
     calls = build_step(svq, synth, torch)
+    extra = build_extra(svq, synth, torch)
     step_bytes = sum(c[1] for c in calls)
     torch.cuda.synchronize()
 
@@ -277,7 +316,7 @@ def main():
     # cache, so every launch streams its weights from HBM (the method of the
     # streaming-read ceiling below).
     kernels = {}
-    for name, nbytes, fn, fresh in calls:
+    for name, nbytes, fn, fresh in calls + extra:
         copies = max(2, -(-2 * LLC_BYTES // nbytes))
         rot = [fn] + [fresh() for _ in range(copies - 1)]
         for f in rot[:3]:
@@ -294,7 +333,10 @@ def main():
         gbps = nbytes / (us * 1e-6) / 1e9
         kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(gbps, 1),
                          "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "input_copies": copies}
-    dom = max(kernels, key=lambda n: kernels[n]["us"])
+    extra_names = {c[0] for c in extra}
+    for name in extra_names:
+        kernels[name]["in_step"] = False
+    dom = max((n for n in kernels if n not in extra_names), key=lambda n: kernels[n]["us"])
     dom_us, dom_bytes = kernels[dom]["us"], kernels[dom]["bytes"]
     dom_gbps = kernels[dom]["GBps"]
 
@@ -341,6 +383,8 @@ def main():
             "w4a16_n12288": ratio("gemm_smallm_w4a16_m16_n12288", "gemv_w4a16_m1_n12288"),
             "binplane_n12288": ratio("gemm_smallm_binplane_p3_m16_n12288", "gemv_binplane_p3_m1_n12288"),
             "lmhead_n248320": ratio("lmhead_verify_greedy_m16_n248320", "lmhead_argmax_m1_n248320"),
+            "sa_p3_g128_n12288": ratio("gemm_smallm_sa_p3_g128_m16_n12288", "gemv_sa_p3_g128_m1_n12288"),
+            "sa_p3_g64_n12288": ratio("gemm_smallm_sa_p3_g64_m16_n12288", "gemv_sa_p3_g64_m1_n12288"),
         },
     }
     traffic = load_traffic(dom)
@@ -349,7 +393,7 @@ def main():
     if not args.no_ceiling:
         # The same-size cold streaming read: what a pure read of each call's
         # bytes achieves with this launch overhead and start-up latency.
-        for name, nbytes, _, _ in calls:
+        for name, nbytes, _, _ in calls + extra:
             ceil = stream_read_ceiling(svq, torch, nbytes)
             kernels[name]["ceiling_GBps"] = round(ceil, 1)
             kernels[name]["frac_of_ceiling"] = round(kernels[name]["GBps"] / ceil, 4)

@@ -237,6 +237,30 @@ def device_binplane_blob(N: int, K: int, P: int, seed: int, G: int = GROUP, a1=(
     return blob
 
 
+def device_sa_blob(N: int, K: int, P: int, G: int, seed: int, a1=(128, 256), ratio=(0.3, 0.6),
+                   d_range=(6e-5, 2e-4), device: str = "cuda"):
+    """A packed sa blob drawn on the device, with the distributions of
+    sa_weights: Bernoulli(0.5) sign bits, u8 codes a_1 ~ U{a1}, a_{p+1} =
+    floor(a_p * U(ratio)), fp16 d ~ U(d_range).  N % 16 == 0 and K/128 a
+    multiple of 4, so the code and d rows carry no padding."""
+    assert N % 16 == 0 and K % 512 == 0 and 256 % G == 0
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    sign_bytes = N * K // 8 * P
+    ng, ns = K // G, K // 256
+    blob = torch.empty(sign_bytes + P * N * ng + N * ns * 2, dtype=torch.uint8, device=device)
+    blob[:sign_bytes] = torch.randint(0, 256, (sign_bytes,), generator=gen, dtype=torch.uint8, device=device)
+    a = torch.empty((P, N * ng), dtype=torch.float32, device=device)
+    a[0] = torch.randint(a1[0], a1[1], (N * ng,), generator=gen, device=device).float()
+    for p in range(1, P):
+        u = torch.empty(N * ng, device=device).uniform_(ratio[0], ratio[1], generator=gen)
+        a[p] = torch.floor(a[p - 1] * u)
+    blob[sign_bytes:sign_bytes + P * N * ng] = a.to(torch.uint8).reshape(-1)
+    d = torch.empty(N * ns, dtype=torch.float32, device=device).uniform_(d_range[0], d_range[1], generator=gen)
+    blob[sign_bytes + P * N * ng:] = d.to(torch.float16).view(torch.uint8)
+    return blob
+
+
 def device_activations(M: int, K: int, seed: int, device: str = "cuda"):
     """bf16 activations x ~ N(0, 1), [M][K], drawn on the device."""
     gen = torch.Generator(device=device)
