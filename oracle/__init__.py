@@ -16,6 +16,10 @@ activations) and returns fp64 results:
 * ``linear_sa``       the same sum with alpha[p,n,g] = d[n, g*G/256] * a[p,n,g]:
   u8 scale codes per (plane, group) and one fp16 d per 256-weight
   super-block (ShiftAddQwen README, "Method / Format", the sa* types);
+* ``requant_int4``, ``fit_planes``, ``snap_sa``: the offline steps --
+  frozen-grid INT4 requantisation (report sec. 2.1), the greedy + ALS
+  sign-plane fit (README "Output-aware fit") and the snap of plane scales
+  onto the sa* u8 grid (README "Format", "Scale distillation");
 * ``argmax_w4a16``    greedy token = lowest index attaining the max logit
   (DFlash summary sec. 4.1; MTP study sec. 3.3 for the trimmed-head row map);
 * ``pack_int4`` / ``pack_binplane`` / ``pack_sa`` state the packed byte layouts element by
@@ -77,6 +81,14 @@ def _load():
     lib.oracle_sa_blob_bytes.restype = I64
     lib.oracle_pack_sa.argtypes = [P, P, P, I64, I64, I64, I64, P]
     lib.oracle_pack_sa.restype = ctypes.c_int
+    lib.oracle_f16_bits.argtypes = [ctypes.c_double]
+    lib.oracle_f16_bits.restype = ctypes.c_uint16
+    lib.oracle_requant_int4.argtypes = [P, P, I64, I64, I64, P]
+    lib.oracle_requant_int4.restype = ctypes.c_int
+    lib.oracle_fit_planes.argtypes = [P, I64, I64, I64, I64, I64, P, P, P]
+    lib.oracle_fit_planes.restype = ctypes.c_int
+    lib.oracle_snap_sa.argtypes = [P, I64, I64, I64, I64, P, P]
+    lib.oracle_snap_sa.restype = ctypes.c_int
     lib.oracle_argmax_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.oracle_argmax_w4a16.restype = ctypes.c_int
     lib.oracle_argmax_binplane.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]
@@ -274,3 +286,50 @@ def pack_sa(signs, codes, d, G: int = 128) -> np.ndarray:
     if rc:
         raise ValueError(f"oracle_pack_sa rc={rc}")
     return blob
+
+
+def f16_bits(values) -> np.ndarray:
+    """IEEE binary16 bits of fp64 values, round to nearest even."""
+    lib = _load()
+    v = np.atleast_1d(np.asarray(values, np.float64))
+    return np.array([lib.oracle_f16_bits(float(x)) for x in v.ravel()], np.uint16).reshape(v.shape)
+
+
+def requant_int4(w, scales, G: int = 128) -> np.ndarray:
+    """INT4 codes [N][K] of bf16 weights w under frozen bf16 scales [N][K/G]."""
+    w = _c(w, np.uint16)
+    scales = _c(scales, np.uint16)
+    N, K = w.shape
+    assert scales.shape == (N, K // G)
+    codes = np.empty((N, K), np.int8)
+    rc = _load().oracle_requant_int4(_ptr(w), _ptr(scales), N, K, G, _ptr(codes))
+    if rc:
+        raise ValueError(f"oracle_requant_int4 rc={rc}")
+    return codes
+
+
+def fit_planes(w, P: int, G: int = 128, iters: int = 10):
+    """(signs [P][N][K], alpha fp64 [P][N][K/G], alpha fp16 bits) fitted to
+    bf16 weights w [N][K]: greedy init, then `iters` ALS rounds."""
+    w = _c(w, np.uint16)
+    N, K = w.shape
+    signs = np.empty((P, N, K), np.int8)
+    a64 = np.empty((P, N, K // G), np.float64)
+    a16 = np.empty((P, N, K // G), np.uint16)
+    rc = _load().oracle_fit_planes(_ptr(w), N, K, G, P, iters, _ptr(signs), _ptr(a64), _ptr(a16))
+    if rc:
+        raise ValueError(f"oracle_fit_planes rc={rc}")
+    return signs, a64, a16
+
+
+def snap_sa(alpha16, G: int = 128):
+    """(codes u8 [P][N][K/G], d fp16 bits [N][K/256]) for fp16 plane scales."""
+    alpha16 = _c(alpha16, np.uint16)
+    P, N, ng = alpha16.shape
+    K = ng * G
+    codes = np.empty((P, N, ng), np.uint8)
+    d = np.empty((N, K // 256), np.uint16)
+    rc = _load().oracle_snap_sa(_ptr(alpha16), N, K, G, P, _ptr(codes), _ptr(d))
+    if rc:
+        raise ValueError(f"oracle_snap_sa rc={rc}")
+    return codes, d

@@ -21,6 +21,11 @@
  *    sign plane has one unsigned 8-bit scale code a per group of G in
  *    {64, 128, 256} weights, and the super-block has one fp16 scale d; the
  *    plane's scale for that group is alpha = d * a.
+ *  - The same pages for the offline steps: the report's sec. 2.1 rounds the
+ *    updated weights back onto the frozen INT4 grid at packing time; the
+ *    README's "Output-aware fit" fits the planes by greedy initialisation
+ *    and alternating least squares with exhaustive code choice, and its
+ *    "Scale distillation" snaps the scales onto the u8 grid.
  *  - DFlash summary, sec. 4.1 and the tech report sec. 2.2: the target
  *    verifies a drafted block in one parallel pass, and greedy (temperature 0)
  *    decoding takes the argmax of the target's logits.
@@ -445,6 +450,235 @@ int oracle_pack_sa(const int8_t* signs, const uint8_t* codes, const uint16_t* d,
       const uint16_t v = d[n * ns + j];
       blob[doff + 2 * (n * KS2 + j)] = (uint8_t)(v & 0xff);
       blob[doff + 2 * (n * KS2 + j) + 1] = (uint8_t)(v >> 8);
+    }
+  return 0;
+}
+
+/* ---- host quantizers ------------------------------------------------------ */
+
+/* fp64 -> IEEE binary16 bits, round to nearest, ties to even (overflow to
+ * infinity, gradual underflow to subnormals), from the format's definition. */
+uint16_t oracle_f16_bits(double v) {
+  uint16_t sign = 0;
+  if (signbit(v)) {
+    sign = 0x8000;
+    v = -v;
+  }
+  if (isnan(v)) return (uint16_t)(sign | 0x7e00);
+  if (v >= 65520.0) return (uint16_t)(sign | 0x7c00); /* >= max + half an ulp */
+  /* quantum of the binade holding v (subnormal quantum 2^-24) */
+  int e;
+  frexp(v, &e);             /* v = m * 2^e, m in [0.5, 1) */
+  int q = e - 11;           /* 11 significant bits: quantum 2^(e-11) */
+  if (q < -24) q = -24;
+  double units = ldexp(v, -q); /* exact: a power-of-two scaling */
+  double fl = floor(units), rem = units - fl;
+  double n = fl;
+  if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) n = fl + 1.0;
+  double r = ldexp(n, q);   /* rounded value */
+  if (r >= 65520.0) return (uint16_t)(sign | 0x7c00);
+  if (r == 0.0) return sign;
+  int re;
+  frexp(r, &re);
+  int exp_field = re - 1 + 15; /* r = 1.f * 2^(re-1) */
+  if (exp_field <= 0)           /* subnormal: r = f * 2^-24 */
+    return (uint16_t)(sign | (uint16_t)ldexp(r, 24));
+  uint16_t frac = (uint16_t)(ldexp(r, -(re - 1)) * 1024.0 - 1024.0);
+  return (uint16_t)(sign | (uint16_t)(exp_field << 10) | frac);
+}
+
+/* Round half to even of an fp64 value to an integer-valued fp64. */
+static double rne(double v) {
+  double fl = floor(v), rem = v - fl;
+  if (rem > 0.5) return fl + 1.0;
+  if (rem < 0.5) return fl;
+  return fmod(fl, 2.0) == 0.0 ? fl : fl + 1.0;
+}
+
+/*
+ * Frozen-grid requantisation (tech report sec. 2.1): at packing time the
+ * updated bf16 weights are rounded back onto the original grid, i.e. the
+ * code of w under its frozen group scale s is the nearest grid point:
+ *   c[n][k] = clamp(rne(w[n][k] / s[n][g(k)]), -8, 7);  s == 0 gives c = 0.
+ * w [N][K] and s [N][K/G] are bf16 bits; the quotient is taken in fp64,
+ * where an exact half-way case stays exact.
+ */
+int oracle_requant_int4(const uint16_t* w, const uint16_t* s, int64_t N,
+                        int64_t K, int64_t G, int8_t* codes) {
+  if (N < 1 || K < 1 || G < 1 || K % G) return -1;
+  const int64_t ng = K / G;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const double sv = oracle_bf16_value(s[n * ng + k / G]);
+      double c = 0.0;
+      if (sv != 0.0) {
+        c = rne(oracle_bf16_value(w[n * K + k]) / sv);
+        if (c < -8.0) c = -8.0;
+        if (c > 7.0) c = 7.0;
+      }
+      codes[n * K + k] = (int8_t)c;
+    }
+  return 0;
+}
+
+/* sum_p alpha_p b_p for the sign vector of candidate c (bit p of c set means
+ * b_p = -1), summed in plane order. */
+static double candidate_value(const double* alpha, int64_t P, int64_t c) {
+  double v = 0.0;
+  for (int64_t p = 0; p < P; ++p) v += ((c >> p) & 1) ? -alpha[p] : alpha[p];
+  return v;
+}
+
+/* Least-squares plane scales for fixed signs: solve (B B^T) a = B w by
+ * Cholesky.  Returns 0, or -1 when B B^T is singular (a plane equal to or the
+ * negation of a combination of the others over the group), leaving a alone. */
+static int ls_scales(const double* w, const int8_t* b, int64_t P, int64_t G,
+                     double* a) {
+  double A[36], r[6], L[36];
+  for (int64_t p = 0; p < P; ++p) {
+    r[p] = 0.0;
+    for (int64_t k = 0; k < G; ++k) r[p] += (double)b[p * G + k] * w[k];
+    for (int64_t q = 0; q < P; ++q) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < G; ++k) acc += (double)(b[p * G + k] * b[q * G + k]);
+      A[p * P + q] = acc;
+    }
+  }
+  for (int64_t i = 0; i < P; ++i)
+    for (int64_t j = 0; j <= i; ++j) {
+      double acc = A[i * P + j];
+      for (int64_t t = 0; t < j; ++t) acc -= L[i * P + t] * L[j * P + t];
+      if (i == j) {
+        if (acc <= 1e-9 * (double)G) return -1;
+        L[i * P + i] = sqrt(acc);
+      } else {
+        L[i * P + j] = acc / L[j * P + j];
+      }
+    }
+  double y[6];
+  for (int64_t i = 0; i < P; ++i) {
+    double acc = r[i];
+    for (int64_t t = 0; t < i; ++t) acc -= L[i * P + t] * y[t];
+    y[i] = acc / L[i * P + i];
+  }
+  for (int64_t i = P - 1; i >= 0; --i) {
+    double acc = y[i];
+    for (int64_t t = i + 1; t < P; ++t) acc -= L[t * P + i] * a[t];
+    a[i] = acc / L[i * P + i];
+  }
+  return 0;
+}
+
+/*
+ * Binary-coding fit of one group (ShiftAddQwen README, "Output-aware fit":
+ * greedy initialisation, then alternating least squares with exhaustive code
+ * choice; here on the plain weight error, without the Hessian weighting):
+ *   greedy:  r = w; for p = 1..P: b_p = sign(r) (sign(0) = +1),
+ *            alpha_p = mean_k |r_k|, r -= alpha_p b_p
+ *   a round: every weight takes the sign vector whose sum_p alpha_p b_p is
+ *            nearest to it (lowest candidate index on ties), then alpha is
+ *            re-solved by least squares for those signs (kept when the
+ *            system is singular)
+ * After `iters` rounds every plane with alpha_p < 0 is flipped (alpha_p and
+ * b_p negated, the same weights).  w has G values; b is [P][G]; a is [P].
+ */
+static void fit_group(const double* w, int64_t G, int64_t P, int64_t iters,
+                      int8_t* b, double* a) {
+  double r[256];
+  for (int64_t k = 0; k < G; ++k) r[k] = w[k];
+  for (int64_t p = 0; p < P; ++p) {
+    double m = 0.0;
+    for (int64_t k = 0; k < G; ++k) {
+      b[p * G + k] = r[k] < 0.0 ? -1 : 1;
+      m += fabs(r[k]);
+    }
+    a[p] = m / (double)G;
+    for (int64_t k = 0; k < G; ++k) r[k] -= a[p] * (double)b[p * G + k];
+  }
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t nc = (int64_t)1 << P;
+    for (int64_t k = 0; k < G; ++k) {
+      int64_t best = 0;
+      double bd = fabs(w[k] - candidate_value(a, P, 0));
+      for (int64_t c = 1; c < nc; ++c) {
+        const double dd = fabs(w[k] - candidate_value(a, P, c));
+        if (dd < bd) {
+          bd = dd;
+          best = c;
+        }
+      }
+      for (int64_t p = 0; p < P; ++p) b[p * G + k] = ((best >> p) & 1) ? -1 : 1;
+    }
+    ls_scales(w, b, P, G, a);
+  }
+  for (int64_t p = 0; p < P; ++p)
+    if (a[p] < 0.0) {
+      a[p] = -a[p];
+      for (int64_t k = 0; k < G; ++k) b[p * G + k] = (int8_t)-b[p * G + k];
+    }
+}
+
+/*
+ * The fit for every (row, group) of bf16 weights w [N][K]:
+ * signs [P][N][K], alpha [P][N][K/G] as fp64 (alpha64, unrounded) and as
+ * fp16 bits (round to nearest even).  G <= 256, 1 <= P <= 6.
+ */
+int oracle_fit_planes(const uint16_t* w, int64_t N, int64_t K, int64_t G,
+                      int64_t P, int64_t iters, int8_t* signs, double* alpha64,
+                      uint16_t* alpha16) {
+  if (N < 1 || K < 1 || G < 1 || G > 256 || K % G || P < 1 || P > 6 || iters < 0) return -1;
+  const int64_t ng = K / G;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    double wv[256], a[6];
+    int8_t b[6 * 256];
+    for (int64_t g = 0; g < ng; ++g) {
+      for (int64_t k = 0; k < G; ++k) wv[k] = oracle_bf16_value(w[n * K + g * G + k]);
+      fit_group(wv, G, P, iters, b, a);
+      for (int64_t p = 0; p < P; ++p) {
+        alpha64[(p * N + n) * ng + g] = a[p];
+        alpha16[(p * N + n) * ng + g] = oracle_f16_bits(a[p]);
+        for (int64_t k = 0; k < G; ++k) signs[(p * N + n) * K + g * G + k] = b[p * G + k];
+      }
+    }
+  }
+  return 0;
+}
+
+/*
+ * Snap fp16 plane scales onto the sa* grid (ShiftAddQwen README, "Format":
+ * alpha = d * a with u8 codes a and one fp16 d per 256-weight super-block;
+ * "Scale distillation": scales end snapped to the u8 grid).  Per (row,
+ * super-block j): m = the largest alpha over its planes and groups,
+ * d = fp16(m / 255), and a = min(rne(alpha / d), 255) (a = 0 when
+ * d == 0).  Negative alphas are not representable and are rejected (-2).
+ * alpha [P][N][K/G] fp16 bits -> codes [P][N][K/G], d [N][K/256].
+ */
+int oracle_snap_sa(const uint16_t* alpha, int64_t N, int64_t K, int64_t G,
+                   int64_t P, uint8_t* codes, uint16_t* d) {
+  if (N < 1 || K < 256 || K % 256 || G < 1 || 256 % G || P < 1) return -1;
+  const int64_t ng = K / G, ns = K / 256, gps = 256 / G;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < ns; ++j) {
+      double m = 0.0;
+      for (int64_t p = 0; p < P; ++p)
+        for (int64_t g = j * gps; g < (j + 1) * gps; ++g) {
+          const double v = oracle_f16_value(alpha[(p * N + n) * ng + g]);
+          if (v < 0.0) return -2;
+          if (v > m) m = v;
+        }
+      const uint16_t db = oracle_f16_bits(m / 255.0);
+      const double dv = oracle_f16_value(db);
+      d[n * ns + j] = db;
+      for (int64_t p = 0; p < P; ++p)
+        for (int64_t g = j * gps; g < (j + 1) * gps; ++g) {
+          double c = 0.0;
+          if (dv > 0.0) {
+            c = rne(oracle_f16_value(alpha[(p * N + n) * ng + g]) / dv);
+            if (c > 255.0) c = 255.0;
+          }
+          codes[(p * N + n) * ng + g] = (uint8_t)c;
+        }
     }
   return 0;
 }

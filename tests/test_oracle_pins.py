@@ -295,6 +295,186 @@ def test_sa_pack_places_every_code_and_d_in_its_own_slot():
     assert len(seen) == P * N * (K // G) + N * (K // 256)
 
 
+# ---- offline quantizers ------------------------------------------------------
+
+def test_f16_encode_rounds_like_numpy_at_every_midpoint():
+    # Every finite positive fp16 value, the midpoints between neighbours (ties
+    # to even) and points just beside them: numpy's float64 -> float16 cast is
+    # correctly rounded.
+    finite = ALL16[(ALL16 & 0x7C00) != 0x7C00].view(np.float16).astype(np.float64)
+    pos = np.unique(finite[finite >= 0])
+    mids = (pos[:-1] + pos[1:]) / 2
+    v = np.concatenate([pos, mids, np.nextafter(mids, 0), np.nextafter(mids, 1), [65519.0, 65520.0, 1e6]])
+    v = np.concatenate([v, -v])
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f16_bits(v), want)
+
+
+def test_requant_round_trips_dequantized_codes():
+    # bf16(s * c) is within 2^-9 |c| of s * c, so rounding w / s returns c.
+    rng = np.random.default_rng(40)
+    N, K = 8, 512
+    codes = np.tile(np.arange(-8, 8, dtype=np.int8), (N, K // 16))
+    rng.shuffle(codes, axis=1)
+    _, scales = synth.int4_weights(rng, N, K)
+    s = synth.bf16_bits_to_f32(scales)
+    w = synth.f32_to_bf16_bits(np.repeat(s, 128, axis=1) * codes.astype(np.float32))
+    assert np.array_equal(oracle.requant_int4(w, scales), codes)
+
+
+def test_requant_is_the_nearest_grid_point():
+    # Brute force over the 16 grid points (ties to the even code), including
+    # weights far outside the grid (clamped to its ends) and zero scales.
+    rng = np.random.default_rng(41)
+    N, K = 6, 256
+    _, scales = synth.int4_weights(rng, N, K)
+    scales[2, 1] = 0
+    s = oracle.bf16_values(scales)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.15).astype(np.float32))
+    wv = oracle.bf16_values(w)
+    got = oracle.requant_int4(w, scales)
+    grid = np.arange(-8, 8)
+    for n in range(N):
+        for k in range(K):
+            sv = s[n, k // 128]
+            if sv == 0:
+                assert got[n, k] == 0
+                continue
+            dist = np.abs(wv[n, k] - sv * grid)
+            best = grid[dist == dist.min()]
+            want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            assert got[n, k] == want, (n, k)
+
+
+def test_requant_half_way_goes_to_the_even_code():
+    s = np.full((1, 1), 0x3C80, np.uint16)      # bf16 2^-6
+    c = np.arange(-8, 7)
+    w = synth.f32_to_bf16_bits(((c + 0.5) * 2.0 ** -6).astype(np.float32))[None, :]
+    w = np.pad(w, ((0, 0), (0, 128 - w.shape[1])))
+    got = oracle.requant_int4(w, s)[0, :len(c)]
+    assert np.array_equal(got, np.where(c % 2 == 0, c, c + 1))
+
+
+@pytest.mark.parametrize("iters", [0, 3])
+def test_fit_one_plane_is_mean_abs_and_sign(iters):
+    rng = np.random.default_rng(42)
+    N, K = 5, 256
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    w[0, :3] = 0
+    wv = oracle.bf16_values(w)
+    signs, a64, a16 = oracle.fit_planes(w, P=1, G=128, iters=iters)
+    assert np.array_equal(signs[0], np.where(wv < 0, -1, 1))
+    want = np.abs(wv).reshape(N, 2, 128).mean(axis=2)
+    assert np.allclose(a64[0], want, rtol=1e-15, atol=0)
+    assert np.array_equal(a16[0], want.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("iters", [0, 5])
+def test_fit_recovers_exact_superincreasing_planes(iters):
+    # w = 2^-3 b1 + 2^-4 b2 + 2^-5 b3 (each alpha above the sum of the later
+    # ones): the greedy pass already finds the signs (its mean-|r| scales are
+    # biased by the planes' overlap), and the least-squares rounds then give
+    # the scales exactly.
+    rng = np.random.default_rng(43)
+    N, K, P = 4, 384, 3
+    b = np.where(rng.integers(0, 2, size=(P, N, K)) == 1, -1, 1).astype(np.int8)
+    b[:, :, 0] = 1  # every group sees both signs of every plane below
+    b[:, :, 1] = -1
+    al = np.array([2.0 ** -3, 2.0 ** -4, 2.0 ** -5])
+    wv = np.tensordot(al, b.astype(np.float64), axes=1)
+    w = synth.f32_to_bf16_bits(wv.astype(np.float32))
+    assert np.array_equal(oracle.bf16_values(w), wv)
+    signs, a64, _ = oracle.fit_planes(w, P=P, G=128, iters=iters)
+    assert np.array_equal(signs, b)
+    want = np.broadcast_to(al[:, None, None], a64.shape)
+    if iters == 0:
+        # greedy: alpha_1 = mean |w| = 2^-3 + (overlap of plane 1 with 2, 3) / 128
+        b64 = b.astype(np.float64)
+        over = (al[1] * (b64[0] * b64[1]).reshape(N, 3, 128).sum(2)
+                + al[2] * (b64[0] * b64[2]).reshape(N, 3, 128).sum(2)) / 128
+        assert np.allclose(a64[0], al[0] + over, rtol=1e-15, atol=0)
+        assert np.all(np.abs(a64 - want) < al[2])
+    else:
+        assert np.allclose(a64, want, rtol=1e-13, atol=0)
+
+
+def fit_error(w, signs, a64, G):
+    wv = oracle.bf16_values(w)
+    P, N, K = signs.shape
+    approx = np.zeros((N, K))
+    for p in range(P):
+        approx += np.repeat(a64[p], G, axis=1) * signs[p]
+    return ((wv - approx) ** 2).reshape(N, K // G, G).sum(axis=2)
+
+
+@pytest.mark.parametrize("P,G", [(2, 64), (3, 128), (4, 256)])
+def test_fit_rounds_never_increase_the_error(P, G):
+    rng = np.random.default_rng(44 + P)
+    N, K = 6, 512
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    errs = [fit_error(w, *oracle.fit_planes(w, P=P, G=G, iters=it)[:2], G) for it in (0, 1, 2, 5, 20)]
+    for a, b in zip(errs, errs[1:]):
+        assert np.all(b <= a * (1 + 1e-12)), (P, G)
+    # the greedy fit is rarely a fixed point already: most groups, and the total, improve
+    assert np.mean(errs[-1] < errs[0] * (1 - 1e-9)) > 0.5 and errs[-1].sum() < errs[0].sum()
+
+
+def test_fit_fixed_point_is_least_squares_and_nearest_codes():
+    # After enough rounds the fit stops moving: alpha is the least-squares
+    # solution for its signs (numpy lstsq) and every weight's sign vector is a
+    # nearest one for that alpha (enumeration of all 2^P vectors).
+    rng = np.random.default_rng(45)
+    N, K, P, G = 3, 256, 3, 64
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wv = oracle.bf16_values(w)
+    signs, a64, _ = oracle.fit_planes(w, P=P, G=G, iters=60)
+    s2, a2, _ = oracle.fit_planes(w, P=P, G=G, iters=61)
+    assert np.array_equal(signs, s2) and np.allclose(a64, a2, rtol=1e-12, atol=0)
+    combos = np.array([[1 - 2 * ((c >> p) & 1) for p in range(P)] for c in range(1 << P)])
+    for n in range(N):
+        for g in range(K // G):
+            B = signs[:, n, g * G:(g + 1) * G].astype(np.float64)
+            x = wv[n, g * G:(g + 1) * G]
+            ls = np.linalg.lstsq(B.T, x, rcond=None)[0]
+            assert np.allclose(np.abs(ls), a64[:, n, g], rtol=1e-9, atol=1e-15)
+            vals = combos @ a64[:, n, g]
+            for k in range(G):
+                d = np.abs(x[k] - vals)
+                assert abs(x[k] - B[:, k] @ a64[:, n, g]) <= d.min() * (1 + 1e-12) + 1e-18
+
+
+def test_snap_recovers_codes_on_a_power_of_two_grid():
+    # alpha = d0 * a0 with d0 a power of two and a0 reaching 255 in every
+    # super-block: the snap returns exactly (a0, d0).
+    rng = np.random.default_rng(46)
+    P, N, K, G = 3, 5, 512, 64
+    a0 = rng.integers(0, 256, size=(P, N, K // G)).astype(np.uint8)
+    a0[0, :, 0] = 255
+    a0[1, :, 4] = 255
+    d0 = 2.0 ** -12
+    alpha = synth.f32_to_f16_bits((a0.astype(np.float64) * d0).astype(np.float32))
+    assert np.array_equal(oracle.f16_values(alpha), a0 * d0)
+    codes, d = oracle.snap_sa(alpha, G=G)
+    assert np.array_equal(codes, a0)
+    assert np.all(oracle.f16_values(d) == d0)
+
+
+def test_snap_error_is_at_most_half_a_step():
+    rng = np.random.default_rng(47)
+    P, N, K, G = 4, 7, 768, 128
+    _, alpha = synth.binplane_weights(rng, N, K, P=P, G=G)
+    codes, d = oracle.snap_sa(alpha, G=G)
+    al = oracle.f16_values(alpha)
+    dv = np.repeat(oracle.f16_values(d), 256 // G, axis=1)[None]
+    err = np.abs(al - dv * codes)
+    clamped = codes == 255
+    assert np.all(err[~clamped] <= dv.repeat(P, 0)[~clamped] / 2 * (1 + 1e-12))
+    # the largest scale of each super-block maps to 254 or 255
+    top = codes.reshape(P, N, K // 256, 256 // G).max(axis=(0, 3))
+    assert np.all(top >= 254)
+
+
 # ---- greedy argmax -----------------------------------------------------------
 
 def test_argmax_finds_planted_rows_with_closed_form_logit():
