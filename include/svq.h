@@ -169,6 +169,59 @@ int unpack_sa(const uint8_t* packed, int64_t N, int64_t K, int32_t G, int32_t P,
               int8_t* signs, uint8_t* codes, uint16_t* d_f16);
 
 /*
+ * Offline quantizers -- HOST pointers, synchronous, CPU only (threads over
+ * rows).  All arithmetic is fp64; results do not depend on the thread count.
+ *
+ * quantize_int4_frozen: the packing step of the report's sec. 2.1 -- weights
+ * trained under frozen symmetric group scales go back onto the same INT4
+ * grid, each to its nearest grid point:
+ *   codes[n][k] = clamp(round_half_even(w[n][k] / s[n][k/G]), -8, 7)
+ * (0 where s == 0).
+ *   w_bf16       [N][K] bf16 bits;  scales_bf16 [N][K/G] bf16 bits
+ *   codes        [N][K] int8 (pack with pack_int4_grouped)
+ * Errors: NULL, SHAPE (N < 1, G not in {64, 128, 256}, K % G).
+ */
+int quantize_int4_frozen(const uint16_t* w_bf16, const uint16_t* scales_bf16,
+                         int64_t N, int64_t K, int32_t G, int8_t* codes);
+
+/*
+ * fit_binary_planes: the binary-coding fit of the ShiftAddQwen README
+ * ("Output-aware fit": greedy initialisation, then alternating least squares
+ * with exhaustive code choice), per (row, group of G), on the plain weight
+ * error sum_k (w_k - sum_p alpha_p b_pk)^2:
+ *   greedy  r = w; for p = 1..P: b_p = sign(r) (+1 at 0), alpha_p = mean|r|,
+ *           r -= alpha_p b_p
+ *   round   each weight takes the sign vector whose sum_p alpha_p b_p is
+ *           nearest (lowest index on ties, index bit p set means b_p = -1),
+ *           then alpha is re-solved by least squares for those signs (kept
+ *           when the system is singular); `iters` rounds, fewer once the
+ *           signs stop changing (a fixed point)
+ *   finally every plane with alpha_p < 0 is negated (same weights), and
+ *   alpha is rounded to fp16 (nearest even).
+ *   w_bf16     [N][K] bf16 bits
+ *   signs      [P][N][K] int8 in {-1, +1};  alpha_f16 [P][N][K/G] fp16 bits
+ * Errors: NULL, SHAPE (N < 1, G not in {64, 128, 256}, K % G, P outside
+ * 1..6, iters < 0).
+ */
+int fit_binary_planes(const uint16_t* w_bf16, int64_t N, int64_t K, int32_t G,
+                      int32_t P, int32_t iters, int8_t* signs,
+                      uint16_t* alpha_f16);
+
+/*
+ * snap_sa_scales: plane scales onto the sa* grid (README "Format": alpha =
+ * d * a, u8 a per (plane, group), one fp16 d per 256-weight super-block;
+ * "Scale distillation": scales end snapped to the u8 grid).  Per (row,
+ * super-block j): d = fp16(max alpha / 255) over its planes and groups, and
+ * a = min(round_half_even(alpha / d), 255) (0 when d == 0).
+ *   alpha_f16  [P][N][K/G] fp16 bits, each >= 0
+ *   codes      [P][N][K/G] uint8;  d_f16 [N][K/256] fp16 bits (for pack_sa)
+ * Errors: NULL, SHAPE (N < 1, G not in {64, 128, 256}, K % 256, P outside
+ * 1..6), RANGE (a negative or NaN alpha).
+ */
+int snap_sa_scales(const uint16_t* alpha_f16, int64_t N, int64_t K, int32_t G,
+                   int32_t P, uint8_t* codes, uint16_t* d_f16);
+
+/*
  * gemv_w4a16 -- DEVICE pointers, asynchronous on `stream`.
  * One decode step of a W4A16 linear layer (report sec. 2.1, 3.3):
  *   y[n] = bf16_rne( sum_g s[n][g] * sum_{k in g} c[n][k] * x[k] ),

@@ -8,7 +8,9 @@ raises -- there is no fallback path.
 
 Functions (same names as the C ABI):
   pack_int4_grouped, unpack_int4_grouped, pack_binary_planes,
-  unpack_binary_planes, pack_sa, unpack_sa   host numpy arrays
+  unpack_binary_planes, pack_sa, unpack_sa,
+  quantize_int4_frozen, fit_binary_planes,
+  snap_sa_scales                             host numpy arrays
   gemv_w4a16, gemv_binplane, gemv_sa, gemm_smallm_w4a16,
   gemm_smallm_binplane, gemm_smallm_sa,
   lmhead_argmax, lmhead_argmax_binplane, lmhead_verify_greedy, verify_greedy,
@@ -24,7 +26,8 @@ import numpy as np
 __all__ = [
     "SvqError", "lib_path", "load", "int4_packed_bytes", "binplane_packed_bytes",
     "sa_packed_bytes", "lmhead_workspace_bytes", "pack_int4_grouped", "unpack_int4_grouped",
-    "pack_binary_planes", "unpack_binary_planes", "pack_sa", "unpack_sa", "gemv_w4a16",
+    "pack_binary_planes", "unpack_binary_planes", "pack_sa", "unpack_sa", "quantize_int4_frozen",
+    "fit_binary_planes", "snap_sa_scales", "gemv_w4a16",
     "gemv_binplane", "gemv_sa", "gemm_smallm_w4a16", "gemm_smallm_binplane", "gemm_smallm_sa", "lmhead_argmax", "lmhead_argmax_binplane",
     "lmhead_verify_greedy",
     "verify_greedy", "svq_stream_read",
@@ -70,6 +73,9 @@ def load():
         "unpack_binary_planes": ([V, I64, I64, I32, I32, V, V], ctypes.c_int),
         "pack_sa": ([V, V, V, I64, I64, I32, I32, V], ctypes.c_int),
         "unpack_sa": ([V, I64, I64, I32, I32, V, V, V], ctypes.c_int),
+        "quantize_int4_frozen": ([V, V, I64, I64, I32, V], ctypes.c_int),
+        "fit_binary_planes": ([V, I64, I64, I32, I32, I32, V, V], ctypes.c_int),
+        "snap_sa_scales": ([V, I64, I64, I32, I32, V, V], ctypes.c_int),
         "gemv_w4a16": ([V, V, V, I64, I64, I32, V], ctypes.c_int),
         "gemv_sa": ([V, V, V, I64, I64, I32, I32, V], ctypes.c_int),
         "gemm_smallm_sa": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
@@ -191,6 +197,35 @@ def unpack_sa(packed: np.ndarray, N: int, K: int, P: int, G: int = GROUP):
     d = np.empty((N, K // 256), np.uint16)
     _check("unpack_sa", load().unpack_sa(_np_ptr(packed), N, K, G, P, _np_ptr(signs), _np_ptr(codes), _np_ptr(d)))
     return signs, codes, d
+
+
+def quantize_int4_frozen(w_bf16: np.ndarray, scales_bf16: np.ndarray, G: int = GROUP) -> np.ndarray:
+    w = np.ascontiguousarray(w_bf16, np.uint16)
+    s = np.ascontiguousarray(scales_bf16, np.uint16)
+    N, K = w.shape
+    codes = np.empty((N, K), np.int8)
+    _check("quantize_int4_frozen", load().quantize_int4_frozen(_np_ptr(w), _np_ptr(s), N, K, G, _np_ptr(codes)))
+    return codes
+
+
+def fit_binary_planes(w_bf16: np.ndarray, P: int, G: int = GROUP, iters: int = 10):
+    w = np.ascontiguousarray(w_bf16, np.uint16)
+    N, K = w.shape
+    signs = np.empty((P, N, K), np.int8)
+    alpha = np.empty((P, N, K // G), np.uint16)
+    _check("fit_binary_planes",
+           load().fit_binary_planes(_np_ptr(w), N, K, G, P, iters, _np_ptr(signs), _np_ptr(alpha)))
+    return signs, alpha
+
+
+def snap_sa_scales(alpha_f16: np.ndarray, G: int = GROUP):
+    a = np.ascontiguousarray(alpha_f16, np.uint16)
+    P, N, ng = a.shape
+    K = ng * G
+    codes = np.empty((P, N, ng), np.uint8)
+    d = np.empty((N, K // 256), np.uint16)
+    _check("snap_sa_scales", load().snap_sa_scales(_np_ptr(a), N, K, G, P, _np_ptr(codes), _np_ptr(d)))
+    return codes, d
 
 
 # ---- device calls (torch tensors; bf16/fp16 values as int16/uint16 bits or bf16) --

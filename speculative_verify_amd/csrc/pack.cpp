@@ -7,33 +7,11 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
-#include <thread>
-#include <vector>
 
 #include "svq.h"
 #include "svq_internal.h"
 
 namespace {
-
-// Split [0, n) over the host's threads; each chunk is independent.
-template <class F>
-void parallel_for(int64_t n, F f) {
-  int nt = (int)std::thread::hardware_concurrency();
-  if (nt < 1) nt = 1;
-  if (nt > 32) nt = 32;
-  if (n < 64 || nt == 1) {
-    f((int64_t)0, n);
-    return;
-  }
-  std::vector<std::thread> th;
-  const int64_t chunk = (n + nt - 1) / nt;
-  for (int i = 0; i < nt; ++i) {
-    const int64_t lo = i * chunk, hi = lo + chunk < n ? lo + chunk : n;
-    if (lo >= hi) break;
-    th.emplace_back([=] { f(lo, hi); });
-  }
-  for (auto& t : th) t.join();
-}
 
 inline void store_u32(uint8_t* p, uint32_t v) { std::memcpy(p, &v, 4); }
 inline uint32_t load_u32(const uint8_t* p) {
@@ -53,7 +31,7 @@ int check_common(int64_t N, int64_t K, int32_t G) {
 // Sign section shared by the binary-plane and sa blobs (layout in svq.h).
 void put_signs(const int8_t* signs, int64_t N, int64_t K, int32_t P, uint8_t* packed) {
   const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16;
-  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+  svq::parallel_for(NT, [&](int64_t lo, int64_t hi) {
     for (int64_t rt = lo; rt < hi; ++rt)
       for (int64_t kt = 0; kt < KT; ++kt) {
         uint8_t* tile = packed + (rt * KT + kt) * 256 * P;
@@ -79,7 +57,7 @@ void put_signs(const int8_t* signs, int64_t N, int64_t K, int32_t P, uint8_t* pa
 
 void get_signs(const uint8_t* packed, int64_t N, int64_t K, int32_t P, int8_t* signs) {
   const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16;
-  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+  svq::parallel_for(NT, [&](int64_t lo, int64_t hi) {
     for (int64_t rt = lo; rt < hi; ++rt)
       for (int64_t kt = 0; kt < KT; ++kt) {
         const uint8_t* tile = packed + (rt * KT + kt) * 256 * P;
@@ -152,7 +130,7 @@ int pack_int4_grouped(const int8_t* codes, const uint16_t* scales_bf16, int64_t 
       return svq::fail(SVQ_ERR_RANGE, "pack_int4_grouped: code %d at (n=%lld, k=%lld) outside [-8, 7]",
                        (int)codes[i], (long long)(i / K), (long long)(i % K));
   const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16, ng = K / G;
-  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+  svq::parallel_for(NT, [&](int64_t lo, int64_t hi) {
     static const int8_t zero_row[32] = {0};
     for (int64_t rt = lo; rt < hi; ++rt)
       for (int64_t kt = 0; kt < KT; ++kt) {
@@ -187,7 +165,7 @@ int unpack_int4_grouped(const uint8_t* packed, int64_t N, int64_t K, int32_t G, 
   if (!codes || !scales_bf16 || !packed) return svq::fail(SVQ_ERR_NULL, "unpack_int4_grouped: NULL pointer");
   if (int rc = check_common(N, K, G)) return rc;
   const int64_t N16 = svq::round16(N), KT = K / 128, NT = N16 / 16, ng = K / G;
-  parallel_for(NT, [&](int64_t lo, int64_t hi) {
+  svq::parallel_for(NT, [&](int64_t lo, int64_t hi) {
     for (int64_t rt = lo; rt < hi; ++rt)
       for (int64_t kt = 0; kt < KT; ++kt) {
         const uint8_t* tile = packed + (rt * KT + kt) * 1024;
