@@ -91,7 +91,8 @@ enum {
 };
 
 #define SVQ_GROUP 128     /* the only supported group size */
-#define SVQ_MAX_M 16      /* rows of a verify block */
+#define SVQ_MAX_M 16      /* rows of a verify block (heads, acceptance) */
+#define SVQ_MAX_M_GEMM 64 /* rows of X a gemm_smallm_w4a16 call takes */
 #define SVQ_MAX_P 6       /* sign planes per weight */
 #define SVQ_MAX_K 8192    /* largest input dimension the kernels accept */
 
@@ -248,8 +249,11 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y,
  * The target's pass over a drafted block of M <= 16 positions (DFlash
  * summary sec. 4.1: the drafted tokens are verified in parallel; report
  * sec. 3.2: block size 16):  Y[m][n] = the W4A16 result for row m of X.
+ * Blocks of 16 < M <= 64 rows (a prefill chunk; the ShiftAddQwen README
+ * places batches below 64 in the quantized mat-mul regime) take a kernel
+ * that streams X with the weights; the result is defined the same way.
  *   X  [M][K] bf16 bits, 16-byte aligned;  Y [M][N] bf16 bits, 2-byte aligned.
- * Errors: as gemv_w4a16, plus SHAPE for M outside 1..16.
+ * Errors: as gemv_w4a16, plus SHAPE for M outside 1..64.
  */
 int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                       int32_t M, int64_t N, int64_t K, int32_t G, void* stream);

@@ -38,14 +38,14 @@ inline int device_cus(int* cus) {
 inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 inline int check_linear(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N, int64_t K,
-                 int32_t G, int32_t P) {
+                        int32_t G, int32_t P, int32_t max_m = SVQ_MAX_M) {
   svq::clear_error();
   if (!packed || !x || !y) return svq::fail(SVQ_ERR_NULL, "%s: NULL pointer", fn);
   if (N < 1 || N > (int64_t)INT_MAX - 16) return svq::fail(SVQ_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
   if (G != SVQ_GROUP) return svq::fail(SVQ_ERR_SHAPE, "%s: group size must be 128 (got %d)", fn, G);
   if (K < SVQ_GROUP || K % SVQ_GROUP || K > SVQ_MAX_K)
     return svq::fail(SVQ_ERR_SHAPE, "%s: K=%lld must be a multiple of 128 in [128, %d]", fn, (long long)K, SVQ_MAX_K);
-  if (M < 1 || M > SVQ_MAX_M) return svq::fail(SVQ_ERR_SHAPE, "%s: M=%d must be in 1..16", fn, M);
+  if (M < 1 || M > max_m) return svq::fail(SVQ_ERR_SHAPE, "%s: M=%d must be in 1..%d", fn, M, max_m);
   if (P != 0 && (P < 1 || P > SVQ_MAX_P)) return svq::fail(SVQ_ERR_SHAPE, "%s: P=%d must be in 1..6", fn, P);
   const int64_t N16 = (N + 15) / 16 * 16;
   if (N16 * K / 2 >= ((int64_t)1 << 31) || (P != 0 && N16 * K / 8 * P >= ((int64_t)1 << 31)))
@@ -115,6 +115,37 @@ inline int launched(const char* fn) {
 
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+// Launch shape of the 16 < M <= 64 kernels: R row tiles per block, so that
+// about one block lands on each CU (at most four tiles: the accumulators of
+// a wave are R x 2 x 4 registers), and a grid of at most one workgroup per
+// CU walking the blocks.
+struct MmqShape {
+  int R, grid;
+};
+
+inline int plan_mmq(int64_t N, MmqShape* s) {
+  int cus = 0;
+  if (int rc = device_cus(&cus)) return rc;
+  const int NT = (int)((N + 15) / 16);
+  int R = (NT + cus - 1) / cus;
+  R = R < 1 ? 1 : R > 4 ? 4 : R;
+  const int NB = (NT + R - 1) / R;
+  s->R = R;
+  s->grid = NB < cus ? NB : cus;
+  return SVQ_OK;
+}
+
+// Calls launch(ic<R>) for the block height of a 16 < M <= 64 launch.
+template <class L>
+void dispatch_r(int R, L&& launch) {
+  switch (R) {
+    case 1: launch(ic<1>{}); break;
+    case 2: launch(ic<2>{}); break;
+    case 3: launch(ic<3>{}); break;
+    default: launch(ic<4>{}); break;
+  }
+}
 
 // Calls launch(ic<GPW>, ic<MAXW>, ic<D>) for the shape's compile-time
 // parameters.  Depths above 2 are instantiated only for the 8-wave shapes,

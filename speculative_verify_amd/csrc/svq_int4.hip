@@ -9,6 +9,7 @@
 
 #include "kernels.h"
 #include "launch.h"
+#include "mmq.h"
 #include "svq.h"
 #include "svq_internal.h"
 
@@ -57,10 +58,26 @@ int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
 
 int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
                       int32_t G, void* stream) {
-  if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0)) return rc;
+  if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0, SVQ_MAX_M_GEMM)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M > SVQ_MAX_M) {
+    MmqShape sh;
+    if (int rc = plan_mmq(N, &sh)) return rc;
+    const int KT = (int)(K / 128), NT = (int)((N + 15) / 16);
+    dispatch_r(sh.R, [&](auto Rc) {
+      constexpr int R = decltype(Rc)::value;
+      constexpr int D = R == 4 ? 2 : 3;  // the deepest ring that stays in registers
+      if (M <= 32)
+        hipLaunchKernelGGL((k_gemm_mmq_w4a16<2, 1, R, D>), dim3(sh.grid), dim3(64 * kMmqWaves), 0, st, packed, X, Y,
+                           M, (int)N, (int)K, KT, NT);
+      else
+        hipLaunchKernelGGL((k_gemm_mmq_w4a16<2, 2, R, D>), dim3(sh.grid), dim3(64 * kMmqWaves), 0, st, packed, X, Y,
+                           M, (int)N, (int)K, KT, NT);
+    });
+    return launched("gemm_smallm_w4a16");
+  }
   Shape sh;
   if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch(sh, [&](auto G, auto W, auto D) {
     hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,

@@ -266,6 +266,61 @@ def test_gemm_wide_k(M, N, K):
     assert np.array_equal(idx, rows.astype(np.int32))
 
 
+# Blocks of 16 < M <= 64 rows (the kernel that streams X with the weights).
+
+@pytest.mark.parametrize("M", [17, 20, 24, 31, 32, 33, 40, 47, 48, 56, 63, 64])
+def test_gemm_w4a16_midm_ragged(M):
+    rng = np.random.default_rng(300 + M)
+    N, K = 1000 + 37 * M, 1152
+    codes, scales = synth.int4_weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    print(f"gemm_smallm_w4a16 M={M} N={N} K={K}", flush=True)
+    check_close(run_gemm_w4a16(codes, scales, X), Y, A, f"M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 12288, 4096), (64, 4096, 4096), (32, 12288, 4096), (48, 4096, 4096),
+                                   (64, 1, 128), (17, 33, 8192), (64, 300, 256)])
+def test_gemm_w4a16_midm_shapes(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    codes, scales = synth.int4_weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    print(f"gemm_smallm_w4a16 M={M} N={N} K={K}", flush=True)
+    got = run_gemm_w4a16(codes, scales, X)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    check_close(got, Y, A, f"M={M} N={N} K={K}")
+
+
+def test_gemm_w4a16_midm_many_blocks_per_workgroup():
+    # 2063 row tiles: blocks of four tiles, several blocks per workgroup, a
+    # ragged last tile; checked on a sample of output rows.
+    rng = np.random.default_rng(77)
+    M, N, K = 64, 33000, 1024
+    codes, scales = synth.int4_weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    got = run_gemm_w4a16(codes, scales, X)
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(N - 70, N), rng.integers(0, N, 600)]))
+    Y, A = oracle.linear_w4a16(codes[rows], scales[rows], X)
+    check_close(got[:, rows], Y, A, "M=64 N=33000 sample")
+
+
+@pytest.mark.parametrize("M", [33, 64])
+def test_gemm_w4a16_midm_onehot_unit_scale_is_exact(M):
+    # Row m of X is e_{k_m}: Y[m][n] = c[n][k_m] exactly, for every m-tile.
+    N, K = 48, 512
+    rng = np.random.default_rng(90 + M)
+    codes = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    scales = np.full((N, K // 128), 0x3F80, np.uint16)
+    blob = dev(svq.pack_int4_grouped(codes, scales))
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    for base in range(0, K, 64):
+        ks = [(base + 3 * m) % K for m in range(M)]
+        X = np.zeros((M, K), np.uint16)
+        X[np.arange(M), ks] = 0x3F80
+        svq.gemm_smallm_w4a16(blob, dev(X), Y, M, N, K)
+        assert np.array_equal(bf16_host(Y), codes[:, ks].T.astype(np.float64)), base
+
+
 def test_gemm_onehot_unit_scale_is_exact():
     # Row m of X is e_{k_m}; Y[m][n] = c[n][k_m] exactly (checks both MFMA operand layouts).
     N, K, M = 48, 256, 16
