@@ -20,7 +20,8 @@ last-level cache, so every call streams its weights from HBM.
 Also timed, each call on its own but outside the step (so the step and its
 `value` keep their definition): the sa* storage of sign planes (u8 scale
 codes per plane and group, one fp16 d per 256-weight super-block) for
-decode and verify, P=3, groups of 64 and 128.
+decode and verify, P=3, groups of 64 and 128; and W4A16 blocks of M=32 and
+M=64 rows (a prefill chunk, the kernel for 16 < M <= 64).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one
 GPU's share.
@@ -159,11 +160,26 @@ def build_extra(svq, synth, torch):
         name = (f"gemv_sa_p{P}_g{Gs}_m1_n{N}" if M == 1 else f"gemm_smallm_sa_p{P}_g{Gs}_m{M}_n{N}")
         calls.append((name, alg_bytes_sa(M, N, P, Gs), make(), make))
 
+    def w4(M, N):
+        def make():
+            seed[0] += 1
+            blob = synth.device_int4_blob(N, K, seed[0])
+            seed[0] += 1
+            X = synth.device_activations(M, K, seed[0]).view(torch.int16)
+            Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+            return lambda: svq.gemm_smallm_w4a16(blob, X, Y, M, N, K)
+
+        calls.append((f"gemm_smallm_w4a16_m{M}_n{N}", alg_bytes_linear("w4a16", M, N), make(), make))
+
     sa(1, 12288, 3, 128)
     sa(16, 4096, 3, 128)
     sa(16, 12288, 3, 128)
     sa(1, 12288, 3, 64)
     sa(16, 12288, 3, 64)
+    w4(32, 4096)
+    w4(32, 12288)
+    w4(64, 4096)
+    w4(64, 12288)
     return calls
 
 

@@ -117,19 +117,20 @@ template <int V>
 using ic = std::integral_constant<int, V>;
 
 // Launch shape of the 16 < M <= 64 kernels: R row tiles per block, so that
-// about one block lands on each CU (at most four tiles: the accumulators of
-// a wave are R x 2 x 4 registers), and a grid of at most one workgroup per
-// CU walking the blocks.
+// about one block lands on each CU (at most four tiles, three above M = 32:
+// a wave holds R x ceil(M / 16) accumulator tiles), and a grid of at most
+// one workgroup per CU walking the blocks.
 struct MmqShape {
   int R, grid;
 };
 
-inline int plan_mmq(int64_t N, MmqShape* s) {
+inline int plan_mmq(int64_t N, int32_t M, MmqShape* s) {
   int cus = 0;
   if (int rc = device_cus(&cus)) return rc;
   const int NT = (int)((N + 15) / 16);
+  const int rmax = M > 32 ? 3 : 4;  // the accumulators of R x ceil(M / 16) tiles must stay in registers
   int R = (NT + cus - 1) / cus;
-  R = R < 1 ? 1 : R > 4 ? 4 : R;
+  R = R < 1 ? 1 : R > rmax ? rmax : R;
   const int NB = (NT + R - 1) / R;
   s->R = R;
   s->grid = NB < cus ? NB : cus;

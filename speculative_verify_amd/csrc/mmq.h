@@ -7,29 +7,28 @@
 // The M <= 16 kernels keep a wave's whole K slice of X in registers; at
 // M = 64 that slice no longer fits, so here X streams with the weights.
 // Work decomposition: a workgroup owns R consecutive 16-row weight tiles (a
-// block) at a time, grid-stride over blocks.  Its 8 waves form WM groups
-// along M (MTW 16-row m-tiles each) times WK = 8 / WM groups along K; wave
-// (wm, wk) walks the 128-wide column tiles [wk * CK, (wk + 1) * CK) of the
-// block, and each step loads, for one column tile, its rows of X (cached,
-// every workgroup reads them) and the block's R weight tiles (non-temporal,
-// read once), D steps ahead.  A decoded weight tile feeds MTW MFMA chains
-// and an X fragment R chains, so X is reused across the block's rows and the
-// weights across the wave's m-tiles.  The partial sums of the WK groups meet
-// in LDS once per block.
+// block) at a time, grid-stride over blocks; its 8 waves split K, wave w
+// walking the 128-wide column tiles [w * CK, (w + 1) * CK) of the block.  A
+// step of a wave covers one column tile for all MT 16-row m-tiles of X and
+// the block's R weight tiles: the weights are decoded once per step and feed
+// MT MFMA chains each, and every X fragment feeds R chains.  The partial
+// sums of the 8 waves meet in LDS once per block.
 //
-// X staging.  The MFMA A operand gives consecutive lanes consecutive rows,
-// so loading it straight from row-major X touches one cache line per lane.
-// Instead a quarter-wave loads one row's 256 bytes of the column tile (fully
-// coalesced), the wave writes its rows into a private LDS region with the
-// 16-byte chunks of row p XOR-swizzled by p mod 16, and reads them back in
-// operand order: in both directions the 16 lanes of a quarter-wave touch 16
-// distinct chunks of 256 bytes, so neither side has bank conflicts, and as
-// the region is the wave's own no barrier is needed.
+// Data movement per step.  Weight tiles (read once, non-temporal) run in a
+// register ring D - 1 steps ahead.  X (read by every workgroup, cached) is
+// loaded coalesced -- a quarter-wave reads one row's 256 bytes of the column
+// tile -- one step ahead, in two halves of at most two m-tiles, and written
+// into the wave's private LDS buffer with the 16-byte chunks of row p
+// XOR-swizzled by p mod 16; the MFMA fragments are read back from it one
+// m-tile at a time (both directions free of bank conflicts).  LDS executes a
+// wave's operations in order, so a half of the next step's X is written as
+// soon as the current step has read the rows it replaces; no barrier is
+// needed until the block ends.
 //
 // Exact operands as in the M <= 16 kernel: nibble u = c + 8 decodes to the
-// bf16 value 136 + c; the correction -136 * sum_k X[m][k] over the group is
-// one MFMA chain per m-tile against the constant bf16 pair (-136, -136),
-// shared by the block's R row tiles and exact term by term.
+// bf16 value 136 + c, and each chain starts from -136 * sum_k X[m][k] over
+// the group, one MFMA chain per m-tile against the constant bf16 pair
+// (-136, -136), exact term by term.
 #pragma once
 
 #include "kernels.h"
@@ -39,128 +38,121 @@ namespace {
 constexpr int kMmqWaves = 8;
 constexpr uint32_t kMinus136Pair = 0xC308C308u;  // bf16 pair (-136, -136)
 
-template <int MTW, int R>
-struct MmqSlot {
-  uint4 x[MTW][4];  // load j = 4 mi + u: row 16 mi + 4 u + lane / 16, k chunk lane % 16
-  uint4 c[R];       // the lane's 16 code bytes of each row tile of the block
-  uint32_t s[R];    // bf16 scale of (row 16 rt + r, group g) in the low half
+// The R weight tiles of one step and their scales.
+template <int R>
+struct MmqW {
+  uint4 c[R];     // the lane's 16 code bytes of each row tile of the block
+  uint32_t s[R];  // bf16 scale of (row 16 rt + r, group g) in the low half
 };
 
-// Lane-dependent parts of a step's buffer offsets, fixed for the kernel:
-// X row 16 (mt0 + mi) + 4 u + lane / 16 at k chunk lane % 16; the lane's 16
-// bytes of a weight tile; row r of a scale run.  A step adds one uniform
-// value per load (which carries bit 31 when the step reads nothing), so all
-// range-relevant offsets stay in the per-lane register, where the buffer
-// range check sees them: rows >= M and tiles past NT fall outside their
-// sections and read zero.
-template <int MTW>
-struct MmqLanes {
-  uint32_t x[MTW][4];
-  uint32_t w, s;
-};
-
-template <int MTW>
-__device__ __forceinline__ MmqLanes<MTW> mmq_lanes(int K, int KT4, int mt0, int lane) {
-  MmqLanes<MTW> o;
-#pragma unroll
-  for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      o.x[mi][u] = ((uint32_t)(16 * (mt0 + mi) + 4 * u + (lane >> 4)) * (uint32_t)K + 8u * (lane & 15)) * 2u;
-  o.w = 16u * lane;
-  o.s = (uint32_t)(lane & 15) * (uint32_t)KT4 * 2u;
-  return o;
-}
-
-// Loads step (blk, g) of a wave; `live` false makes the whole step read zero.
-template <int MTW, int R>
-__device__ __forceinline__ void load_mmq_step(MmqSlot<MTW, R>& sl, __amdgpu_buffer_rsrc_t xr, const BlobView& b,
-                                              const MmqLanes<MTW>& lo, int blk, bool live, int g) {
-  const uint32_t oob = oob_bit(live && g < b.KT);
-  const uint32_t xs = (256u * g) | oob;
-#pragma unroll
-  for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, lo.x[mi][u] + xs, 0, 0);
-      sl.x[mi][u] = make_uint4(v.x, v.y, v.z, v.w);
-    }
-#pragma unroll
-  for (int rt = 0; rt < R; ++rt) {
-    const uint32_t tile = (uint32_t)(R * blk + rt);
-    sl.c[rt] = ld_stream16(b.w, lo.w + (((tile * b.KT + g) * 1024u) | oob));
-    sl.s[rt] = __builtin_amdgcn_raw_buffer_load_b16(b.s, lo.s + (((16u * tile * b.KT4 + g) * 2u) | oob), 0, 0);
-  }
-}
-
-// Byte offset of 16-byte chunk c of row p in a wave's staging region.
+// Byte offset of 16-byte chunk c of row p in a wave's X buffer.
 __device__ __forceinline__ uint32_t mmq_chunk(int p, int c) { return (uint32_t)(p * 256 + ((c ^ (p & 15)) << 4)); }
 
-// The slot's rows of X into the wave's region, then back as MFMA A operands:
-// a[mi][t] is lane (q, r)'s X[16 (mt0 + mi) + r][128 g + 32 t + 8 q + 0..7].
-template <int MTW>
-__device__ __forceinline__ void mmq_stage_x(const uint4 (&x)[MTW][4], char* region, int lane, int q, int r,
-                                            uint4 (&a)[MTW][4]) {
-#pragma unroll
-  for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<uint4*>(region + mmq_chunk(16 * mi + 4 * u + (lane >> 4), lane & 15)) = x[mi][u];
-#pragma unroll
-  for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      a[mi][t] = *reinterpret_cast<const uint4*>(region + mmq_chunk(16 * mi + r, 4 * t + q));
-}
-
-template <int MTW, int WM, int R, int D>
+template <int MT, int R, int D>
 __global__ void __launch_bounds__(64 * kMmqWaves)
     k_gemm_mmq_w4a16(const uint8_t* __restrict__ blob, const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                      int M, int N, int K, int KT, int NT) {
-  constexpr int WK = kMmqWaves / WM;
+  // m-tiles of the first and second half of a step's X: the whole step in
+  // one half when the registers allow (one row tile per block).
+  constexpr int H0 = (MT < 2 || R == 1) ? MT : 2;
+  constexpr int H1 = MT - H0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, r = lane & 15;
-  const int wm = wave % WM, wk = wave / WM;
-  const int mt0 = wm * MTW;
   const BlobView bv = int4_view(blob, KT, NT);
+  // Rows >= M lie past the end of this range and read zero; the range check
+  // sees the whole offset, which is kept in the per-lane register.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
   const int NB = (NT + R - 1) / R;
-  const int CK = (KT + WK - 1) / WK;
+  const int CK = (KT + kMmqWaves - 1) / kMmqWaves;
   const int T = ((NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * CK;  // steps of every wave
-  const MmqLanes<MTW> lo = mmq_lanes<MTW>(K, bv.KT4, mt0, lane);
-  // Step order: the workgroup's blocks in turn (blockIdx.x, + gridDim.x, ...),
-  // within a block the wave's column tiles wk * CK + (c + blockIdx.x) % CK,
-  // c = 0 .. CK - 1.  Every workgroup reads all of X; starting each one at a
-  // different column tile spreads those reads over the whole of X instead
-  // of sending every CU to the same lines at once.  The load cursor runs D
-  // steps ahead of the consumer.
-  int ld_blk = (int)blockIdx.x, ld_c = 0, ld_rot = (int)blockIdx.x % CK, ld_i = 0;
-  auto load_next = [&](MmqSlot<MTW, R>& slot) {
-    load_mmq_step<MTW, R>(slot, xr, bv, lo, ld_blk, ld_i < T, wk * CK + ld_rot);
-    ++ld_i;
-    ld_rot = ld_rot + 1 == CK ? 0 : ld_rot + 1;
-    if (++ld_c == CK) {
-      ld_c = 0;
-      ld_blk += (int)gridDim.x;
+
+  // LDS: each wave's X buffer (MT * 16 rows of 256 bytes), then the
+  // cross-wave staging of one row tile's partial sums.
+  __shared__ uint4 xbuf[kMmqWaves][MT * 16 * 16];
+  __shared__ float4 red[kMmqWaves][MT][64];
+  char* xb = reinterpret_cast<char*>(xbuf[wave]);
+
+  // Lane-dependent offsets.  X: row 4 u + lane / 16 of an m-tile, chunk
+  // lane % 16; the m-tile and the column tile are added per load.
+  const uint32_t xlane = ((uint32_t)(lane >> 4) * (uint32_t)K + 8u * (lane & 15)) * 2u;
+  const uint32_t xrow4 = 4u * (uint32_t)K * 2u;  // four rows further
+  const uint32_t wlane = 16u * lane, slane = (uint32_t)r * (uint32_t)bv.KT4 * 2u;
+
+  // Step order: the workgroup's blocks in turn; within a block the wave's
+  // column tiles w * CK + (c + blockIdx.x) % CK, c = 0 .. CK - 1 (every
+  // workgroup reads all of X; starting each at a different column tile
+  // spreads those reads over X).  Cursors for X (one step ahead) and the
+  // weights (D - 1 ahead) advance without division.
+  struct Cursor {
+    int blk, c, rot, i;
+  };
+  auto advance = [&](Cursor& u) {
+    ++u.i;
+    u.rot = u.rot + 1 == CK ? 0 : u.rot + 1;
+    if (++u.c == CK) {
+      u.c = 0;
+      u.blk += (int)gridDim.x;
+    }
+  };
+  auto col = [&](const Cursor& u) { return wave * CK + u.rot; };
+  auto step_oob = [&](const Cursor& u) { return oob_bit(u.i < T && col(u) < KT); };
+
+  auto load_x = [&](const Cursor& u, int mt0, int nm, uint4 (&xh)[H0][4]) {
+    const uint32_t uni = (256u * (uint32_t)col(u)) | step_oob(u);
+#pragma unroll
+    for (int h = 0; h < H0; ++h)
+      if (h < nm)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t off = xlane + (uint32_t)(mt0 + h) * 4u * xrow4 + (uint32_t)v * xrow4;  // row 16 (mt0 + h) + 4 v
+          const v4u_t t = __builtin_amdgcn_raw_buffer_load_b128(xr, off + uni, 0, 0);
+          xh[h][v] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+  };
+  auto store_x = [&](int mt0, int nm, const uint4 (&xh)[H0][4]) {
+#pragma unroll
+    for (int h = 0; h < H0; ++h)
+      if (h < nm)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<uint4*>(xb + mmq_chunk(16 * (mt0 + h) + 4 * v + (lane >> 4), lane & 15)) = xh[h][v];
+  };
+  auto load_w = [&](const Cursor& u, MmqW<R>& w) {
+    const uint32_t oob = step_oob(u);
+    const uint32_t g = (uint32_t)col(u);
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt) {
+      const uint32_t tile = (uint32_t)(R * u.blk + rt);
+      w.c[rt] = ld_stream16(bv.w, wlane + (((tile * bv.KT + g) * 1024u) | oob));
+      w.s[rt] = __builtin_amdgcn_raw_buffer_load_b16(bv.s, slane + (((16u * tile * bv.KT4 + g) * 2u) | oob), 0, 0);
     }
   };
 
-  MmqSlot<MTW, R> ring[D];
+  Cursor xc{(int)blockIdx.x, 0, (int)blockIdx.x % CK, 0};
+  Cursor wc = xc;
+  uint4 xh[H0][4];
+  // Prologue: step 0's X into LDS, the first D - 1 steps' weights in flight.
+  load_x(xc, 0, H0, xh);
+  MmqW<R> ring[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    load_next(ring[j]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int j = 0; j + 1 < D; ++j) {
+    load_w(wc, ring[j]);
+    advance(wc);
   }
-  __shared__ float4 red[WK][WM * R * MTW][64];
-  __shared__ uint4 xstage[kMmqWaves][MTW * 16 * 16];  // a wave's rows of one column tile
-  char* region = reinterpret_cast<char*>(xstage[wave]);
+  store_x(0, H0, xh);
+  if constexpr (H1 > 0) {
+    load_x(xc, H0, H1, xh);
+    store_x(H0, H1, xh);
+  }
+  advance(xc);
+
   const PairDecode magic = int4_decode();
   const uint32_t minus136[4] = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
-  f32x4_t acc[R][MTW];
+  f32x4_t acc[R][MT];
 #pragma unroll
   for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-    for (int mi = 0; mi < MTW; ++mi) acc[rt][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mi = 0; mi < MT; ++mi) acc[rt][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   int blk = (int)blockIdx.x, cc = 0;  // consumer: current block, column tiles done in it
   int i0 = 0;
@@ -168,81 +160,113 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const MmqSlot<MTW, R>& sl = ring[j];
-      uint4 xa[MTW][4];
-      mmq_stage_x<MTW>(sl.x, region, lane, q, r, xa);
-      // All R x MTW chains advance together, one 32-wide k block at a time,
-      // so consecutive MFMAs are independent; the correction chain of each
-      // m-tile leads its k block.
-      f32x4_t corr[MTW], c[R][MTW];
-#pragma unroll
-      for (int mi = 0; mi < MTW; ++mi) corr[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int mi = 0; mi < MTW; ++mi) {
-          const uint32_t a[4] = {xa[mi][t].x, xa[mi][t].y, xa[mi][t].z, xa[mi][t].w};
-          corr[mi] = mfma16x16x32(a, minus136, corr[mi]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < R; ++rt) {
-          const uint32_t wt = t == 0 ? sl.c[rt].x : t == 1 ? sl.c[rt].y : t == 2 ? sl.c[rt].z : sl.c[rt].w;
-          const uint32_t bq[4] = {int4_pair(wt, 0, magic), int4_pair(wt, 1, magic), int4_pair(wt, 2, magic),
-                                  int4_pair(wt, 3, magic)};
-#pragma unroll
-          for (int mi = 0; mi < MTW; ++mi) {
-            const uint32_t a[4] = {xa[mi][t].x, xa[mi][t].y, xa[mi][t].z, xa[mi][t].w};
-            c[rt][mi] = mfma16x16x32(a, bq, t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c[rt][mi]);
-          }
-        }
+      const bool block_done = cc + 1 == CK;
+      // Next step's X (first half) goes out first.  The weights D - 1 steps
+      // ahead (into the slot step i - 1 freed) follow the last X load of the
+      // step: loads complete in order, so waiting for that X then leaves the
+      // weight loads in flight.
+      load_x(xc, 0, H0, xh);
+      if constexpr (H1 == 0) {
+        load_w(wc, ring[(j + D - 1) % D]);
+        advance(wc);
       }
+      const MmqW<R>& w = ring[j];
+      uint32_t bq[R][4][4];
+      float sc[R];
 #pragma unroll
       for (int rt = 0; rt < R; ++rt) {
-        const float sc = __uint_as_float(sl.s[rt] << 16);
+        const uint32_t wd[4] = {w.c[rt].x, w.c[rt].y, w.c[rt].z, w.c[rt].w};
 #pragma unroll
-        for (int mi = 0; mi < MTW; ++mi)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[rt][mi][e] = fmaf(sc, c[rt][mi][e] + corr[mi][e], acc[rt][mi][e]);
+          for (int e = 0; e < 4; ++e) bq[rt][t][e] = int4_pair(wd[t], e, magic);
+        sc[rt] = __uint_as_float(w.s[rt] << 16);
       }
-      // Slot j is refilled only after its last use, so it keeps its registers.
-      __builtin_amdgcn_sched_barrier(0);
-      load_next(ring[j]);
-      // The block's last column tile: every wave is at the same step, so the
-      // condition (and the barriers under it) is uniform across the workgroup.
-      const bool block_done = ++cc == CK;
-      if (block_done) cc = 0;
-      if (i < T && block_done) {
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        uint32_t a[4][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 v = *reinterpret_cast<const uint4*>(xb + mmq_chunk(16 * mi + r, 4 * t + q));
+          a[t][0] = v.x;
+          a[t][1] = v.y;
+          a[t][2] = v.z;
+          a[t][3] = v.w;
+        }
+        // The first half's rows have been read: the next step's first half
+        // replaces them (in-order LDS) and its second half goes out.
+        if constexpr (H1 > 0) {
+          if (mi == H0 - 1) {
+            if (!block_done) {
+              store_x(0, H0, xh);
+              load_x(xc, H0, H1, xh);
+            }
+            load_w(wc, ring[(j + D - 1) % D]);
+            advance(wc);
+          }
+        }
+        f32x4_t corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) corr = mfma16x16x32(a[t], minus136, corr);
+        f32x4_t c[R];
+#pragma unroll
+        for (int rt = 0; rt < R; ++rt) c[rt] = corr;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int rt = 0; rt < R; ++rt) c[rt] = mfma16x16x32(a[t], bq[rt][t], c[rt]);
 #pragma unroll
         for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-          for (int mi = 0; mi < MTW; ++mi) {
-            red[wk][(wm * R + rt) * MTW + mi][lane] =
-                make_float4(acc[rt][mi][0], acc[rt][mi][1], acc[rt][mi][2], acc[rt][mi][3]);
-            acc[rt][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        __syncthreads();
-        for (int e = threadIdx.x; e < WM * R * MTW * 64; e += 64 * kMmqWaves) {
-          const int ln = e & 63, slot = e >> 6;
-          const int mi = slot % MTW, rt = (slot / MTW) % R, wmm = slot / (MTW * R);
-          float4 tot = red[0][slot][ln];
-#pragma unroll
-          for (int w = 1; w < WK; ++w) {
-            const float4 v = red[w][slot][ln];
-            tot.x += v.x;
-            tot.y += v.y;
-            tot.z += v.z;
-            tot.w += v.w;
-          }
-          const int n = 16 * (R * blk + rt) + (ln & 15);
-          const int mb = 16 * (wmm * MTW + mi) + 4 * (ln >> 4);
-          const float v[4] = {tot.x, tot.y, tot.z, tot.w};
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
-            if (mb + ii < M && n < N) Y[(size_t)(mb + ii) * N + n] = f32_to_bf16_rne(v[ii]);
-        }
-        __syncthreads();
+          for (int e = 0; e < 4; ++e) acc[rt][mi][e] = fmaf(sc[rt], c[rt][e], acc[rt][mi][e]);
       }
-      if (block_done) blk += (int)gridDim.x;
+      if (block_done) {
+        // Every wave is at the same step, so this branch (and its barriers)
+        // is uniform.  The partial sums of one row tile at a time meet in LDS.
+        if (i < T) {
+#pragma unroll
+          for (int rt = 0; rt < R; ++rt) {
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+              red[wave][mi][lane] = make_float4(acc[rt][mi][0], acc[rt][mi][1], acc[rt][mi][2], acc[rt][mi][3]);
+              acc[rt][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            __syncthreads();
+            for (int e = threadIdx.x; e < MT * 64; e += 64 * kMmqWaves) {
+              const int ln = e & 63, mi = e >> 6;
+              float4 tot = red[0][mi][ln];
+#pragma unroll
+              for (int ww = 1; ww < kMmqWaves; ++ww) {
+                const float4 v = red[ww][mi][ln];
+                tot.x += v.x;
+                tot.y += v.y;
+                tot.z += v.z;
+                tot.w += v.w;
+              }
+              const int n = 16 * (R * blk + rt) + (ln & 15);
+              const int mb = 16 * mi + 4 * (ln >> 4);
+              const float v[4] = {tot.x, tot.y, tot.z, tot.w};
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii)
+                if (mb + ii < M && n < N) Y[(size_t)(mb + ii) * N + n] = f32_to_bf16_rne(v[ii]);
+            }
+            __syncthreads();
+          }
+        }
+        blk += (int)gridDim.x;
+        cc = 0;
+        // The next block's first X: its first half waited in registers.
+        store_x(0, H0, xh);
+        if constexpr (H1 > 0) {
+          load_x(xc, H0, H1, xh);
+          store_x(H0, H1, xh);
+        }
+      } else {
+        ++cc;
+        if constexpr (H1 > 0) store_x(H0, H1, xh);
+        else store_x(0, H0, xh);
+      }
+      advance(xc);
     }
     i0 += D;
   } while (i0 < T);

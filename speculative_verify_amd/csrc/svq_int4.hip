@@ -62,17 +62,20 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (M > SVQ_MAX_M) {
     MmqShape sh;
-    if (int rc = plan_mmq(N, &sh)) return rc;
+    if (int rc = plan_mmq(N, M, &sh)) return rc;
     const int KT = (int)(K / 128), NT = (int)((N + 15) / 16);
     dispatch_r(sh.R, [&](auto Rc) {
       constexpr int R = decltype(Rc)::value;
-      constexpr int D = R == 4 ? 2 : 3;  // the deepest ring that stays in registers
+      // The deepest weight ring that stays in registers for the block height.
       if (M <= 32)
-        hipLaunchKernelGGL((k_gemm_mmq_w4a16<2, 1, R, D>), dim3(sh.grid), dim3(64 * kMmqWaves), 0, st, packed, X, Y,
-                           M, (int)N, (int)K, KT, NT);
+        hipLaunchKernelGGL((k_gemm_mmq_w4a16<2, R, R == 4 ? 2 : 3>), dim3(sh.grid), dim3(64 * kMmqWaves), 0, st,
+                           packed, X, Y, M, (int)N, (int)K, KT, NT);
+      else if (M <= 48)
+        hipLaunchKernelGGL((k_gemm_mmq_w4a16<3, R < 4 ? R : 3, R >= 3 ? 2 : 3>), dim3(sh.grid),
+                           dim3(64 * kMmqWaves), 0, st, packed, X, Y, M, (int)N, (int)K, KT, NT);
       else
-        hipLaunchKernelGGL((k_gemm_mmq_w4a16<2, 2, R, D>), dim3(sh.grid), dim3(64 * kMmqWaves), 0, st, packed, X, Y,
-                           M, (int)N, (int)K, KT, NT);
+        hipLaunchKernelGGL((k_gemm_mmq_w4a16<4, R < 4 ? R : 3, R >= 3 ? 2 : 3>), dim3(sh.grid),
+                           dim3(64 * kMmqWaves), 0, st, packed, X, Y, M, (int)N, (int)K, KT, NT);
     });
     return launched("gemm_smallm_w4a16");
   }
