@@ -445,6 +445,56 @@ __device__ __forceinline__ void load_sa_tile(SaSlot<GPW, P, G>& sl, const SaView
   load_run<GPW >= 4 ? 4 : 2>(b.d, ((uint32_t)(row * (b.KT4 / 2) + g0 / 2) * 2u) | oob, &sl.d);
 }
 
+// Activation staging for the M <= 16 mat-muls (see load_x_pairs above).  Loading
+// xp directly gives the 16 lanes of a quarter-wave 16 different rows, i.e. 16
+// cache lines per quarter; instead a quarter-wave loads one row's 256 bytes
+// of a column tile (lane: row 4 u + lane / 16, 16-byte chunk lane % 16), and
+// the wave transposes through a private 4 KiB LDS region, one column tile at
+// a time, with the chunks of row p XOR-swizzled by p mod 16 so that neither
+// the writes nor the reads have bank conflicts.  Rows >= M and groups >= KT
+// read zero (buffer range and offset bit 31).
+template <int GPW>
+struct XRows {
+  uint4 v[GPW][4];
+};
+
+template <int GPW>
+__device__ __forceinline__ void load_x_rows(const uint16_t* __restrict__ X, int M, int K, int g0, int KT, int lane,
+                                            XRows<GPW>& xr) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+  const uint32_t lo = ((uint32_t)(lane >> 4) * (uint32_t)K + 8u * (lane & 15)) * 2u;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t off = (lo + (uint32_t)(4 * u) * (uint32_t)K * 2u + 256u * (g0 + gi)) | oob_bit(g0 + gi < KT);
+      const v4u_t t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      xr.v[gi][u] = make_uint4(t.x, t.y, t.z, t.w);
+    }
+}
+
+__device__ __forceinline__ uint32_t xrow_chunk(int p, int c) { return (uint32_t)(p * 256 + ((c ^ (p & 15)) << 4)); }
+
+template <int GPW>
+__device__ __forceinline__ void transpose_x_rows(const XRows<GPW>& xr, uint4* region, int lane, int q, int r,
+                                                 uint32_t (&xp)[GPW][16]) {
+  char* base = reinterpret_cast<char*>(region);
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<uint4*>(base + xrow_chunk(4 * u + (lane >> 4), lane & 15)) = xr.v[gi][u];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + xrow_chunk(r, 4 * t + q));
+      xp[gi][4 * t + 0] = v.x;
+      xp[gi][4 * t + 1] = v.y;
+      xp[gi][4 * t + 2] = v.z;
+      xp[gi][4 * t + 3] = v.w;
+    }
+  }
+}
+
 // Number of row tiles this workgroup owns in the grid-stride order.
 __device__ __forceinline__ int tiles_of_wg(int NT) { return (NT - 1 - (int)blockIdx.x) / (int)gridDim.x + 1; }
 
@@ -1156,8 +1206,15 @@ __global__ void __launch_bounds__(64 * MAXW)
   const BlobView bv = int4_view(blob, KT, NT);
   const int T = tiles_of_wg(NT);
 
+  // Up to 8 waves, X comes in coalesced and is transposed through LDS; the
+  // 16-wave shapes (128 registers a lane) load it in operand order directly.
+  constexpr bool kRowsX = MAXW <= 8;
+  XRows<kRowsX ? GPW : 1> xrows;
   uint32_t xa[GPW][16];
-  load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
+  if constexpr (kRowsX)
+    load_x_rows<GPW>(reinterpret_cast<const uint16_t*>(Xw), M, KT * 128, g0, KT, lane, xrows);
+  else
+    load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
   // The activation loads go out first: the first tile's work waits on them.
   __builtin_amdgcn_sched_barrier(0);
   Int4Slot<GPW> ring[D];
@@ -1171,7 +1228,12 @@ __global__ void __launch_bounds__(64 * MAXW)
   __builtin_amdgcn_sched_barrier(0);
   constexpr int C = chunk_gemm<MAXW>();
   __shared__ ChunkStage<float4, C, MAXW, 64> stage;
-  mask_x_pairs<GPW>(r, M, g0, KT, xa);
+  if constexpr (kRowsX) {
+    __shared__ uint4 xt[MAXW][256];  // a wave's transposition region (4 KiB)
+    transpose_x_rows<GPW>(xrows, xt[wave], lane, q, r, xa);
+  } else {
+    mask_x_pairs<GPW>(r, M, g0, KT, xa);
+  }
   f32x4_t cinit[GPW];
   x_row_group_init<GPW>(xa, q, g0, KT, cinit);
   const PairDecode magic = int4_decode();
@@ -1235,8 +1297,15 @@ __global__ void __launch_bounds__(64 * MAXW)
   const typename F::View bv = F::view(blob, KT, NT);
   const int T = tiles_of_wg(NT);
 
+  // Up to 8 waves, X comes in coalesced and is transposed through LDS; the
+  // 16-wave shapes (128 registers a lane) load it in operand order directly.
+  constexpr bool kRowsX = MAXW <= 8;
+  XRows<kRowsX ? GPW : 1> xrows;
   uint32_t xa[GPW][16];
-  load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
+  if constexpr (kRowsX)
+    load_x_rows<GPW>(reinterpret_cast<const uint16_t*>(Xw), M, KT * 128, g0, KT, lane, xrows);
+  else
+    load_x_pairs<GPW>(Xw, r, M, g0, KT, q, xa);
   // The activation loads go out first: the first tile's work waits on them.
   __builtin_amdgcn_sched_barrier(0);
   typename F::template Slot<GPW> ring[D];
@@ -1250,7 +1319,12 @@ __global__ void __launch_bounds__(64 * MAXW)
   __builtin_amdgcn_sched_barrier(0);
   constexpr int C = chunk_gemm<MAXW>();
   __shared__ ChunkStage<float4, C, MAXW, 64> stage;
-  mask_x_pairs<GPW>(r, M, g0, KT, xa);
+  if constexpr (kRowsX) {
+    __shared__ uint4 xt[MAXW][256];  // a wave's transposition region (4 KiB)
+    transpose_x_rows<GPW>(xrows, xt[wave], lane, q, r, xa);
+  } else {
+    mask_x_pairs<GPW>(r, M, g0, KT, xa);
+  }
   const PairDecode one = sign_decode();
 
   RowBest4 best;

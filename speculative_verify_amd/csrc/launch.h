@@ -98,8 +98,11 @@ inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* 
   s->gpw = s->KT <= 8 ? 1 : s->KT <= 16 ? 2 : 4;
   s->waves = (s->KT + s->gpw - 1) / s->gpw;
   s->waves = (s->waves + wave_quantum - 1) / wave_quantum * wave_quantum;
-  // SVQ_WG_PER_CU / SVQ_PIPE_DEPTH override the preferences (for tuning runs).
-  const int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
+  // SVQ_WG_PER_CU / SVQ_PIPE_DEPTH / SVQ_GRID_MAX override the preferences
+  // (for tuning runs).
+  int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
+  const int gmax = env_int("SVQ_GRID_MAX", 1, 1 << 20, want);
+  if (gmax < want) want = gmax;
   s->grid = s->NT < want ? s->NT : want;
   const int tmin = s->NT / s->grid;
   const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 6, pref.max_depth);
