@@ -92,7 +92,7 @@ enum {
 
 #define SVQ_GROUP 128     /* the only supported group size */
 #define SVQ_MAX_M 16      /* rows of a verify block (heads, acceptance) */
-#define SVQ_MAX_M_GEMM 64 /* rows of X a gemm_smallm_w4a16 call takes */
+#define SVQ_MAX_M_GEMM 64 /* rows of X a gemm_smallm_* call takes */
 #define SVQ_MAX_P 6       /* sign planes per weight */
 #define SVQ_MAX_K 8192    /* largest input dimension the kernels accept */
 
@@ -260,7 +260,8 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
 
 /*
  * gemm_smallm_binplane -- DEVICE pointers, asynchronous on `stream`.
- * Y[m][n] = the binary-plane result for row m of X, M in 1..16.
+ * Y[m][n] = the binary-plane result for row m of X, M in 1..64 (above 16
+ * rows, one pass of the M <= 16 kernel per 16-row block of X).
  */
 int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                          int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,
@@ -281,9 +282,10 @@ int gemv_sa(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
 
 /*
  * gemm_smallm_sa -- DEVICE pointers, asynchronous on `stream`.
- * Y[m][n] = the sa* result for row m of X, M in 1..16 (the verify pass over
- * a drafted block, as gemm_smallm_w4a16).  Errors: as gemv_sa, plus SHAPE
- * for M outside 1..16.
+ * Y[m][n] = the sa* result for row m of X, M in 1..64 (the verify pass over
+ * a drafted block, as gemm_smallm_w4a16; the README's batches below 64 run
+ * its quantized mat-mul; above 16 rows, one pass of the M <= 16 kernel per
+ * 16-row block of X).  Errors: as gemv_sa, plus SHAPE for M outside 1..64.
  */
 int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                    int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,

@@ -217,13 +217,13 @@ constexpr int kMaxDepthSa = 3;
 
 // Argument checks of the sa* entry points; the rest as check_linear.
 inline int check_sa(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N,
-                    int64_t K, int32_t G, int32_t P) {
+                    int64_t K, int32_t G, int32_t P, int32_t max_m = SVQ_MAX_M) {
   svq::clear_error();
   if (G != 64 && G != 128 && G != 256)
     return svq::fail(SVQ_ERR_SHAPE, "%s: group size must be 64, 128 or 256 (got %d)", fn, G);
   if (K % 256) return svq::fail(SVQ_ERR_SHAPE, "%s: K=%lld must be a multiple of 256", fn, (long long)K);
   if (P < 2 || P > SVQ_MAX_P) return svq::fail(SVQ_ERR_SHAPE, "%s: P=%d must be in 2..6", fn, P);
-  return check_linear(fn, packed, x, y, M, N, K, SVQ_GROUP, P);
+  return check_linear(fn, packed, x, y, M, N, K, SVQ_GROUP, P, max_m);
 }
 
 // Argument checks shared by the head entry points (P = 0: INT4 weights;

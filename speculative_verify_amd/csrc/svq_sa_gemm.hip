@@ -15,23 +15,30 @@ extern "C" {
 
 int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
                    int32_t G, int32_t P, void* stream) {
-  if (int rc = check_sa("gemm_smallm_sa", packed, X, Y, M, N, K, G, P)) return rc;
+  if (int rc = check_sa("gemm_smallm_sa", packed, X, Y, M, N, K, G, P, SVQ_MAX_M_GEMM)) return rc;
   Shape sh;
   if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  dispatch_group(G, [&](auto Gc) {
-    dispatch_p(P, [&](auto Pc) {
-      if constexpr (decltype(Pc)::value >= 2) {
-        using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
-        dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
-          hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                             st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
-        });
-      }
+  // Blocks above 16 rows: one launch per 16-row block of X (the same sum per
+  // row; the weights are read once per block).
+  for (int32_t m0 = 0; m0 < M; m0 += SVQ_MAX_M) {
+    const int Mb = M - m0 < SVQ_MAX_M ? M - m0 : SVQ_MAX_M;
+    const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X + (size_t)m0 * K);
+    uint16_t* Yb = Y + (size_t)m0 * N;
+    dispatch_group(G, [&](auto Gc) {
+      dispatch_p(P, [&](auto Pc) {
+        if constexpr (decltype(Pc)::value >= 2) {
+          using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
+          dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
+            hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves),
+                               0, st, packed, Xw, Yb, (uint8_t*)nullptr, HeadOut{}, Mb, (int)N, sh.KT, sh.NT);
+          });
+        }
+      });
     });
-  });
-  return launched("gemm_smallm_sa");
+    if (int rc = launched("gemm_smallm_sa")) return rc;
+  }
+  return SVQ_OK;
 }
 
 }  // extern "C"

@@ -269,7 +269,7 @@ def test_gemm_wide_k(M, N, K):
 # Blocks of 16 < M <= 64 rows (the kernel that streams X with the weights).
 
 @pytest.mark.parametrize("M", [17, 20, 24, 31, 32, 33, 40, 47, 48, 56, 63, 64])
-def test_gemm_w4a16_midm_ragged(M):
+def test_gemm_w4a16_midm_ragged(M):  # "midm": 16 < M <= 64
     rng = np.random.default_rng(300 + M)
     N, K = 1000 + 37 * M, 1152
     codes, scales = synth.int4_weights(rng, N, K)
@@ -302,6 +302,22 @@ def test_gemm_w4a16_midm_many_blocks_per_workgroup():
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(N - 70, N), rng.integers(0, N, 600)]))
     Y, A = oracle.linear_w4a16(codes[rows], scales[rows], X)
     check_close(got[:, rows], Y, A, "M=64 N=33000 sample")
+
+
+@pytest.mark.parametrize("M,N,K,P", [(17, 300, 512, 3), (40, 1000, 1024, 2), (64, 4096, 4096, 3), (64, 77, 2048, 6)])
+def test_gemm_planes_midm(M, N, K, P):
+    # Sign planes (fp16 alphas and sa* codes) above 16 rows: one pass of the
+    # M <= 16 kernel per 16-row block, each row against the oracle.
+    rng = np.random.default_rng(M * 7 + N + K + P)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_binplane(signs, alpha, X)
+    print(f"gemm_smallm_binplane M={M} N={N} K={K} P={P}", flush=True)
+    check_close(run_gemm_binplane(signs, alpha, X), Y, A, f"binplane M={M}")
+    G = (64, 128, 256)[M % 3]
+    s2, codes, d = synth.sa_weights(rng, N, K, max(P, 2), G)
+    Y, A = oracle.linear_sa(s2, codes, d, X, G=G)
+    check_close(run_gemm_sa(s2, codes, d, X, G), Y, A, f"sa M={M} G={G}")
 
 
 @pytest.mark.parametrize("M", [33, 64])
