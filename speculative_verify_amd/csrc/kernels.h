@@ -445,9 +445,10 @@ __device__ __forceinline__ void load_sa_tile(SaSlot<GPW, P, G>& sl, const SaView
   load_run<GPW >= 4 ? 4 : 2>(b.d, ((uint32_t)(row * (b.KT4 / 2) + g0 / 2) * 2u) | oob, &sl.d);
 }
 
-// Activation staging for the M <= 16 mat-muls (see load_x_pairs above).  Loading
-// xp directly gives the 16 lanes of a quarter-wave 16 different rows, i.e. 16
-// cache lines per quarter; instead a quarter-wave loads one row's 256 bytes
+// Activation staging for the 8-wave M <= 16 mat-muls (the 16-wave shapes,
+// with 128 registers a lane, keep load_x_pairs above).  Loading xp directly
+// gives the 16 lanes of a quarter-wave 16 different rows, i.e. 16 cache
+// lines per quarter; instead a quarter-wave loads one row's 256 bytes
 // of a column tile (lane: row 4 u + lane / 16, 16-byte chunk lane % 16), and
 // the wave transposes through a private 4 KiB LDS region, one column tile at
 // a time, with the chunks of row p XOR-swizzled by p mod 16 so that neither
@@ -473,6 +474,8 @@ __device__ __forceinline__ void load_x_rows(const uint16_t* __restrict__ X, int 
     }
 }
 
+// Byte offset of 16-byte chunk c of row p in a transposition region of
+// 256-byte rows (chunk index XOR-swizzled by the row).
 __device__ __forceinline__ uint32_t xrow_chunk(int p, int c) { return (uint32_t)(p * 256 + ((c ^ (p & 15)) << 4)); }
 
 template <int GPW>

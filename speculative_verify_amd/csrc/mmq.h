@@ -45,9 +45,6 @@ struct MmqW {
   uint32_t s[R];  // bf16 scale of (row 16 rt + r, group g) in the low half
 };
 
-// Byte offset of 16-byte chunk c of row p in a wave's X buffer.
-__device__ __forceinline__ uint32_t mmq_chunk(int p, int c) { return (uint32_t)(p * 256 + ((c ^ (p & 15)) << 4)); }
-
 template <int MT, int R, int D>
 __global__ void __launch_bounds__(64 * kMmqWaves)
     k_gemm_mmq_w4a16(const uint8_t* __restrict__ blob, const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
@@ -115,7 +112,7 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
       if (h < nm)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          *reinterpret_cast<uint4*>(xb + mmq_chunk(16 * (mt0 + h) + 4 * v + (lane >> 4), lane & 15)) = xh[h][v];
+          *reinterpret_cast<uint4*>(xb + xrow_chunk(16 * (mt0 + h) + 4 * v + (lane >> 4), lane & 15)) = xh[h][v];
   };
   auto load_w = [&](const Cursor& u, MmqW<R>& w) {
     const uint32_t oob = step_oob(u);
@@ -187,7 +184,7 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
         uint32_t a[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint4 v = *reinterpret_cast<const uint4*>(xb + mmq_chunk(16 * mi + r, 4 * t + q));
+          const uint4 v = *reinterpret_cast<const uint4*>(xb + xrow_chunk(16 * mi + r, 4 * t + q));
           a[t][0] = v.x;
           a[t][1] = v.y;
           a[t][2] = v.z;
