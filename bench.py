@@ -233,9 +233,9 @@ def cpu_baseline(target_s: float = 12.0):
               ("head", 16, 32768, 0)]
     rng = np.random.default_rng(7)
 
-    def make(frac):
+    def make(frac, which=shapes):
         jobs = []
-        for kind, M, N, P in shapes:
+        for kind, M, N, P in which:
             n = max(16, int(N * frac) // 16 * 16)
             X = synth.activations(rng, M, K)
             if kind == "binplane":
@@ -270,6 +270,18 @@ def cpu_baseline(target_s: float = 12.0):
         reps, frac = min(8, math.ceil(frac)), 1.0
     jobs = make(frac)
     nbytes, secs = run(jobs, reps)
+    del jobs
+    # One thread, on the mat-vec and verify shapes only (about 3 s).
+    threads = oracle.num_threads()
+    lin = shapes[:6]
+    oracle.set_num_threads(1)
+    try:
+        f1 = 1.0 / 512
+        _, s1 = run(make(f1, lin))
+        f1 = min(1.0, f1 * 3.0 / max(s1, 1e-3))
+        b1, t1 = run(make(f1, lin))
+    finally:
+        oracle.set_num_threads(threads)
     return {
         "value": round(nbytes / secs / 1e9, 4),
         "unit": "GB/s",
@@ -278,6 +290,9 @@ def cpu_baseline(target_s: float = 12.0):
         "sample": (f"each step call on its first {frac:.2%} of output rows (at least 16), same K, M "
                    f"and value distributions, timed {reps}x: {nbytes / 1e6:.1f} MB of weights in "
                    f"{secs:.1f} s of oracle time"),
+        "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "sample": (f"the W4A16 and P3 mat-vec and M=16 verify calls on their first "
+                                     f"{f1:.2%} of output rows: {b1 / 1e6:.1f} MB in {t1:.1f} s")},
     }
 
 
@@ -346,9 +361,22 @@ def main():
         torch.cuda.synchronize()
         us = c_begin.elapsed_time(c_end) * 1e3 / args.steps
         del rot
+        # Hot: the same launches on one copy of the inputs, which stays in
+        # the caches between launches when it fits (a lower bound on the
+        # kernel's own latency and arithmetic, not a bandwidth figure).
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        c_begin.record(stream)
+        for _ in range(args.steps):
+            fn()
+        c_end.record(stream)
+        torch.cuda.synchronize()
+        hot_us = c_begin.elapsed_time(c_end) * 1e3 / args.steps
         gbps = nbytes / (us * 1e-6) / 1e9
         kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(gbps, 1),
-                         "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "input_copies": copies}
+                         "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "input_copies": copies,
+                         "hot_us": round(hot_us, 3)}
     extra_names = {c[0] for c in extra}
     for name in extra_names:
         kernels[name]["in_step"] = False

@@ -39,6 +39,7 @@
 #include <cfloat>
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "svq.h"
 
@@ -128,6 +129,57 @@ __device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i, const PairDecod
 // bf16 pair (b_even, b_odd) in {-1, +1} for pair ip = 4t + i of a sign dword.
 __device__ __forceinline__ uint32_t sign_pair(uint32_t w, int ip, const PairDecode& d) {
   return ((w << (15 - ip)) & d.mask) | d.orv;
+}
+
+// Sign-plane MFMA operands, one AND-OR per bf16 pair.  A sign bit b is not
+// moved to the bf16 sign position; it stays where a view of the dword puts
+// it, at bit 4, 5, 6 or 7 of a half (or 15), over a base C chosen so that
+// setting the bit adds exactly 2: C = 16, 8, 4 (mantissa bits 4-6, one ulp
+// of C being 2^-3 C, 2^-2 C, 2^-1 C) and C = 2 (exponent LSB, 2 -> 4).  At
+// bit 15 the pair is the plain +-1 and its activations enter negated.  Every
+// product is then c x + 2 b x with c in {16, 8, 4, 2, -1} known per
+// position, so a chain started at -(sum x + sum c x) over the group ends at
+// -(sum of (1 - 2b) x): minus the plane's signed sum.  Four views (w, w << 4,
+// w >> 4, w >> 8) cover the 16 pairs: 3 shifts and 16 AND-ORs per dword.
+struct PlaneDecode {
+  uint32_t m4, m5, m6, m7, m15;  // SGPR masks: bit p of both halves
+  uint32_t c4, c5, c6, c7, c15;  // VGPR base pairs
+};
+
+__device__ __forceinline__ PlaneDecode plane_decode() {
+  return PlaneDecode{opaque_sgpr<0x00100010u>(), opaque_sgpr<0x00200020u>(), opaque_sgpr<0x00400040u>(),
+                     opaque_sgpr<0x00800080u>(), opaque_sgpr<0x80008000u>(), opaque_vgpr<0x41804180u>(),
+                     opaque_vgpr<0x41004100u>(), opaque_vgpr<0x40804080u>(), opaque_vgpr<0x40004000u>(),
+                     opaque_vgpr<kOnePair>()};
+}
+
+// B operands of the four 32-wide k blocks of sign dword w: b[t][i] is pair
+// ip = 4t + i (bits ip and 16 + ip of w).
+__device__ __forceinline__ void plane_operands(uint32_t w, const PlaneDecode& d, uint32_t (&b)[4][4]) {
+  const uint32_t v1 = w << 4, v2 = w >> 4, v3 = w >> 8;
+  b[0][0] = (v1 & d.m4) | d.c4;  // pairs 0-3 at bits 4-7 of w << 4
+  b[0][1] = (v1 & d.m5) | d.c5;
+  b[0][2] = (v1 & d.m6) | d.c6;
+  b[0][3] = (v1 & d.m7) | d.c7;
+  b[1][0] = (w & d.m4) | d.c4;  // pairs 4-7 at bits 4-7 of w
+  b[1][1] = (w & d.m5) | d.c5;
+  b[1][2] = (w & d.m6) | d.c6;
+  b[1][3] = (w & d.m7) | d.c7;
+  b[2][0] = (v2 & d.m4) | d.c4;  // pairs 8-10 at bits 4-6 of w >> 4
+  b[2][1] = (v2 & d.m5) | d.c5;
+  b[2][2] = (v2 & d.m6) | d.c6;
+  b[2][3] = (v1 & d.m15) | d.c15;  // pair 11 at bit 15 of w << 4
+  b[3][0] = (v3 & d.m4) | d.c4;  // pairs 12-14 at bits 4-6 of w >> 8
+  b[3][1] = (v3 & d.m5) | d.c5;
+  b[3][2] = (v3 & d.m6) | d.c6;
+  b[3][3] = (w & d.m15) | d.c15;  // pair 15 at bit 15 of w
+}
+
+// 1 + c per pair position ip (0 at the two +-1 positions, whose activations
+// are negated), as bf16 pairs: the weights of the chain start.
+__device__ __forceinline__ constexpr uint32_t plane_init_weight(int ip) {
+  constexpr uint32_t w[4] = {0x41884188u, 0x41104110u, 0x40A040A0u, 0x40404040u};  // 17, 9, 5, 3
+  return (ip & 3) == 3 ? (ip < 8 ? w[3] : 0u) : w[ip & 3];
 }
 
 // Sum over the four lanes r, r+16, r+32, r+48 of a wave (the q index), via
@@ -940,22 +992,69 @@ struct PlaneFmt {
                                                   const PairDecode& one) {
     return binplane_tile_partial<GPW, P>(sl, xp, one);
   }
-  // One accumulator chain per (column tile, plane), scaled by its alpha.
+  // MFMA tiles.  Up to eight waves (256 registers a lane): the activations
+  // with the pairs at the +-1 positions negated, and per group the chain
+  // start -(sum x + sum c x) of the rows 4q + i this lane's results hold
+  // (see plane_operands).  The 16-wave shapes (128 registers) keep the two
+  // instructions per pair of sign_pair and chains started at zero.
   template <int GPW>
+  struct MmaFast {
+    f32x4_t cinit[GPW];
+    PlaneDecode d;
+  };
+  struct MmaLean {
+    PairDecode one;
+  };
+  template <int GPW, int MAXW>
+  using MmaX = std::conditional_t<(MAXW <= 8), MmaFast<GPW>, MmaLean>;
+
+  template <int GPW, int MAXW>
+  static __device__ __forceinline__ void prepare_mma(uint32_t (&xa)[GPW][16], int q, MmaX<GPW, MAXW>& mx) {
+    if constexpr (MAXW <= 8) {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        xa[gi][11] ^= 0x80008000u;
+        xa[gi][15] ^= 0x80008000u;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (plane_init_weight(j) != 0u) s = dot2(xa[gi][j], plane_init_weight(j), s);
+        const float srow = sum_over_q(s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx.cinit[gi][i] = -__shfl(srow, 4 * q + i);
+      }
+      mx.d = plane_decode();
+    } else {
+      mx.one = sign_decode();
+    }
+  }
+  // One accumulator chain per (column tile, plane), scaled by its alpha.  In
+  // the fast form each chain ends at minus the plane's signed sum, so the
+  // weighted total is negated once.
+  template <int GPW, int MAXW>
   static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
-                                               const PairDecode& one) {
+                                               const MmaX<GPW, MAXW>& mx) {
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const uint32_t wp = sl.w[gi][p];
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t c;
+        if constexpr (MAXW <= 8) {
+          uint32_t b[4][4];
+          plane_operands(sl.w[gi][p], mx.d, b);
+          c = mx.cinit[gi];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, one), sign_pair(wp, 4 * t + 1, one),
-                                  sign_pair(wp, 4 * t + 2, one), sign_pair(wp, 4 * t + 3, one)};
-          c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+          for (int t = 0; t < 4; ++t) c = mfma16x16x32(&xa[gi][4 * t], b[t], c);
+        } else {
+          const uint32_t wp = sl.w[gi][p];
+          c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, mx.one), sign_pair(wp, 4 * t + 1, mx.one),
+                                    sign_pair(wp, 4 * t + 2, mx.one), sign_pair(wp, 4 * t + 3, mx.one)};
+            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+          }
         }
         const float a = sl.a[p].f16(gi);
         yv.x = fmaf(a, c[0], yv.x);
@@ -963,6 +1062,7 @@ struct PlaneFmt {
         yv.z = fmaf(a, c[2], yv.z);
         yv.w = fmaf(a, c[3], yv.w);
       }
+    if constexpr (MAXW <= 8) return make_float4(-yv.x, -yv.y, -yv.z, -yv.w);
     return yv;
   }
 };
@@ -995,9 +1095,18 @@ struct SaFmt {
                                                   const PairDecode& one) {
     return sa_tile_partial<GPW, P, G>(sl, xp, one);
   }
-  template <int GPW>
+  template <int GPW, int MAXW>
+  struct MmaX {
+    PairDecode one;
+  };
+  template <int GPW, int MAXW>
+  static __device__ __forceinline__ void prepare_mma(uint32_t (&)[GPW][16], int, MmaX<GPW, MAXW>& mx) {
+    mx.one = sign_decode();
+  }
+  template <int GPW, int MAXW>
   static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
-                                               const PairDecode& one) {
+                                               const MmaX<GPW, MAXW>& mx) {
+    const PairDecode& one = mx.one;
     constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1328,7 +1437,8 @@ __global__ void __launch_bounds__(64 * MAXW)
   } else {
     mask_x_pairs<GPW>(r, M, g0, KT, xa);
   }
-  const PairDecode one = sign_decode();
+  typename F::template MmaX<GPW, MAXW> mx;
+  F::template prepare_mma<GPW, MAXW>(xa, q, mx);
 
   RowBest4 best;
 #pragma unroll
@@ -1341,7 +1451,7 @@ __global__ void __launch_bounds__(64 * MAXW)
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      const float4 yv = F::template mma<GPW>(ring[j], xa, one);
+      const float4 yv = F::template mma<GPW, MAXW>(ring[j], xa, mx);
       stage.put(i, i < T, wave, lane, yv);
       // Slot j is refilled only after its last use, so it keeps its registers.
       __builtin_amdgcn_sched_barrier(0);

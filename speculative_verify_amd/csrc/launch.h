@@ -211,9 +211,11 @@ constexpr int max_depth_planes(int P) { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
   F, decltype(G)::value, decltype(W)::value,                                                       \
       (decltype(D)::value < max_depth_planes(F::P) ? decltype(D)::value : max_depth_planes(F::P))
 
-// The sa* kernels keep rings of at most three tiles (the plane kernels'
-// measured best; deeper rings are not instantiated for them).
+// The sa* kernels and the sign-plane mat-muls keep rings of at most three
+// tiles (the measured best of the plane kernels; deeper rings would spill
+// registers and are not instantiated for them).
 constexpr int kMaxDepthSa = 3;
+constexpr int kMaxDepthPlanesGemm = 3;
 
 // Argument checks of the sa* entry points; the rest as check_linear.
 inline int check_sa(const char* fn, const void* packed, const void* x, const void* y, int32_t M, int64_t N,

@@ -30,7 +30,7 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
     uint16_t* Yb = Y + (size_t)m0 * N;
     dispatch_p(P, [&](auto Pc) {
       using F = PlaneFmt<decltype(Pc)::value>;
-      dispatch(sh, [&](auto G, auto W, auto D) {
+      dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
         hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
                            packed, Xw, Yb, (uint8_t*)nullptr, HeadOut{}, Mb, (int)N, sh.KT, sh.NT);
       });
@@ -57,7 +57,7 @@ int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   dispatch_p(P, [&](auto Pc) {
     using F = PlaneFmt<decltype(Pc)::value>;
-    dispatch(sh, [&](auto G, auto W, auto D) {
+    dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
                          st, packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
     });
