@@ -1095,45 +1095,110 @@ struct SaFmt {
                                                   const PairDecode& one) {
     return sa_tile_partial<GPW, P, G>(sl, xp, one);
   }
-  template <int GPW, int MAXW>
-  struct MmaX {
+  // MFMA tiles.  Up to eight waves: the sign decode of PlaneFmt (one AND-OR
+  // per pair, chains ending at minus each plane's signed sum over a group,
+  // or over each half of a group at G = 64, where the two halves take their
+  // own codes), each chain weighted by its code and the super-block's sum by
+  // d.  The 16-wave shapes keep the B = a * b pairs: there every plane and
+  // group of a super-block accumulates in one chain that d scales once (a
+  // code a <= 255 is exact in bf16, so a * b * x is an exact product).
+  template <int GPW>
+  struct MmaFast {
+    f32x4_t cinit[GPW][G == 64 ? 2 : 1];
+    PlaneDecode d;
+  };
+  struct MmaLean {
     PairDecode one;
   };
   template <int GPW, int MAXW>
-  static __device__ __forceinline__ void prepare_mma(uint32_t (&)[GPW][16], int, MmaX<GPW, MAXW>& mx) {
-    mx.one = sign_decode();
+  using MmaX = std::conditional_t<(MAXW <= 8), MmaFast<GPW>, MmaLean>;
+
+  template <int GPW, int MAXW>
+  static __device__ __forceinline__ void prepare_mma(uint32_t (&xa)[GPW][16], int q, MmaX<GPW, MAXW>& mx) {
+    if constexpr (MAXW <= 8) {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        xa[gi][11] ^= 0x80008000u;
+        xa[gi][15] ^= 0x80008000u;
+        float s[2] = {0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (plane_init_weight(j) != 0u) s[j >> 3] = dot2(xa[gi][j], plane_init_weight(j), s[j >> 3]);
+#pragma unroll
+        for (int h = 0; h < (G == 64 ? 2 : 1); ++h) {
+          const float srow = sum_over_q(G == 64 ? s[h] : s[0] + s[1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx.cinit[gi][h][i] = -__shfl(srow, 4 * q + i);
+        }
+      }
+      mx.d = plane_decode();
+    } else {
+      mx.one = sign_decode();
+    }
   }
   template <int GPW, int MAXW>
   static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
                                                const MmaX<GPW, MAXW>& mx) {
-    const PairDecode& one = mx.one;
     constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (MAXW <= 8) {
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb < SB; ++sb) {
+        float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
+        for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const uint32_t wp = sl.w[gi][p];
+          for (int p = 0; p < P; ++p) {
+            uint32_t b[4][4];
+            plane_operands(sl.w[gi][p], mx.d, b);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t ap = code_pair(sl.code(p, gi, t));
-            const uint32_t bq[4] = {scaled_sign_pair(wp, 4 * t + 0, one.mask, ap),
-                                    scaled_sign_pair(wp, 4 * t + 1, one.mask, ap),
-                                    scaled_sign_pair(wp, 4 * t + 2, one.mask, ap),
-                                    scaled_sign_pair(wp, 4 * t + 3, one.mask, ap)};
-            c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+            for (int h = 0; h < (G == 64 ? 2 : 1); ++h) {
+              f32x4_t c = mx.cinit[gi][h];
+#pragma unroll
+              for (int t = (G == 64 ? 2 * h : 0); t < (G == 64 ? 2 * h + 2 : 4); ++t)
+                c = mfma16x16x32(&xa[gi][4 * t], b[t], c);
+              const float a = (float)sl.code(p, gi, 2 * h);
+              ys.x = fmaf(a, c[0], ys.x);
+              ys.y = fmaf(a, c[1], ys.y);
+              ys.z = fmaf(a, c[2], ys.z);
+              ys.w = fmaf(a, c[3], ys.w);
+            }
           }
-        }
-      const float d = sl.dscale(2 * sb);
-      yv.x = fmaf(d, c[0], yv.x);
-      yv.y = fmaf(d, c[1], yv.y);
-      yv.z = fmaf(d, c[2], yv.z);
-      yv.w = fmaf(d, c[3], yv.w);
+        const float d = sl.dscale(2 * sb);
+        yv.x = fmaf(d, ys.x, yv.x);
+        yv.y = fmaf(d, ys.y, yv.y);
+        yv.z = fmaf(d, ys.z, yv.z);
+        yv.w = fmaf(d, ys.w, yv.w);
+      }
+      return make_float4(-yv.x, -yv.y, -yv.z, -yv.w);
+    } else {
+      const PairDecode& one = mx.one;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const uint32_t wp = sl.w[gi][p];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t ap = code_pair(sl.code(p, gi, t));
+              const uint32_t bq[4] = {scaled_sign_pair(wp, 4 * t + 0, one.mask, ap),
+                                      scaled_sign_pair(wp, 4 * t + 1, one.mask, ap),
+                                      scaled_sign_pair(wp, 4 * t + 2, one.mask, ap),
+                                      scaled_sign_pair(wp, 4 * t + 3, one.mask, ap)};
+              c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+            }
+          }
+        const float d = sl.dscale(2 * sb);
+        yv.x = fmaf(d, c[0], yv.x);
+        yv.y = fmaf(d, c[1], yv.y);
+        yv.z = fmaf(d, c[2], yv.z);
+        yv.w = fmaf(d, c[3], yv.w);
+      }
+      return yv;
     }
-    return yv;
   }
 };
 
