@@ -299,8 +299,10 @@ def cpu_baseline(target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # About 50 ms of untimed steps: the GPU's clocks settle over tens of
+    # milliseconds of load, and a short warm-up times part of that ramp.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     args = ap.parse_args()
