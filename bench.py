@@ -356,12 +356,17 @@ def main():
             f()
         torch.cuda.synchronize()
         c_begin, c_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c_begin.record(stream)
-        for i in range(args.steps):
-            rot[i % copies]()
-        c_end.record(stream)
-        torch.cuda.synchronize()
-        us = c_begin.elapsed_time(c_end) * 1e3 / args.steps
+        # Five timed rounds of K launches; the median round is reported (one
+        # round alone varies by a few percent from run to run).
+        rounds = []
+        for _ in range(5):
+            c_begin.record(stream)
+            for i in range(args.steps):
+                rot[i % copies]()
+            c_end.record(stream)
+            torch.cuda.synchronize()
+            rounds.append(c_begin.elapsed_time(c_end) * 1e3 / args.steps)
+        us = sorted(rounds)[2]
         del rot
         # Hot: the same launches on one copy of the inputs, which stays in
         # the caches between launches when it fits (a lower bound on the
