@@ -245,32 +245,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Activation staging for the M = 1 kernels.  The 16 lanes of a row q all
-// need the same 16 pairs (their k sub-range), so instead of loading them 16
-// times over, lane (q, r) loads only the pair with (t, i) = (r/4, r%4) -- a
-// wave reads each of a group's 64 pairs exactly once -- and DPP row_newbcast
-// then copies pair j of the row to every lane of the row.
-template <int GPW>
-__device__ __forceinline__ void load_x_own(const uint32_t* __restrict__ xw, int g0, int KT, int q, int r,
-                                           uint32_t (&xo)[GPW]) {
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
-    xo[gi] = xw[64 * min(g0 + gi, KT - 1) + 16 * (r >> 2) + 4 * q + (r & 3)];
-}
-
-template <int GPW>
-__device__ __forceinline__ void expand_x(const uint32_t (&xo)[GPW], int g0, int KT, uint32_t (&xp)[GPW][16]) {
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const bool live = g0 + gi < KT;
-    static_for<0, 16>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      const uint32_t v = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x150 + j, 0xF, 0xF, false);  // row_newbcast:j
-      xp[gi][j] = live ? v : 0u;
-    });
-  }
-}
-
 // Sum of the 32 activations a lane holds for each of its groups.
 template <int GPW>
 __device__ __forceinline__ void lane_group_sums(const uint32_t (&xp)[GPW][16], float (&xs)[GPW]) {
@@ -314,6 +288,33 @@ __device__ __forceinline__ uint4 ld_stream16(__amdgpu_buffer_rsrc_t r, uint32_t 
 
 __device__ __forceinline__ uint32_t ld_stream4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAuxStream);
+}
+
+// Activation staging for the M = 1 kernels.  The 16 lanes of a row q all
+// need the same 16 pairs (their k sub-range), so instead of loading them 16
+// times over, lane (q, r) loads only the pair with (t, i) = (r/4, r%4) -- a
+// wave reads each of a group's 64 pairs exactly once -- and DPP row_newbcast
+// then copies pair j of the row to every lane of the row.  Groups past K
+// read zero (buffer offset bit 31), so nothing is masked afterwards.
+template <int GPW>
+__device__ __forceinline__ void load_x_own(const uint32_t* __restrict__ xw, int g0, int KT, int q, int r,
+                                           uint32_t (&xo)[GPW]) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(xw, (uint32_t)KT * 256u);
+  const uint32_t lo = (uint32_t)(16 * (r >> 2) + 4 * q + (r & 3)) * 4u;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+    xo[gi] = __builtin_amdgcn_raw_buffer_load_b32(rs, (lo + 256u * (uint32_t)(g0 + gi)) | oob_bit(g0 + gi < KT), 0, 0);
+}
+
+template <int GPW>
+__device__ __forceinline__ void expand_x(const uint32_t (&xo)[GPW], uint32_t (&xp)[GPW][16]) {
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    static_for<0, 16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      xp[gi][j] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x150 + j, 0xF, 0xF, false);  // row_newbcast:j
+    });
+  }
 }
 
 // GPW consecutive 16-bit scale entries, kept as the raw dwords one load
@@ -803,7 +804,7 @@ __global__ void __launch_bounds__(64 * MAXW)
   __builtin_amdgcn_sched_barrier(0);
   __shared__ ChunkStage<float, kChunkGemv, MAXW, 16> stage;
   uint32_t xp[GPW][16];
-  expand_x<GPW>(xo, g0, KT, xp);
+  expand_x<GPW>(xo, xp);
   float nxs[GPW];
   lane_group_sums<GPW>(xp, nxs);
 #pragma unroll
@@ -871,18 +872,29 @@ struct SignLut {
 
 template <int GPW>
 __device__ __forceinline__ void build_sign_lut(SignLut<GPW>& lut, const uint32_t (&xp)[GPW][16], int q, int r) {
-  const uint32_t f0 = (uint32_t)(r & 1) << 31, f1 = (uint32_t)((r >> 1) & 1) << 31;
-  const uint32_t f2 = (uint32_t)((r >> 2) & 1) << 31, f3 = (uint32_t)((r >> 3) & 1) << 31;
+  // The first term's sign is an XOR into the widened activation; for the
+  // other three, bf16 pairs (s_i, 0) and (0, s_i) (s_i = -1 where bit i of
+  // the entry index r is set) let one dot2 add the even (odd) activation of
+  // a pair with its sign: four instructions per entry.
+  const uint32_t f0 = (uint32_t)(r & 1) << 31;
+  uint32_t se[4], so[4];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    se[i] = ((r >> i) & 1) ? 0xBF80u : 0x3F80u;
+    so[i] = se[i] << 16;
+  }
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t* pr = &xp[gi][4 * t];
-      // even k's: the pairs' low halves; odd k's: the high halves.
-      const float e0 = __uint_as_float((pr[0] << 16) ^ f0) + __uint_as_float((pr[1] << 16) ^ f1) +
-                       __uint_as_float((pr[2] << 16) ^ f2) + __uint_as_float((pr[3] << 16) ^ f3);
-      const float e1 = __uint_as_float((pr[0] & 0xFFFF0000u) ^ f0) + __uint_as_float((pr[1] & 0xFFFF0000u) ^ f1) +
-                       __uint_as_float((pr[2] & 0xFFFF0000u) ^ f2) + __uint_as_float((pr[3] & 0xFFFF0000u) ^ f3);
+      float e0 = __uint_as_float((pr[0] << 16) ^ f0);
+      float e1 = __uint_as_float((pr[0] & 0xFFFF0000u) ^ f0);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        e0 = dot2(pr[i], se[i], e0);
+        e1 = dot2(pr[i], so[i], e1);
+      }
       lut.e[gi][t][0][16 * q + r] = e0;
       lut.e[gi][t][1][16 * q + r] = e1;
     }
@@ -1238,7 +1250,7 @@ __global__ void __launch_bounds__(64 * MAXW)
   __shared__ ChunkStage<float, C, MAXW, 16> stage;
   __shared__ SignLut<kLut ? GPW : 1> luts[kLut ? MAXW : 1];
   uint32_t xp[GPW][16];
-  expand_x<GPW>(xo, g0, KT, xp);
+  expand_x<GPW>(xo, xp);
   const PairDecode one = sign_decode();
   if constexpr (kLut) build_sign_lut<GPW>(luts[wave], xp, q, r);
   // Opaque copy: the compiler would otherwise turn the OR of disjoint bits in
