@@ -64,18 +64,32 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
     MmqShape sh;
     if (int rc = plan_mmq(N, M, &sh)) return rc;
     const int KT = (int)(K / 128), NT = (int)((N + 15) / 16);
+    // Every workgroup runs a multiple of CK steps (CK column tiles per wave
+    // and block), and the unrolled ring loop runs whole rounds of D steps:
+    // a depth of 3 is kept only where CK is a multiple of 3 (or of neither 2
+    // nor 3), so no round ends in steps on empty tiles.
+    const int CK = (KT + kMmqWaves - 1) / kMmqWaves;
+    const bool three = CK % 3 == 0 || CK % 2 != 0;
+    auto launch = [&](auto MTc, auto Rc, auto Dc) {
+      hipLaunchKernelGGL((k_gemm_mmq_w4a16<decltype(MTc)::value, decltype(Rc)::value, decltype(Dc)::value>),
+                         dim3(sh.grid), dim3(64 * kMmqWaves), 0, st, packed, X, Y, M, (int)N, (int)K, KT, NT);
+    };
     dispatch_r(sh.R, [&](auto Rc) {
       constexpr int R = decltype(Rc)::value;
-      // The deepest weight ring that stays in registers for the block height.
-      if (M <= 32)
-        hipLaunchKernelGGL((k_gemm_mmq_w4a16<2, R, R == 4 ? 2 : 3>), dim3(sh.grid), dim3(64 * kMmqWaves), 0, st,
-                           packed, X, Y, M, (int)N, (int)K, KT, NT);
-      else if (M <= 48)
-        hipLaunchKernelGGL((k_gemm_mmq_w4a16<3, R < 4 ? R : 3, R >= 3 ? 2 : 3>), dim3(sh.grid),
-                           dim3(64 * kMmqWaves), 0, st, packed, X, Y, M, (int)N, (int)K, KT, NT);
-      else
-        hipLaunchKernelGGL((k_gemm_mmq_w4a16<4, R < 4 ? R : 3, R >= 3 ? 2 : 3>), dim3(sh.grid),
-                           dim3(64 * kMmqWaves), 0, st, packed, X, Y, M, (int)N, (int)K, KT, NT);
+      // The deepest weight ring that stays in registers for the block height
+      // (3 tiles, or 2), where the step count allows it.
+      if (M <= 32) {
+        if (R != 4 && three) launch(ic<2>{}, Rc, ic<3>{});
+        else launch(ic<2>{}, Rc, ic<2>{});
+      } else {
+        constexpr int R3 = R < 4 ? R : 3;
+        auto by_m = [&](auto MTc) {
+          if (R < 3 && three) launch(MTc, ic<R3>{}, ic<3>{});
+          else launch(MTc, ic<R3>{}, ic<2>{});
+        };
+        if (M <= 48) by_m(ic<3>{});
+        else by_m(ic<4>{});
+      }
     });
     return launched("gemm_smallm_w4a16");
   }
