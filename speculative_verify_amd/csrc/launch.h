@@ -80,15 +80,19 @@ inline int env_int(const char* name, int lo, int hi, int dflt) {
 // workgroup per CU; a ring of 2 tiles already keeps more bytes in flight
 // than the memory system's bandwidth-latency product, and deeper rings were
 // slower for the W4A16 kernels (the sign-plane verify kernel, with more
-// arithmetic per byte, gains a little from 3).
+// arithmetic per byte, gains a little from 3).  Workgroups of the M <= 16
+// mat-muls that own at most `shallow` tiles run without a ring (depth 1):
+// at three tiles each (N = 12288) that was 6% faster for the sign planes,
+// 3% for sa* and 1% for W4A16 than rings of 2 or 3 (the prefetch of later
+// tiles delays the first tile's activations and weights).
 struct LaunchPref {
-  int wgs_per_cu, max_depth;
+  int wgs_per_cu, max_depth, shallow;
 };
-constexpr LaunchPref kPrefGemv = {2, 2};
-constexpr LaunchPref kPrefGemmW4 = {1, 2};
-constexpr LaunchPref kPrefGemmPlanes = {1, 3};
-constexpr LaunchPref kPrefHeadM1 = {1, 2};
-constexpr LaunchPref kPrefHeadM16 = {1, 2};
+constexpr LaunchPref kPrefGemv = {2, 2, 0};
+constexpr LaunchPref kPrefGemmW4 = {1, 2, 3};
+constexpr LaunchPref kPrefGemmPlanes = {1, 3, 3};
+constexpr LaunchPref kPrefHeadM1 = {1, 2, 0};
+constexpr LaunchPref kPrefHeadM16 = {1, 2, 0};
 
 inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* s) {
   int cus = 0;
@@ -106,7 +110,8 @@ inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* 
   s->grid = s->NT < want ? s->NT : want;
   const int tmin = s->NT / s->grid;
   const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 6, pref.max_depth);
-  s->depth = tmin < 1 ? 1 : tmin > dmax ? dmax : tmin;
+  const bool shallow = tmin <= pref.shallow && env_int("SVQ_PIPE_DEPTH", 1, 6, 0) == 0;
+  s->depth = tmin < 1 || shallow ? 1 : tmin > dmax ? dmax : tmin;
   return SVQ_OK;
 }
 
