@@ -29,9 +29,11 @@
 // dot products see 136 + c exactly; the group sum of x times 136 is taken
 // back out before the group scale is applied in fp32.  A sign bit becomes the
 // bf16 value +1 or -1 (0x3F80 with the sign bit set for b = -1) with one
-// shift and one AND-OR.  Neither s*c nor sum_p alpha_p b_p is ever rounded to
-// bf16; the scales are applied per group in fp32, and the output is rounded
-// to bf16 once, to nearest even.
+// shift and one AND-OR; the M <= 16 sign-plane tiles skip the shift (see
+// plane_operands) and the M = 1 ones read precomputed signed sums from LDS.
+// Neither s*c nor sum_p alpha_p b_p is ever rounded to bf16; the scales are
+// applied per group in fp32, and the output is rounded to bf16 once, to
+// nearest even.
 #pragma once
 
 #include <hip/hip_runtime.h>
