@@ -682,3 +682,61 @@ def test_lmhead_binplane_planted(M, N, K, P):
     assert np.array_equal(idx.cpu().numpy(), r["out"])
     check_close(mx.double().cpu().numpy(), r["zmax"], r["amax"], "binplane head max")
     assert int(ws.count_nonzero().item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# Launch-shape independence: the workgroup count, the ring depth and the
+# workgroups per CU change which workgroup computes a tile and how far ahead
+# it loads, never the arithmetic (each tile's per-wave partials are combined
+# in wave order), so every output must be bit-identical under every setting
+# of the tuning knobs.
+
+_KNOBS = [{}, {"SVQ_WG_PER_CU": "1"}, {"SVQ_WG_PER_CU": "3"}, {"SVQ_PIPE_DEPTH": "1"}, {"SVQ_PIPE_DEPTH": "3"},
+          {"SVQ_GRID_MAX": "37"}]
+
+
+def _under_knobs(fn, monkeypatch):
+    outs = []
+    for knobs in _KNOBS:
+        for k in ("SVQ_WG_PER_CU", "SVQ_PIPE_DEPTH", "SVQ_GRID_MAX"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in knobs.items():
+            monkeypatch.setenv(k, v)
+        outs.append((knobs, fn()))
+        torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("kind,M", [("w4a16", 1), ("w4a16", 16), ("w4a16", 5), ("binplane", 1), ("binplane", 16),
+                                    ("sa", 1), ("sa", 16), ("head", 1), ("head", 16)])
+def test_outputs_do_not_depend_on_launch_shape(kind, M, monkeypatch):
+    N, K, P, G = 5008, 4096, 3, 64  # 313 row tiles (the device generators need whole tiles)
+    X = synth.device_activations(M, K, 11).view(torch.int16)
+    if kind in ("w4a16", "head"):
+        blob = synth.device_int4_blob(N, K, 12)
+    elif kind == "binplane":
+        blob = synth.device_binplane_blob(N, K, P, 13)
+    else:
+        blob = synth.device_sa_blob(N, K, P, G, 14)
+
+    def call():
+        if kind == "head":
+            idx = torch.empty(M, dtype=torch.int32, device="cuda")
+            mx = torch.empty(M, dtype=torch.float32, device="cuda")
+            ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+            svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
+            return torch.cat([idx.view(torch.int32), mx.view(torch.int32)]).cpu().numpy()
+        Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        if kind == "w4a16":
+            (svq.gemv_w4a16(blob, X, Y, N, K) if M == 1 else svq.gemm_smallm_w4a16(blob, X, Y, M, N, K))
+        elif kind == "binplane":
+            (svq.gemv_binplane(blob, X, Y, N, K, P) if M == 1 else svq.gemm_smallm_binplane(blob, X, Y, M, N, K, P))
+        else:
+            (svq.gemv_sa(blob, X, Y, N, K, P, G) if M == 1 else svq.gemm_smallm_sa(blob, X, Y, M, N, K, P, G))
+        return Y.cpu().numpy()
+
+    print(f"launch-shape independence {kind} M={M}", flush=True)
+    outs = _under_knobs(call, monkeypatch)
+    ref = outs[0][1]
+    for knobs, out in outs[1:]:
+        assert np.array_equal(out, ref), f"{kind} M={M}: outputs differ under {knobs}"
