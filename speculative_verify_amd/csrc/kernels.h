@@ -177,6 +177,23 @@ __device__ __forceinline__ void plane_operands(uint32_t w, const PlaneDecode& d,
   b[3][3] = (w & d.m15) | d.c15;  // pair 15 at bit 15 of w
 }
 
+// The same operands one 32-wide k block at a time, from the four views of
+// the dword (w, w << 4, w >> 4, w >> 8), so that several dwords' MFMA
+// chains can be interleaved without holding every decoded operand.
+struct PlaneViews {
+  uint32_t w, v1, v2, v3;
+};
+
+__device__ __forceinline__ PlaneViews plane_views(uint32_t w) { return PlaneViews{w, w << 4, w >> 4, w >> 8}; }
+
+__device__ __forceinline__ void plane_operands_t(const PlaneViews& v, int t, const PlaneDecode& d, uint32_t (&b)[4]) {
+  const uint32_t lo = t == 0 ? v.v1 : t == 1 ? v.w : t == 2 ? v.v2 : v.v3;
+  b[0] = (lo & d.m4) | d.c4;
+  b[1] = (lo & d.m5) | d.c5;
+  b[2] = (lo & d.m6) | d.c6;
+  b[3] = t < 2 ? (lo & d.m7) | d.c7 : ((t == 2 ? v.v1 : v.w) & d.m15) | d.c15;
+}
+
 // 1 + c per pair position ip (0 at the two +-1 positions, whose activations
 // are negated), as bf16 pairs: the weights of the chain start.
 __device__ __forceinline__ constexpr uint32_t plane_init_weight(int ip) {
@@ -1044,40 +1061,82 @@ struct PlaneFmt {
   }
   // One accumulator chain per (column tile, plane), scaled by its alpha.  In
   // the fast form each chain ends at minus the plane's signed sum, so the
-  // weighted total is negated once.
+  // weighted total is negated once, and a plane's chains over the wave's
+  // column tiles are interleaved k block by k block (consecutive MFMAs are
+  // independent).
   template <int GPW, int MAXW>
   static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
                                                const MmaX<GPW, MAXW>& mx) {
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (MAXW <= 8) {
+      if constexpr (P <= 4) {
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi)
+        for (int p = 0; p < P; ++p) {
+          PlaneViews v[GPW];
+          f32x4_t c[GPW];
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        f32x4_t c;
-        if constexpr (MAXW <= 8) {
-          uint32_t b[4][4];
-          plane_operands(sl.w[gi][p], mx.d, b);
-          c = mx.cinit[gi];
+          for (int gi = 0; gi < GPW; ++gi) {
+            v[gi] = plane_views(sl.w[gi][p]);
+            c[gi] = mx.cinit[gi];
+          }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) c = mfma16x16x32(&xa[gi][4 * t], b[t], c);
-        } else {
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int gi = 0; gi < GPW; ++gi) {
+              uint32_t b[4];
+              plane_operands_t(v[gi], t, mx.d, b);
+              c[gi] = mfma16x16x32(&xa[gi][4 * t], b, c[gi]);
+            }
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi) {
+            const float a = sl.a[p].f16(gi);
+            yv.x = fmaf(a, c[gi][0], yv.x);
+            yv.y = fmaf(a, c[gi][1], yv.y);
+            yv.z = fmaf(a, c[gi][2], yv.z);
+            yv.w = fmaf(a, c[gi][3], yv.w);
+          }
+        }
+      } else {
+        // Five or six planes: the tile's registers leave no room for
+        // interleaved chains, so each (column tile, plane) runs its own.
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            uint32_t b[4][4];
+            plane_operands(sl.w[gi][p], mx.d, b);
+            f32x4_t c = mx.cinit[gi];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) c = mfma16x16x32(&xa[gi][4 * t], b[t], c);
+            const float a = sl.a[p].f16(gi);
+            yv.x = fmaf(a, c[0], yv.x);
+            yv.y = fmaf(a, c[1], yv.y);
+            yv.z = fmaf(a, c[2], yv.z);
+            yv.w = fmaf(a, c[3], yv.w);
+          }
+      }
+      return make_float4(-yv.x, -yv.y, -yv.z, -yv.w);
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
           const uint32_t wp = sl.w[gi][p];
-          c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const uint32_t bq[4] = {sign_pair(wp, 4 * t + 0, mx.one), sign_pair(wp, 4 * t + 1, mx.one),
                                     sign_pair(wp, 4 * t + 2, mx.one), sign_pair(wp, 4 * t + 3, mx.one)};
             c = mfma16x16x32(&xa[gi][4 * t], bq, c);
           }
+          const float a = sl.a[p].f16(gi);
+          yv.x = fmaf(a, c[0], yv.x);
+          yv.y = fmaf(a, c[1], yv.y);
+          yv.z = fmaf(a, c[2], yv.z);
+          yv.w = fmaf(a, c[3], yv.w);
         }
-        const float a = sl.a[p].f16(gi);
-        yv.x = fmaf(a, c[0], yv.x);
-        yv.y = fmaf(a, c[1], yv.y);
-        yv.z = fmaf(a, c[2], yv.z);
-        yv.w = fmaf(a, c[3], yv.w);
-      }
-    if constexpr (MAXW <= 8) return make_float4(-yv.x, -yv.y, -yv.z, -yv.w);
-    return yv;
+      return yv;
+    }
   }
 };
 
@@ -1441,22 +1500,33 @@ __global__ void __launch_bounds__(64 * MAXW)
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
       float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
+      // One MFMA chain per group.  Up to eight waves the groups' chains are
+      // interleaved k block by k block, so consecutive MFMAs are independent
+      // and the matrix core need not wait for each result before the next
+      // issue; the 16-wave shapes (128 registers) run them one after another.
+      constexpr int IL = MAXW <= 8 ? GPW : 1;  // chains in flight
 #pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        const uint4 cw = ring[j].c[gi];
-        const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-        f32x4_t c = cinit[gi];
+      for (int g0c = 0; g0c < GPW; g0c += IL) {
+        f32x4_t c[IL];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t bq[4] = {int4_pair(w[t], 0, magic), int4_pair(w[t], 1, magic),
-                                  int4_pair(w[t], 2, magic), int4_pair(w[t], 3, magic)};
-          c = mfma16x16x32(&xa[gi][4 * t], bq, c);
+        for (int u = 0; u < IL; ++u) c[u] = cinit[g0c + u];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int u = 0; u < IL; ++u) {
+            const uint32_t w = (&ring[j].c[g0c + u].x)[t];
+            const uint32_t bq[4] = {int4_pair(w, 0, magic), int4_pair(w, 1, magic), int4_pair(w, 2, magic),
+                                    int4_pair(w, 3, magic)};
+            c[u] = mfma16x16x32(&xa[g0c + u][4 * t], bq, c[u]);
+          }
+#pragma unroll
+        for (int u = 0; u < IL; ++u) {
+          const float sc = ring[j].s.bf16(g0c + u);
+          yv.x = fmaf(sc, c[u][0], yv.x);
+          yv.y = fmaf(sc, c[u][1], yv.y);
+          yv.z = fmaf(sc, c[u][2], yv.z);
+          yv.w = fmaf(sc, c[u][3], yv.w);
         }
-        const float sc = ring[j].s.bf16(gi);
-        yv.x = fmaf(sc, c[0], yv.x);
-        yv.y = fmaf(sc, c[1], yv.y);
-        yv.z = fmaf(sc, c[2], yv.z);
-        yv.w = fmaf(sc, c[3], yv.w);
       }
       stage.put(i, i < T, wave, lane, yv);
       // Slot j is refilled only after its last use, so it keeps its registers.

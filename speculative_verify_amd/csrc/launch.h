@@ -79,8 +79,8 @@ inline int env_int(const char* name, int lo, int hi, int dflt) {
 // two workgroups per CU with a ring of <= 2 tiles, everything else at one
 // workgroup per CU; a ring of 2 tiles already keeps more bytes in flight
 // than the memory system's bandwidth-latency product, and deeper rings were
-// slower for the W4A16 kernels (the sign-plane verify kernel, with more
-// arithmetic per byte, gains a little from 3).  Workgroups of the M <= 16
+// slower (the M = 16 sign-plane head at 32768 rows, eight tiles a
+// workgroup: 26.4 us at a ring of 2, 28.7 at 3).  Workgroups of the M <= 16
 // mat-muls that own at most `shallow` tiles run without a ring (depth 1):
 // at three tiles each (N = 12288) that was 6% faster for the sign planes,
 // 3% for sa* and 1% for W4A16 than rings of 2 or 3 (the prefetch of later
@@ -90,7 +90,7 @@ struct LaunchPref {
 };
 constexpr LaunchPref kPrefGemv = {2, 2, 0};
 constexpr LaunchPref kPrefGemmW4 = {1, 2, 3};
-constexpr LaunchPref kPrefGemmPlanes = {1, 3, 3};
+constexpr LaunchPref kPrefGemmPlanes = {1, 2, 3};
 constexpr LaunchPref kPrefHeadM1 = {1, 2, 0};
 constexpr LaunchPref kPrefHeadM16 = {1, 2, 0};
 
