@@ -63,6 +63,11 @@ def alg_bytes_head(M: int, N: int) -> int:
     return N * K // 2 + N * (K // G) * 2 + M * K * 2 + M * 8
 
 
+def alg_bytes_head_binplane(M: int, N: int, P: int) -> int:
+    """Sign planes + fp16 alphas + X in + (int32 index, fp32 max) per row out."""
+    return N * K // 8 * P + P * N * (K // G) * 2 + M * K * 2 + M * 8
+
+
 def build_step(svq, synth, torch):
     """Allocate every call's inputs on the device.
 
@@ -142,7 +147,8 @@ def build_step(svq, synth, torch):
 
 
 def build_extra(svq, synth, torch):
-    """The sa* calls, in build_step's format (timed alone, not in the step)."""
+    """The calls timed alone, outside the step, in build_step's format: sa*
+    storage, W4A16 blocks of 32 and 64 rows, and the sign-plane LM head."""
     calls = []
     seed = [500]
 
@@ -171,6 +177,19 @@ def build_extra(svq, synth, torch):
 
         calls.append((f"gemm_smallm_w4a16_m{M}_n{N}", alg_bytes_linear("w4a16", M, N), make(), make))
 
+    def bphead(M, N, P):
+        def make():
+            seed[0] += 1
+            blob = synth.device_binplane_blob(N, K, P, seed[0])
+            seed[0] += 1
+            X = synth.device_activations(M, K, seed[0]).view(torch.int16)
+            idx = torch.empty(M, dtype=torch.int32, device="cuda")
+            mx = torch.empty(M, dtype=torch.float32, device="cuda")
+            ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+            return lambda: svq.lmhead_argmax_binplane(blob, X, M, N, K, P, idx, mx, ws)
+
+        calls.append((f"lmhead_argmax_binplane_p{P}_m{M}_n{N}", alg_bytes_head_binplane(M, N, P), make(), make))
+
     sa(1, 12288, 3, 128)
     sa(16, 4096, 3, 128)
     sa(16, 12288, 3, 128)
@@ -180,6 +199,8 @@ def build_extra(svq, synth, torch):
     w4(32, 12288)
     w4(64, 4096)
     w4(64, 12288)
+    bphead(1, 32768, 3)
+    bphead(16, 32768, 3)
     return calls
 
 
@@ -436,6 +457,8 @@ def main():
             "lmhead_n248320": ratio("lmhead_verify_greedy_m16_n248320", "lmhead_argmax_m1_n248320"),
             "sa_p3_g128_n12288": ratio("gemm_smallm_sa_p3_g128_m16_n12288", "gemv_sa_p3_g128_m1_n12288"),
             "sa_p3_g64_n12288": ratio("gemm_smallm_sa_p3_g64_m16_n12288", "gemv_sa_p3_g64_m1_n12288"),
+            "binplane_head_p3_n32768": ratio("lmhead_argmax_binplane_p3_m16_n32768",
+                                             "lmhead_argmax_binplane_p3_m1_n32768"),
         },
     }
     traffic = load_traffic(dom)

@@ -35,6 +35,9 @@ def test_head_bytes_replace_the_output_by_index_and_max():
     assert bench.alg_bytes_head(16, 32768) == 69_337_216
     assert bench.alg_bytes_head(1, 248320) == 524_460_040
     assert bench.alg_bytes_head(16, 248320) == 524_583_040
+    # The sign-plane head: P bits per weight and an fp16 alpha per (plane,
+    # row, group) instead of the nibble and the bf16 scale.
+    assert bench.alg_bytes_head_binplane(1, 32768, 3) == 32768 * 512 * 3 + 3 * 32768 * 32 * 2 + 8192 + 8
     # No logits are stored: the fused head moves M * N * 4 bytes less than
     # a mat-mul writing fp32 logits would.
     assert bench.alg_bytes_head(16, 248320) < bench.alg_bytes_linear("w4a16", 16, 248320)
