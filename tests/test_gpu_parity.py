@@ -708,23 +708,27 @@ def _under_knobs(fn, monkeypatch):
 
 
 @pytest.mark.parametrize("kind,M", [("w4a16", 1), ("w4a16", 16), ("w4a16", 5), ("binplane", 1), ("binplane", 16),
-                                    ("sa", 1), ("sa", 16), ("head", 1), ("head", 16)])
+                                    ("sa", 1), ("sa", 16), ("head", 1), ("head", 16), ("bphead", 1),
+                                    ("bphead", 16)])
 def test_outputs_do_not_depend_on_launch_shape(kind, M, monkeypatch):
     N, K, P, G = 5008, 4096, 3, 64  # 313 row tiles (the device generators need whole tiles)
     X = synth.device_activations(M, K, 11).view(torch.int16)
     if kind in ("w4a16", "head"):
         blob = synth.device_int4_blob(N, K, 12)
-    elif kind == "binplane":
+    elif kind in ("binplane", "bphead"):
         blob = synth.device_binplane_blob(N, K, P, 13)
     else:
         blob = synth.device_sa_blob(N, K, P, G, 14)
 
     def call():
-        if kind == "head":
+        if kind in ("head", "bphead"):
             idx = torch.empty(M, dtype=torch.int32, device="cuda")
             mx = torch.empty(M, dtype=torch.float32, device="cuda")
             ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
-            svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
+            if kind == "head":
+                svq.lmhead_argmax(blob, X, M, N, K, idx, mx, ws)
+            else:
+                svq.lmhead_argmax_binplane(blob, X, M, N, K, P, idx, mx, ws)
             return torch.cat([idx.view(torch.int32), mx.view(torch.int32)]).cpu().numpy()
         Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
         if kind == "w4a16":
