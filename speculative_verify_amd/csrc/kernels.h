@@ -216,6 +216,54 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// Running greedy choices (value, row) combined across lanes without LDS:
+// DPP moves within a row of 16 lanes (rotations by 8 and 4, then the quad
+// swaps of lanes 1 apart and 2 apart) and the gfx950 lane-swap instructions
+// across rows.  Every lane ends with the best of the lanes combined, lowest
+// row on equal values.
+template <int CTRL>
+__device__ __forceinline__ void best_with_dpp(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Over the 16 lanes of each row.
+__device__ __forceinline__ void best_over_row(float& v, int& i) {
+  best_with_dpp<0x128>(v, i);  // row_ror:8
+  best_with_dpp<0x124>(v, i);  // row_ror:4
+  best_with_dpp<0x4E>(v, i);   // quad_perm [2, 3, 0, 1]
+  best_with_dpp<0xB1>(v, i);   // quad_perm [1, 0, 3, 2]
+}
+
+// Over all 64 lanes of the wave.
+__device__ __forceinline__ void best_over_wave(float& v, int& i) {
+  {
+    const auto sv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const auto si = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+    v = __uint_as_float(sv[0]);
+    i = (int)si[0];
+    if (better(__uint_as_float(sv[1]), (int)si[1], v, i)) {
+      v = __uint_as_float(sv[1]);
+      i = (int)si[1];
+    }
+  }
+  {
+    const auto sv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const auto si = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
+    v = __uint_as_float(sv[0]);
+    i = (int)si[0];
+    if (better(__uint_as_float(sv[1]), (int)si[1], v, i)) {
+      v = __uint_as_float(sv[1]);
+      i = (int)si[1];
+    }
+  }
+  best_over_row(v, i);
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t* a, const uint32_t* b, f32x4_t c) {
   u32x4_t av = {a[0], a[1], a[2], a[3]};
   u32x4_t bv = {b[0], b[1], b[2], b[3]};
@@ -777,14 +825,7 @@ template <int MAXW>
 __device__ __forceinline__ void gemv_argmax_epilogue(float best_v, int best_i, int wave, int lane, int nwaves,
                                                      uint8_t* ws, int N, const HeadOut& ho) {
   __shared__ ArgBest part[MAXW];
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(best_v, off);
-    const int oi = __shfl_xor(best_i, off);
-    if (better(ov, oi, best_v, best_i)) {
-      best_v = ov;
-      best_i = oi;
-    }
-  }
+  best_over_wave(best_v, best_i);
   if (lane == 0) part[wave] = ArgBest{best_v, best_i};
   __syncthreads();
   if (threadIdx.x == 0)
@@ -1398,15 +1439,7 @@ template <int MAXW>
 __device__ __forceinline__ void gemm_argmax_epilogue(RowBest4& b, int wave, int lane, int nwaves, uint8_t* ws,
                                                      int M, int N, const HeadOut& ho) {
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
-    for (int off = 8; off > 0; off >>= 1) {  // over the 16 lanes of one q
-      const float ov = __shfl_xor(b.v[ii], off);
-      const int oi = __shfl_xor(b.idx[ii], off);
-      if (better(ov, oi, b.v[ii], b.idx[ii])) {
-        b.v[ii] = ov;
-        b.idx[ii] = oi;
-      }
-    }
+  for (int ii = 0; ii < 4; ++ii) best_over_row(b.v[ii], b.idx[ii]);  // over the 16 lanes of one q
   __shared__ ArgBest fin[MAXW][16];  // [wave][query row]
   if ((lane & 15) == 0)
 #pragma unroll
