@@ -128,8 +128,12 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
   Cursor xc{(int)blockIdx.x, 0, (int)blockIdx.x % CK, 0};
   Cursor wc = xc;
   uint4 xh[H0][4];
-  // Prologue: step 0's X into LDS, the first D - 1 steps' weights in flight.
+  // Prologue: step 0's X into LDS (both halves requested before either is
+  // stored: the accumulators are not live yet, so the second half has
+  // registers of its own), the first D - 1 steps' weights in flight.
   load_x(xc, 0, H0, xh);
+  uint4 xh1[H1 > 0 ? H0 : 1][4];
+  if constexpr (H1 > 0) load_x(xc, H0, H1, xh1);
   MmqW<R> ring[D];
 #pragma unroll
   for (int j = 0; j + 1 < D; ++j) {
@@ -137,10 +141,7 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
     advance(wc);
   }
   store_x(0, H0, xh);
-  if constexpr (H1 > 0) {
-    load_x(xc, H0, H1, xh);
-    store_x(H0, H1, xh);
-  }
+  if constexpr (H1 > 0) store_x(H0, H1, xh1);
   advance(xc);
 
   const PairDecode magic = int4_decode();
