@@ -744,3 +744,36 @@ def test_outputs_do_not_depend_on_launch_shape(kind, M, monkeypatch):
     ref = outs[0][1]
     for knobs, out in outs[1:]:
         assert np.array_equal(out, ref), f"{kind} M={M}: outputs differ under {knobs}"
+
+
+# ---------------------------------------------------------------------------
+# Seeded sweep over random shapes: every linear call at random M (1..64), N,
+# K (up to 8192, so both workgroup widths), P and G, against the oracle.
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_random_shapes_against_the_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    for c in range(12):
+        kind = ("w4a16", "binplane", "sa")[c % 3]
+        M = int(rng.choice([1, 2, 5, 16, 17, 33, 64]))
+        if kind == "sa":
+            G, K, P = int(rng.choice([64, 128, 256])), 256 * int(rng.integers(1, 33)), int(rng.integers(2, 7))
+        else:
+            G, K, P = 128, 128 * int(rng.integers(1, 65)), int(rng.integers(1, 7))
+        N = int(rng.integers(1, 1500))
+        what = f"seed {seed} case {c}: {kind} M={M} N={N} K={K} P={P} G={G}"
+        print(what, flush=True)
+        X = synth.activations(rng, M, K)
+        if kind == "w4a16":
+            codes, scales = synth.int4_weights(rng, N, K)
+            Y, A = oracle.linear_w4a16(codes, scales, X)
+            Yg = run_gemv_w4a16(codes, scales, X)[None] if M == 1 else run_gemm_w4a16(codes, scales, X)
+        elif kind == "binplane":
+            signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+            Y, A = oracle.linear_binplane(signs, alpha, X)
+            Yg = run_gemv_binplane(signs, alpha, X)[None] if M == 1 else run_gemm_binplane(signs, alpha, X)
+        else:
+            signs, codes, d = synth.sa_weights(rng, N, K, P, G)
+            Y, A = oracle.linear_sa(signs, codes, d, X, G=G)
+            Yg = run_gemv_sa(signs, codes, d, X, G)[None] if M == 1 else run_gemm_sa(signs, codes, d, X, G)
+        check_close(Yg, Y, A, what)
