@@ -216,9 +216,10 @@ constexpr int max_depth_planes(int P) { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
   F, decltype(G)::value, decltype(W)::value,                                                       \
       (decltype(D)::value < max_depth_planes(F::P) ? decltype(D)::value : max_depth_planes(F::P))
 
-// The sa* kernels and the sign-plane mat-muls keep rings of at most three
-// tiles (the measured best of the plane kernels; deeper rings would spill
-// registers and are not instantiated for them).
+// The sa* kernels and the sign-plane mat-muls are instantiated with rings of
+// at most three tiles (deeper rings would spill registers); the launch
+// preferences above choose at most two, three stays reachable through
+// SVQ_PIPE_DEPTH.
 constexpr int kMaxDepthSa = 3;
 constexpr int kMaxDepthPlanesGemm = 3;
 
