@@ -250,8 +250,9 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y,
  * summary sec. 4.1: the drafted tokens are verified in parallel; report
  * sec. 3.2: block size 16):  Y[m][n] = the W4A16 result for row m of X.
  * Blocks of 16 < M <= 64 rows (a prefill chunk; the ShiftAddQwen README
- * places batches below 64 in the quantized mat-mul regime) take a kernel
- * that streams X with the weights; the result is defined the same way.
+ * places batches below 64 in the quantized mat-mul regime) take the same
+ * kernel with two 16-row tiles of X (M <= 32, K <= 4096) or a kernel that
+ * streams X with the weights; the result is defined the same way.
  *   X  [M][K] bf16 bits, 16-byte aligned;  Y [M][N] bf16 bits, 2-byte aligned.
  * Errors: as gemv_w4a16, plus SHAPE for M outside 1..64.
  */

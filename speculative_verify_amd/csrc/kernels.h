@@ -1580,6 +1580,99 @@ __global__ void __launch_bounds__(64 * MAXW)
     gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
 
+// W4A16 mat-mul for blocks of 17..32 rows at K <= 4096 (eight waves or
+// fewer): the M <= 16 kernel with both 16-row m-tiles of X held in registers,
+// so every decoded weight pair feeds the MFMAs of both m-tiles and the
+// weights are read once for the block.  X arrives as for the M <= 16 kernel
+// (coalesced, transposed through a wave-private LDS region per m-tile); the
+// partial tiles of the two m-tiles meet in two staging areas, two tiles per
+// chunk, waves 0-1 finishing m-tile 0 and waves 2-3 m-tile 1.
+template <int GPW, int D>
+__global__ void __launch_bounds__(64 * 8)
+    k_gemm_w4a16_x2(const uint8_t* __restrict__ blob, const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
+                    int M, int N, int KT, int NT) {
+  constexpr int MAXW = 8, C = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r = lane & 15;
+  const int g0 = wave * GPW;
+  const int K = KT * 128;
+  const BlobView bv = int4_view(blob, KT, NT);
+  const int T = tiles_of_wg(NT);
+
+  // Rows 16..M-1 of the second m-tile read zero past M (buffer range).
+  XRows<GPW> xr0, xr1;
+  load_x_rows<GPW>(X, M, K, g0, KT, lane, xr0);
+  load_x_rows<GPW>(X + (size_t)16 * K, M - 16, K, g0, KT, lane, xr1);
+  __builtin_amdgcn_sched_barrier(0);
+  Int4Slot<GPW> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_int4_tile<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __shared__ ChunkStage<float4, C, MAXW, 64> stage[2];
+  __shared__ uint4 xt[MAXW][2][256];  // a wave's two transposition regions (2 x 4 KiB)
+  uint32_t xa[2][GPW][16];
+  transpose_x_rows<GPW>(xr0, xt[wave][0], lane, q, r, xa[0]);
+  transpose_x_rows<GPW>(xr1, xt[wave][1], lane, q, r, xa[1]);
+  f32x4_t cinit[2][GPW];
+  x_row_group_init<GPW>(xa[0], q, g0, KT, cinit[0]);
+  x_row_group_init<GPW>(xa[1], q, g0, KT, cinit[1]);
+  const PairDecode magic = int4_decode();
+  RowBest4 unused;
+
+  int i0 = 0;
+  do {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      f32x4_t c[2][GPW];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) c[mt][gi] = cinit[mt][gi];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+          const uint32_t w = (&ring[j].c[gi].x)[t];
+          const uint32_t bq[4] = {int4_pair(w, 0, magic), int4_pair(w, 1, magic), int4_pair(w, 2, magic),
+                                  int4_pair(w, 3, magic)};
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) c[mt][gi] = mfma16x16x32(&xa[mt][gi][4 * t], bq, c[mt][gi]);
+        }
+      float4 yv[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        const float sc = ring[j].s.bf16(gi);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          yv[mt].x = fmaf(sc, c[mt][gi][0], yv[mt].x);
+          yv[mt].y = fmaf(sc, c[mt][gi][1], yv[mt].y);
+          yv[mt].z = fmaf(sc, c[mt][gi][2], yv[mt].z);
+          yv[mt].w = fmaf(sc, c[mt][gi][3], yv[mt].w);
+        }
+      }
+      stage[0].put(i, i < T, wave, lane, yv[0]);
+      stage[1].put(i, i < T, wave, lane, yv[1]);
+      // Slot j is refilled only after its last use, so it keeps its registers.
+      __builtin_amdgcn_sched_barrier(0);
+      load_int4_tile<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+      const int ci = i % C;
+      if (i < T && (ci == C - 1 || i == T - 1)) {
+        __syncthreads();
+        const int first = i - ci;
+        const int mt = wave / C, cc = wave % C;  // (m-tile, tile of the chunk) of waves 0-3
+        if (mt < 2 && cc <= ci)
+          gemm_emit<false>(stage[mt].sum(i, cc, nwaves, lane), q, r, row_tile(first + cc), M - 16 * mt, N,
+                           Y + (size_t)16 * mt * N, unused);
+      }
+    }
+    i0 += D;
+  } while (i0 < T);
+}
+
 // Sign-plane verify mat-mul and head (M <= 16) for storage format F.
 template <class F, int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)

@@ -60,6 +60,27 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
                       int32_t G, void* stream) {
   if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0, SVQ_MAX_M_GEMM)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096) {
+    // Two m-tiles held in registers: the M <= 16 kernel's launch shape.
+    Shape sh;
+    if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
+    auto launch = [&](auto Gc, auto Dc) {
+      hipLaunchKernelGGL((k_gemm_w4a16_x2<decltype(Gc)::value, decltype(Dc)::value>), dim3(sh.grid),
+                         dim3(64 * sh.waves), 0, st, packed, X, Y, M, (int)N, sh.KT, sh.NT);
+    };
+    auto by_depth = [&](auto Gc) {
+      // At four groups a wave the two m-tiles' activations leave registers
+      // for a one-tile ring only.
+      if constexpr (decltype(Gc)::value < 4) {
+        if (sh.depth >= 2) return launch(Gc, ic<2>{});
+      }
+      launch(Gc, ic<1>{});
+    };
+    if (sh.gpw == 1) by_depth(ic<1>{});
+    else if (sh.gpw == 2) by_depth(ic<2>{});
+    else by_depth(ic<4>{});
+    return launched("gemm_smallm_w4a16");
+  }
   if (M > SVQ_MAX_M) {
     MmqShape sh;
     if (int rc = plan_mmq(N, M, &sh)) return rc;
