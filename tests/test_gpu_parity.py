@@ -304,6 +304,21 @@ def test_gemm_w4a16_midm_many_blocks_per_workgroup():
     check_close(got[:, rows], Y, A, "M=64 N=33000 sample")
 
 
+@pytest.mark.parametrize("M,N,K", [(24, 20000, 1024), (32, 40000, 4096), (17, 16400, 2048)])
+def test_gemm_w4a16_two_mtiles_many_tiles_per_workgroup(M, N, K):
+    # 17..32 rows at K <= 4096 keep both m-tiles in registers; here every
+    # workgroup owns several row tiles (with a two-tile ring where the
+    # registers allow one), checked on a sample of output rows.
+    rng = np.random.default_rng(M + N + K)
+    codes, scales = synth.int4_weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    print(f"gemm_smallm_w4a16 M={M} N={N} K={K}", flush=True)
+    got = run_gemm_w4a16(codes, scales, X)
+    rows = np.unique(np.concatenate([np.arange(0, 48), np.arange(N - 40, N), rng.integers(0, N, 400)]))
+    Y, A = oracle.linear_w4a16(codes[rows], scales[rows], X)
+    check_close(got[:, rows], Y, A, f"M={M} N={N} K={K} sample")
+
+
 @pytest.mark.parametrize("M,N,K,P", [(17, 300, 512, 3), (40, 1000, 1024, 2), (64, 4096, 4096, 3), (64, 77, 2048, 6)])
 def test_gemm_planes_midm(M, N, K, P):
     # Sign planes (fp16 alphas and sa* codes) above 16 rows: one pass of the
