@@ -173,9 +173,23 @@ def build_extra(svq, synth, torch):
             seed[0] += 1
             X = synth.device_activations(M, K, seed[0]).view(torch.int16)
             Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+            if M == 1:
+                return lambda: svq.gemv_w4a16(blob, X, Y, N, K)
             return lambda: svq.gemm_smallm_w4a16(blob, X, Y, M, N, K)
 
-        calls.append((f"gemm_smallm_w4a16_m{M}_n{N}", alg_bytes_linear("w4a16", M, N), make(), make))
+        name = f"gemv_w4a16_m1_n{N}" if M == 1 else f"gemm_smallm_w4a16_m{M}_n{N}"
+        calls.append((name, alg_bytes_linear("w4a16", M, N), make(), make))
+
+    def bp1(N, P):
+        def make():
+            seed[0] += 1
+            blob = synth.device_binplane_blob(N, K, P, seed[0])
+            seed[0] += 1
+            X = synth.device_activations(1, K, seed[0]).view(torch.int16)
+            Y = torch.empty((1, N), dtype=torch.int16, device="cuda")
+            return lambda: svq.gemv_binplane(blob, X, Y, N, K, P)
+
+        calls.append((f"gemv_binplane_p{P}_m1_n{N}", alg_bytes_linear("binplane", 1, N, P), make(), make))
 
     def bphead(M, N, P):
         def make():
@@ -201,6 +215,9 @@ def build_extra(svq, synth, torch):
     w4(64, 12288)
     bphead(1, 32768, 3)
     bphead(16, 32768, 3)
+    # M = 1 at N = 4096, so the verify/decode ratio exists for both widths.
+    w4(1, 4096)
+    bp1(4096, 3)
     return calls
 
 
@@ -459,6 +476,8 @@ def main():
             "sa_p3_g64_n12288": ratio("gemm_smallm_sa_p3_g64_m16_n12288", "gemv_sa_p3_g64_m1_n12288"),
             "binplane_head_p3_n32768": ratio("lmhead_argmax_binplane_p3_m16_n32768",
                                              "lmhead_argmax_binplane_p3_m1_n32768"),
+            "w4a16_n4096": ratio("gemm_smallm_w4a16_m16_n4096", "gemv_w4a16_m1_n4096"),
+            "binplane_n4096": ratio("gemm_smallm_binplane_p3_m16_n4096", "gemv_binplane_p3_m1_n4096"),
         },
     }
     traffic = load_traffic(dom)
