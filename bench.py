@@ -221,11 +221,14 @@ def build_extra(svq, synth, torch):
     return calls
 
 
-def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 4)):
+def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 4), passes=2):
     """GB/s of a plain non-temporal 16-byte streaming read of `nbytes`, cold:
     launches rotate over copies that together hold at least twice the
     last-level cache, so every launch streams from HBM.  The best of the
-    given launch widths (workgroups per CU) is the ceiling."""
+    given launch widths (workgroups per CU), over `passes` sweeps of them, is
+    the ceiling: a short read's rate dips for a while now and then when the
+    clocks fall back between the synchronising sweeps, and one sweep can fall
+    entirely into such a dip."""
     nbytes = nbytes // 16 * 16
     stride = (nbytes + 255) // 256 * 256
     copies = max(2, -(-2 * LLC_BYTES // stride))
@@ -234,7 +237,7 @@ def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 
     sink = torch.empty(8 * 1024, dtype=torch.int32, device="cuda")
     views = [buf[i * stride: i * stride + nbytes] for i in range(copies)]
     best = 0.0
-    for w in wgs_per_cu:
+    for w in [w for _ in range(passes) for w in wgs_per_cu]:
         for i in range(3):
             svq.svq_stream_read(views[i % copies], nbytes, sink, w)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -29,9 +29,11 @@ __global__ void __launch_bounds__(64) k_verify_greedy(const int32_t* __restrict_
 }
 
 // Streaming-read ceiling: every thread keeps U non-temporal 16-byte loads in
-// flight over a grid-stride walk of the buffer; the last partial round
-// issues its (guarded) loads together as well, so the probe streams any size
-// at full depth.  One checksum per workgroup keeps the loads live.
+// flight over a grid-stride walk of the buffer.  The last partial round
+// issues its loads together as well: past the end they read the last element
+// again and are dropped, so no load sits behind a branch of its own (a
+// guarded load per branch would wait for each load before the next).  One
+// checksum per workgroup keeps the loads live.
 __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ src, size_t n16,
                                                      uint32_t* __restrict__ sink) {
   constexpr int U = 8;
@@ -45,15 +47,16 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ s
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  {
+  if (i < n16) {
     v4u_t v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      v[u] = v4u_t{0u, 0u, 0u, 0u};
-      if (i + u * stride < n16) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + i + u * stride));
+      const size_t j = i + u * stride;
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + (j < n16 ? j : n16 - 1)));
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < U; ++u)
+      if (i + u * stride < n16) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
   __shared__ uint32_t part[4];
