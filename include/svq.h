@@ -308,8 +308,11 @@ int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
  *              it zeroed).  Every call leaves it zero again, so one
  *              workspace serves any number of calls of any M.
  * One launch: each workgroup folds its per-row best (logit, row) into the
- * workspace with device-scope 64-bit atomic max operations; the last
- * workgroup to finish reads the result and clears the workspace.
+ * workspace with device-scope 64-bit atomic max operations (into the keys
+ * of one of 16 groups when every workgroup owns at most 8 row tiles, whose
+ * last workgroup then signals a launch counter); the last workgroup to
+ * finish reads every group's keys, writes the result and clears the
+ * workspace.
  * Errors: as gemm_smallm_w4a16, plus WORKSPACE.  Calls that overlap in time
  * must not share a workspace.
  */

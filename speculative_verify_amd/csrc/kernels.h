@@ -742,19 +742,31 @@ struct ChunkStage {
 // unsigned order is the greedy order: the high word is the logit's bits
 // mapped so that unsigned comparison follows float comparison, the low word
 // is 2^32 - 1 - row, so a larger logit wins and the lower row wins a tie.
-// Every workgroup folds its per-query-row best into key[m] with a
-// device-scope atomicMax and waits for the atomic to return before it bumps a
-// completion counter; the workgroup that brings the counter to gridDim.x
-// takes each key with an atomic exchange against zero, writes the outputs and
-// clears the counter.  Keys and counter are only ever touched by device-scope
-// read-modify-write atomics, which every XCD performs at the same point of
-// coherence, and each step is issued only after the step before it has
-// returned, so no cache-wide fence is needed.  A max does not depend on the
-// order of its operands, so neither does the result.
+// Device-scope atomics on one address are performed one after another, so
+// when all 256 workgroups of a launch finish together, a single key and
+// counter for all of them cost about 2.9 us over an empty launch (MI355X,
+// measured); meeting in two levels, 16 groups and then the groups, costs
+// about 1.2 us there but adds a dependent round trip, which costs more than
+// it saves when the workgroups' completions are spread out (many tiles
+// each).  HeadOut::levels, uniform over the launch, selects the form.  In
+// two levels workgroup b belongs to group b mod 16; in one level all are in
+// group 0.  A workgroup folds its per-query-row best into its group's keys
+// with device-scope atomicMax, waits for the atomics to complete, and bumps
+// its group's counter; in two levels the group's last workgroup clears that
+// counter and bumps the launch counter.  The launch's last workgroup takes
+// every group's keys with atomic exchanges against zero (all at once, one
+// per thread), keeps the largest per row, writes the outputs and clears the
+// launch counter.  Keys and counters are only ever touched by
+// device-scope read-modify-write atomics, which every XCD performs at the
+// same point of coherence, and each step is issued only after the step
+// before it has returned, so no cache-wide fence is needed.  A max does not
+// depend on the order of its operands, so neither does the result.
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
-constexpr int kWsKeys = 0;        // M uint64 keys
-constexpr int kWsCounter = 128;   // uint32 completion counter
-constexpr int kWsBytes = 256;
+constexpr int kWsGroups = 16;
+constexpr int kWsKeys = 0;                         // [group][16] uint64 keys, one 128-byte line a group
+constexpr int kWsGroupCounters = kWsGroups * 128;  // uint32 a group, one 128-byte line each
+constexpr int kWsCounter = 2 * kWsGroups * 128;    // uint32 launch counter
+constexpr int kWsBytes = kWsCounter + 256;
 
 __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
   const uint32_t u = __float_as_uint(v);
@@ -770,6 +782,7 @@ struct HeadOut {
   float* max;              // [M] its logit
   const int32_t* draft;    // NULL or [M - 1] drafted tokens d_1 .. d_{M-1}
   int32_t* accept;         // [1] tau, when draft is set
+  int levels;              // argmax completion in one level (all workgroups) or two (16 groups)
 };
 
 // Greedy acceptance of a verified block (DFlash summary sec. 4.1): query row
@@ -787,21 +800,40 @@ __device__ __forceinline__ int greedy_accept_len(const int32_t* t, const int32_t
 __device__ __forceinline__ void argmax_complete(unsigned long long key, bool holds_row, int m, uint8_t* ws, int M,
                                                 int N, const HeadOut& ho) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kWsKeys);
+  unsigned* group_counter = reinterpret_cast<unsigned*>(ws + kWsGroupCounters);
   unsigned* counter = reinterpret_cast<unsigned*>(ws + kWsCounter);
+  const bool split = ho.levels > 1;
+  const int grp = split ? (int)(blockIdx.x % kWsGroups) : 0;
+  const int ngroups = !split ? 1 : gridDim.x < (unsigned)kWsGroups ? (int)gridDim.x : kWsGroups;
   if (holds_row) {
-    atomicMax(&keys[m], key);
+    atomicMax(&keys[16 * grp + m], key);
     // Wait until the atomic has completed before the counter increment
     // below can be issued (vmcnt(0); the other counters are left free).
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   __syncthreads();
   __shared__ int last;
-  if (threadIdx.x == 0) last = atomicAdd(counter, 1u) == gridDim.x - 1;
+  if (threadIdx.x == 0) {
+    int l = 0;
+    if (!split) {
+      l = atomicAdd(counter, 1u) == gridDim.x - 1;
+    } else if (atomicAdd(&group_counter[32 * grp], 1u) == (gridDim.x - 1 - grp) / kWsGroups) {
+      // The group's last member (the group has (gridDim.x - 1 - grp) / 16 + 1).
+      atomicExch(&group_counter[32 * grp], 0u);
+      l = atomicAdd(counter, 1u) == (unsigned)ngroups - 1;
+    }
+    last = l;
+  }
   __syncthreads();
   if (!last) return;
+  __shared__ unsigned long long group_keys[kWsGroups][SVQ_MAX_M];
+  for (int t = threadIdx.x; t < ngroups * M; t += blockDim.x)
+    group_keys[t / M][t % M] = atomicExch(&keys[16 * (t / M) + t % M], 0ull);
+  __syncthreads();
   __shared__ int32_t ids[SVQ_MAX_M];
   if ((int)threadIdx.x < M) {
-    const unsigned long long k = atomicExch(&keys[threadIdx.x], 0ull);
+    unsigned long long k = 0ull;
+    for (int g = 0; g < ngroups; ++g) k = group_keys[g][threadIdx.x] > k ? group_keys[g][threadIdx.x] : k;
     const uint32_t o = (uint32_t)(k >> 32);
     const int n = (int)(0xFFFFFFFFu - (uint32_t)k);
     // key 0 means no row compared above it: every logit of the row was NaN.

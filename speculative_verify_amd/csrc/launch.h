@@ -236,6 +236,21 @@ inline int check_sa(const char* fn, const void* packed, const void* x, const voi
 
 // Argument checks shared by the head entry points (P = 0: INT4 weights;
 // P >= 1: P sign planes).
+// Argmax completion form for a head launch (see HeadOut::levels): two
+// levels where every workgroup owns at most kArgmaxSplitMaxTiles row tiles
+// (their completions arrive together), one level otherwise.  Measured on
+// MI355X (K = 4096, 256 workgroups, medians of three interleaved rounds):
+// two levels were 1-6% faster at 8 tiles a workgroup (N = 32768, W4A16 and
+// sign-plane heads, M = 1 and 16) and 0.3-1.3% slower at 16, 32 and 61
+// (N = 65536, 131072, 248320).  SVQ_ARGMAX_LEVELS = 1 or 2 overrides it (for
+// tuning runs).
+constexpr int kArgmaxSplitMaxTiles = 8;
+inline HeadOut with_levels(HeadOut ho, const Shape& sh) {
+  const int tmax = (sh.NT + sh.grid - 1) / sh.grid;
+  ho.levels = env_int("SVQ_ARGMAX_LEVELS", 1, 2, tmax <= kArgmaxSplitMaxTiles ? 2 : 1);
+  return ho;
+}
+
 inline int check_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
                       int32_t G, int32_t P, const HeadOut& ho, void* workspace, size_t workspace_bytes) {
   if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, P)) return rc;

@@ -24,15 +24,16 @@ int launch_head_w4a16(const char* fn, const uint8_t* packed, const uint16_t* X, 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const HeadOut h = with_levels(ho, sh);
   if (M == 1) {
     dispatch(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, ho, (int)N, sh.KT, sh.NT);
+                         packed, Xw, (uint16_t*)nullptr, ws, h, (int)N, sh.KT, sh.NT);
     });
   } else {
     dispatch(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
+                         packed, Xw, (uint16_t*)nullptr, ws, h, M, (int)N, sh.KT, sh.NT);
     });
   }
   return launched(fn);

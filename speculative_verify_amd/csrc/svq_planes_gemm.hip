@@ -59,7 +59,7 @@ int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, 
     using F = PlaneFmt<decltype(Pc)::value>;
     dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                         st, packed, Xw, (uint16_t*)nullptr, ws, ho, M, (int)N, sh.KT, sh.NT);
+                         st, packed, Xw, (uint16_t*)nullptr, ws, with_levels(ho, sh), M, (int)N, sh.KT, sh.NT);
     });
   });
   return launched(fn);

@@ -22,7 +22,7 @@ int launch_binplane_head_m1(const char* fn, const uint8_t* packed, const uint16_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  const HeadOut ho{row_ids, argmax, maxlogit, nullptr, nullptr};
+  const HeadOut ho = with_levels(HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr, 0}, sh);
   dispatch_p(P, [&](auto Pc) {
     using F = PlaneFmt<decltype(Pc)::value>;
     dispatch(sh, [&](auto G, auto W, auto D) {

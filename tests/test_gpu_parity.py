@@ -704,16 +704,18 @@ def test_lmhead_binplane_planted(M, N, K, P):
 # workgroups per CU change which workgroup computes a tile and how far ahead
 # it loads, never the arithmetic (each tile's per-wave partials are combined
 # in wave order), so every output must be bit-identical under every setting
-# of the tuning knobs.
+# of the tuning knobs.  The heads' argmax completion in one level or two
+# (SVQ_ARGMAX_LEVELS) changes only the order of max operations.
 
 _KNOBS = [{}, {"SVQ_WG_PER_CU": "1"}, {"SVQ_WG_PER_CU": "3"}, {"SVQ_PIPE_DEPTH": "1"}, {"SVQ_PIPE_DEPTH": "3"},
-          {"SVQ_GRID_MAX": "37"}]
+          {"SVQ_GRID_MAX": "37"}, {"SVQ_ARGMAX_LEVELS": "1"}, {"SVQ_ARGMAX_LEVELS": "2"},
+          {"SVQ_ARGMAX_LEVELS": "2", "SVQ_GRID_MAX": "5"}]
 
 
 def _under_knobs(fn, monkeypatch):
     outs = []
     for knobs in _KNOBS:
-        for k in ("SVQ_WG_PER_CU", "SVQ_PIPE_DEPTH", "SVQ_GRID_MAX"):
+        for k in ("SVQ_WG_PER_CU", "SVQ_PIPE_DEPTH", "SVQ_GRID_MAX", "SVQ_ARGMAX_LEVELS"):
             monkeypatch.delenv(k, raising=False)
         for k, v in knobs.items():
             monkeypatch.setenv(k, v)
