@@ -1401,41 +1401,45 @@ __global__ void __launch_bounds__(64 * MAXW)
   int best_i = INT_MAX;
 
   int i0 = 0;
-  do {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int i = i0 + j;
-      float part;
-      if constexpr (kLut)
-        part = sum_over_q(F::template partial_lut<GPW>(ring[j], luts, lut_off));
-      else
-        part = sum_over_q(F::template partial<GPW>(ring[j], xp, one));
-      stage.put(i, i < T, wave, lane, part);
-      // Slot j is refilled only after its last use, so it keeps its registers.
-      __builtin_amdgcn_sched_barrier(0);
-      F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
-      const int ci = i % C;
-      if (i < T && (ci == C - 1 || i == T - 1)) {
-        __syncthreads();
-        const int first = i - ci;
-        for (int o = threadIdx.x; o < (ci + 1) * 16; o += nwaves * 64) {
-          const int n = 16 * row_tile(first + (o >> 4)) + (o & 15);
-          if (n < N) {
-            const float v = stage.sum(i, o >> 4, nwaves, o & 15);
-            if constexpr (ARGMAX) {
-              if (v > best_v) {  // a thread's rows arrive in increasing n
-                best_v = v;
-                best_i = n;
-              }
-            } else {
-              y[n] = f32_to_bf16_rne(v);
+  auto step = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int i = i0 + j;
+    float part;
+    if constexpr (kLut)
+      part = sum_over_q(F::template partial_lut<GPW>(ring[j], luts, lut_off));
+    else
+      part = sum_over_q(F::template partial<GPW>(ring[j], xp, one));
+    stage.put(i, i < T, wave, lane, part);
+    // Slot j is refilled only after its last use, so it keeps its registers.
+    __builtin_amdgcn_sched_barrier(0);
+    F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+    const int ci = i % C;
+    if (i < T && (ci == C - 1 || i == T - 1)) {
+      __syncthreads();
+      const int first = i - ci;
+      for (int o = threadIdx.x; o < (ci + 1) * 16; o += nwaves * 64) {
+        const int n = 16 * row_tile(first + (o >> 4)) + (o & 15);
+        if (n < N) {
+          const float v = stage.sum(i, o >> 4, nwaves, o & 15);
+          if constexpr (ARGMAX) {
+            if (v > best_v) {  // a thread's rows arrive in increasing n
+              best_v = v;
+              best_i = n;
             }
+          } else {
+            y[n] = f32_to_bf16_rne(v);
           }
         }
       }
     }
-    i0 += D;
-  } while (i0 < T);
+  };
+  // Whole rounds of the ring, then the tiles of a partial last round (held in
+  // the ring's first slots) one by one, so no step runs on an empty tile.
+  const int whole = T - T % D;
+  for (; i0 < whole; i0 += D) static_for<0, D>(step);
+  static_for<0, D - 1>([&](auto jc) {
+    if (decltype(jc)::value < T - whole) step(jc);
+  });
   if constexpr (ARGMAX) gemv_argmax_epilogue<MAXW>(best_v, best_i, wave, lane, nwaves, ws, N, ho);
 }
 
@@ -1764,26 +1768,30 @@ __global__ void __launch_bounds__(64 * MAXW)
     best.idx[ii] = INT_MAX;
   }
   int i0 = 0;
-  do {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int i = i0 + j;
-      const float4 yv = F::template mma<GPW, MAXW>(ring[j], xa, mx);
-      stage.put(i, i < T, wave, lane, yv);
-      // Slot j is refilled only after its last use, so it keeps its registers.
-      __builtin_amdgcn_sched_barrier(0);
-      F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
-      const int ci = i % C;
-      if (i < T && (ci == C - 1 || i == T - 1)) {
-        __syncthreads();
-        const int first = i - ci;
-        // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
-        // same outputs of every tile, so its columns arrive in increasing n.
-        if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, best);
-      }
+  auto step = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int i = i0 + j;
+    const float4 yv = F::template mma<GPW, MAXW>(ring[j], xa, mx);
+    stage.put(i, i < T, wave, lane, yv);
+    // Slot j is refilled only after its last use, so it keeps its registers.
+    __builtin_amdgcn_sched_barrier(0);
+    F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+    const int ci = i % C;
+    if (i < T && (ci == C - 1 || i == T - 1)) {
+      __syncthreads();
+      const int first = i - ci;
+      // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
+      // same outputs of every tile, so its columns arrive in increasing n.
+      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, best);
     }
-    i0 += D;
-  } while (i0 < T);
+  };
+  // Whole rounds of the ring, then the tiles of a partial last round (held in
+  // the ring's first slots) one by one, so no step runs on an empty tile.
+  const int whole = T - T % D;
+  for (; i0 < whole; i0 += D) static_for<0, D>(step);
+  static_for<0, D - 1>([&](auto jc) {
+    if (decltype(jc)::value < T - whole) step(jc);
+  });
   if constexpr (ARGMAX)
     gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
 }
