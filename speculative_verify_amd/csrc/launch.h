@@ -158,8 +158,14 @@ void dispatch_r(int R, L&& launch) {
 
 // Calls launch(ic<GPW>, ic<MAXW>, ic<D>) for the shape's compile-time
 // parameters.  Depths above 2 are instantiated only for the 8-wave shapes,
-// and none above MAXD (a shallower ring is launched instead).
-template <int MAXD = 6, class L>
+// and none above MAXD (a shallower ring is launched instead).  The 16-wave
+// shapes (K > 4096, 128 registers a lane) get a ring of at most MAXD16
+// tiles: a second slot spills every kernel but the W4A16 mat-vec, which
+// cost far more than the ring hides (measured at K = 8192, N = 32768, eight
+// tiles a workgroup: without the ring the W4A16 verify mat-mul ran 32%
+// faster, its head 17%, the P = 6 sign-plane kernels 31-35%, the P = 3 ones
+// 2-6%, while the W4A16 mat-vec, which does not spill, ran 2% slower).
+template <int MAXD = 6, int MAXD16 = 1, class L>
 void dispatch(const Shape& sh, L&& launch) {
   auto depth = [&](auto G, auto W, auto DM) {
     constexpr int dm = decltype(DM)::value < MAXD ? decltype(DM)::value : MAXD;
@@ -171,7 +177,8 @@ void dispatch(const Shape& sh, L&& launch) {
       if (sh.depth >= 4) return launch(G, W, ic<4>{});
     if constexpr (dm >= 3)
       if (sh.depth >= 3) return launch(G, W, ic<3>{});
-    if (sh.depth >= 2) return launch(G, W, ic<2>{});
+    if constexpr (dm >= 2)
+      if (sh.depth >= 2) return launch(G, W, ic<2>{});
     launch(G, W, ic<1>{});
   };
   if (sh.gpw == 1)
@@ -181,7 +188,7 @@ void dispatch(const Shape& sh, L&& launch) {
   else if (sh.waves <= 8)
     depth(ic<4>{}, ic<8>{}, ic<6>{});
   else
-    depth(ic<4>{}, ic<16>{}, ic<2>{});
+    depth(ic<4>{}, ic<16>{}, ic<MAXD16 < 2 ? MAXD16 : 2>{});
 }
 
 template <class L>

@@ -26,7 +26,7 @@ int launch_head_w4a16(const char* fn, const uint8_t* packed, const uint16_t* X, 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const HeadOut h = with_levels(ho, sh);
   if (M == 1) {
-    dispatch(sh, [&](auto G, auto W, auto D) {
+    dispatch<6, 2>(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
                          packed, Xw, (uint16_t*)nullptr, ws, h, (int)N, sh.KT, sh.NT);
     });
@@ -50,7 +50,7 @@ int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
   if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
-  dispatch(sh, [&](auto G, auto W, auto D) {
+  dispatch<6, 2>(sh, [&](auto G, auto W, auto D) {
     hipLaunchKernelGGL((k_gemv_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
                        packed, xw, y, (uint8_t*)nullptr, HeadOut{}, (int)N, sh.KT, sh.NT);
   });
