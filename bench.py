@@ -221,6 +221,29 @@ def build_extra(svq, synth, torch):
     return calls
 
 
+def capture_series(torch, fns, n):
+    """One HIP graph of n launches cycling over the runners fns (each runner
+    launches on torch's current stream, which is the capture stream inside
+    the context), replayed once untimed so its first run is not timed."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fns[i % len(fns)]()
+    graph.replay()
+    torch.cuda.synchronize()
+    return graph
+
+
+def time_replay(torch, graph, stream, n):
+    """Microseconds per launch of one replay of a graph of n launches."""
+    begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    begin.record(stream)
+    graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return begin.elapsed_time(end) * 1e3 / n
+
+
 def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 4), passes=2):
     """GB/s of a plain non-temporal 16-byte streaming read of `nbytes`, cold:
     launches rotate over copies that together hold at least twice the
@@ -237,18 +260,16 @@ def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 
     sink = torch.empty(8 * 1024, dtype=torch.int32, device="cuda")
     views = [buf[i * stride: i * stride + nbytes] for i in range(copies)]
     best = 0.0
+    stream = torch.cuda.current_stream()
     for w in [w for _ in range(passes) for w in wgs_per_cu]:
         for i in range(3):
             svq.svq_stream_read(views[i % copies], nbytes, sink, w)
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        s.record()
-        for i in range(iters):
-            svq.svq_stream_read(views[i % copies], nbytes, sink, w)
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / iters
-        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+        runs = [lambda v=v: svq.svq_stream_read(v, nbytes, sink, w) for v in views]
+        graph = capture_series(torch, runs, iters)
+        us = time_replay(torch, graph, stream, iters)
+        del graph
+        best = max(best, nbytes / (us * 1e-6) / 1e9)
     del views, buf
     return best
 
@@ -384,11 +405,14 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = t_begin.elapsed_time(t_end) / args.steps
 
-    # Per-call durations, each call on its own: launches back to back between
-    # one pair of events on the call stream, rotating over copies of the
-    # call's inputs that together hold at least twice the 256 MB last-level
-    # cache, so every launch streams its weights from HBM (the method of the
-    # streaming-read ceiling below).
+    # Per-call durations, each call on its own: K launches back to back,
+    # rotating over copies of the call's inputs that together hold at least
+    # twice the 256 MB last-level cache, so every launch streams its weights
+    # from HBM (the method of the streaming-read ceiling below).  The K
+    # launches are captured once into a HIP graph and the graph is replayed
+    # between one pair of events: issued one by one from Python, a call's
+    # host path (argument marshalling, the runtime's launch) can take longer
+    # than a small kernel runs, and the series would time the host.
     kernels = {}
     for name, nbytes, fn, fresh in calls + extra:
         copies = max(2, -(-2 * LLC_BYTES // nbytes))
@@ -396,31 +420,20 @@ def main():
         for f in rot[:3]:
             f()
         torch.cuda.synchronize()
-        c_begin, c_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        # Five timed rounds of K launches; the median round is reported (one
-        # round alone varies by a few percent from run to run).
-        rounds = []
-        for _ in range(5):
-            c_begin.record(stream)
-            for i in range(args.steps):
-                rot[i % copies]()
-            c_end.record(stream)
-            torch.cuda.synchronize()
-            rounds.append(c_begin.elapsed_time(c_end) * 1e3 / args.steps)
-        us = sorted(rounds)[2]
-        del rot
+        graph = capture_series(torch, rot, args.steps)
+        # Five timed replays; the median is reported (one alone varies by a
+        # few percent from run to run).
+        us = sorted(time_replay(torch, graph, stream, args.steps) for _ in range(5))[2]
+        del graph, rot
         # Hot: the same launches on one copy of the inputs, which stays in
         # the caches between launches when it fits (a lower bound on the
         # kernel's own latency and arithmetic, not a bandwidth figure).
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        c_begin.record(stream)
-        for _ in range(args.steps):
-            fn()
-        c_end.record(stream)
-        torch.cuda.synchronize()
-        hot_us = c_begin.elapsed_time(c_end) * 1e3 / args.steps
+        graph = capture_series(torch, [fn], args.steps)
+        hot_us = time_replay(torch, graph, stream, args.steps)
+        del graph
         gbps = nbytes / (us * 1e-6) / 1e9
         kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(gbps, 1),
                          "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "input_copies": copies,

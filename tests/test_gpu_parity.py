@@ -794,3 +794,87 @@ def test_random_shapes_against_the_oracle(seed):
             Y, A = oracle.linear_sa(signs, codes, d, X, G=G)
             Yg = run_gemv_sa(signs, codes, d, X, G)[None] if M == 1 else run_gemm_sa(signs, codes, d, X, G)
         check_close(Yg, Y, A, what)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay: the calls captured once and replayed give the eager
+# results, replay after replay, with eager work between the replays (the
+# head's workspace counters reset themselves in the launch that completes the
+# argmax, so consecutive replays start from a clean workspace).
+
+def test_graph_replay_matches_eager_and_oracle():
+    rng = np.random.default_rng(31)
+    N, NH, K, P, M = 2048, 8192, 4096, 3, 16
+    codes, scales = synth.int4_weights(rng, N, K)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+    hc, hs = synth.int4_weights(rng, NH, K)
+    X = synth.activations(rng, M, K)
+    rows = synth.plant_rows(rng, hc, hs, X)
+    w4 = dev(svq.pack_int4_grouped(codes, scales))
+    bp = dev(svq.pack_binary_planes(signs, alpha))
+    hb = dev(svq.pack_int4_grouped(hc, hs))
+    Xd = dev(X)
+    draft = torch.from_numpy(rows[:-1].astype(np.int32)).cuda()
+    draft[5] = (draft[5] + 1) % NH  # the sixth drafted token is rejected: tau = 6
+    ws = torch.zeros(svq.lmhead_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+
+    def outputs():
+        return {"y1": torch.empty(N, dtype=torch.int16, device="cuda"),
+                "p1": torch.empty(N, dtype=torch.int16, device="cuda"),
+                "Y": torch.empty((M, N), dtype=torch.int16, device="cuda"),
+                "PY": torch.empty((M, N), dtype=torch.int16, device="cuda"),
+                "idx": torch.empty(M, dtype=torch.int32, device="cuda"),
+                "mx": torch.empty(M, dtype=torch.float32, device="cuda"),
+                "vidx": torch.empty(M, dtype=torch.int32, device="cuda"),
+                "vmx": torch.empty(M, dtype=torch.float32, device="cuda"),
+                "tau": torch.empty(1, dtype=torch.int32, device="cuda")}
+
+    def run(o):
+        svq.gemv_w4a16(w4, Xd[0], o["y1"], N, K)
+        svq.gemv_binplane(bp, Xd[0], o["p1"], N, K, P)
+        svq.gemm_smallm_w4a16(w4, Xd, o["Y"], M, N, K)
+        svq.gemm_smallm_binplane(bp, Xd, o["PY"], M, N, K, P)
+        svq.lmhead_argmax(hb, Xd, M, NH, K, o["idx"], o["mx"], ws)
+        svq.lmhead_verify_greedy(hb, Xd, M, NH, K, draft, o["vidx"], o["vmx"], o["tau"], ws)
+
+    eager = outputs()
+    run(eager)
+    torch.cuda.synchronize()
+    ref = {k: v.cpu() for k, v in eager.items()}
+
+    # The eager results against the oracle first.
+    y, a = oracle.linear_w4a16(codes, scales, X[:1])
+    check_close(ref["y1"].view(torch.bfloat16).double().numpy(), y[0], a[0], "gemv_w4a16")
+    y, a = oracle.linear_binplane(signs, alpha, X[:1])
+    check_close(ref["p1"].view(torch.bfloat16).double().numpy(), y[0], a[0], "gemv_binplane")
+    y, a = oracle.linear_w4a16(codes, scales, X)
+    check_close(ref["Y"].view(torch.bfloat16).double().numpy(), y, a, "gemm_w4a16")
+    y, a = oracle.linear_binplane(signs, alpha, X)
+    check_close(ref["PY"].view(torch.bfloat16).double().numpy(), y, a, "gemm_binplane")
+    rh = oracle.argmax_w4a16(hc, hs, X)
+    assert np.array_equal(rh["idx"], rows.astype(np.int32))
+    assert np.array_equal(ref["idx"].numpy(), rows.astype(np.int32))
+    assert np.array_equal(ref["vidx"].numpy(), rows.astype(np.int32))
+    want = oracle.verify_greedy(rows.astype(np.int32), draft.cpu().numpy())
+    assert want == 6 and int(ref["tau"][0]) == want
+    check_close(ref["mx"].double().numpy(), rh["zmax"], rh["amax"], "maxlogit")
+
+    graph_out = outputs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(graph_out)
+    torch.cuda.synchronize()
+    other = outputs()
+    for rep in range(4):
+        for v in graph_out.values():
+            v.fill_(-1)  # a fill kernel, not a memset node: outside the graph
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in graph_out.items():
+            assert torch.equal(v.cpu(), ref[k]), f"replay {rep}: {k} differs from the eager result"
+        run(other)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        for k, v in other.items():
+            assert torch.equal(v.cpu(), ref[k]), f"eager after replay {rep}: {k} differs"
+    del graph
