@@ -81,16 +81,20 @@ inline int env_int(const char* name, int lo, int hi, int dflt) {
 // than the memory system's bandwidth-latency product, and deeper rings were
 // slower (the M = 16 sign-plane head at 32768 rows, eight tiles a
 // workgroup: 26.4 us at a ring of 2, 28.7 at 3).  Workgroups of the M <= 16
-// mat-muls that own at most `shallow` tiles run without a ring (depth 1):
-// at three tiles each (N = 12288) that was 6% faster for the sign planes,
-// 3% for sa* and 1% for W4A16 than rings of 2 or 3 (the prefetch of later
-// tiles delays the first tile's activations and weights).
+// mat-muls that own at most `shallow` tiles run without a ring (depth 1).
+// Interleaved A/B runs of ring 2 against no ring (six rounds each, since a
+// partial last round of the ring no longer steps through empty tiles) gave:
+// * three tiles a workgroup (N = 12288): the ring wins (W4A16 -2.6%, sign
+//   planes -0.7%, sa* -1.4 to -4.5%);
+// * two tiles (N = 8192): no ring wins (the ring costs +1.1%, +2.7% and
+//   +3.4 to +4.6%), as the prefetch of the second tile delays the first
+//   tile's activations and weights.
 struct LaunchPref {
   int wgs_per_cu, max_depth, shallow;
 };
 constexpr LaunchPref kPrefGemv = {2, 2, 0};
-constexpr LaunchPref kPrefGemmW4 = {1, 2, 3};
-constexpr LaunchPref kPrefGemmPlanes = {1, 2, 3};
+constexpr LaunchPref kPrefGemmW4 = {1, 2, 2};
+constexpr LaunchPref kPrefGemmPlanes = {1, 2, 2};
 constexpr LaunchPref kPrefHeadM1 = {1, 2, 0};
 constexpr LaunchPref kPrefHeadM16 = {1, 2, 0};
 
