@@ -229,66 +229,131 @@ def snap_sa_scales(alpha_f16: np.ndarray, G: int = GROUP):
 
 
 # ---- device calls (torch tensors; bf16/fp16 values as int16/uint16 bits or bf16) --
+#
+# Every wrapper checks, before anything reaches the library, that each tensor
+# holds at least the bytes the call reads or writes (numel * element_size),
+# so an undersized tensor or a 1-byte dtype where 2-byte values are expected
+# raises ValueError instead of turning into out-of-bounds device accesses.
+# Shape errors the library itself reports (a size function returning 0) are
+# left to the library.
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _args(fn: str, *specs):
+    """Device pointers of the (tensor, bytes needed, name) specs, after
+    checking every tensor's size (all sizes first, then the pointers)."""
+    for t, need, what in specs:
+        if t is not None and need > 0 and _nbytes(t) < need:
+            raise ValueError(f"{fn}: {what} holds {_nbytes(t)} bytes, the call needs {need}")
+    return [_dev_ptr(t) for t, _, _ in specs]
+
+
+def _int4_bytes(N, K, G):
+    return int4_packed_bytes(N, K, G) if N >= 1 and K >= 1 else 0
+
+
+def _plane_bytes(N, K, P, G):
+    return binplane_packed_bytes(N, K, P, G) if N >= 1 and K >= 1 and 1 <= P <= 6 else 0
+
+
+def _sa_bytes(N, K, P, G):
+    return sa_packed_bytes(N, K, P, G) if N >= 1 and K >= 1 and 2 <= P <= 6 else 0
+
+
+def _rows(M, L):
+    return 2 * M * L if M >= 1 and L >= 1 else 0
+
 
 def gemv_w4a16(packed, x, y, N: int, K: int, G: int = GROUP, stream=None) -> None:
-    _check("gemv_w4a16", load().gemv_w4a16(_dev_ptr(packed), _dev_ptr(x), _dev_ptr(y), N, K, G, _stream(stream)))
+    fn = "gemv_w4a16"
+    pw, xp, yp = _args(fn, (packed, _int4_bytes(N, K, G), "packed"), (x, _rows(1, K), "x"), (y, _rows(1, N), "y"))
+    _check(fn, load().gemv_w4a16(pw, xp, yp, N, K, G, _stream(stream)))
 
 
 def gemv_binplane(packed, x, y, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
-    _check("gemv_binplane",
-           load().gemv_binplane(_dev_ptr(packed), _dev_ptr(x), _dev_ptr(y), N, K, G, P, _stream(stream)))
+    fn = "gemv_binplane"
+    pw, xp, yp = _args(fn, (packed, _plane_bytes(N, K, P, G), "packed"), (x, _rows(1, K), "x"),
+                       (y, _rows(1, N), "y"))
+    _check(fn, load().gemv_binplane(pw, xp, yp, N, K, G, P, _stream(stream)))
 
 
 def gemm_smallm_w4a16(packed, X, Y, M: int, N: int, K: int, G: int = GROUP, stream=None) -> None:
-    _check("gemm_smallm_w4a16",
-           load().gemm_smallm_w4a16(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, _stream(stream)))
+    fn = "gemm_smallm_w4a16"
+    pw, xp, yp = _args(fn, (packed, _int4_bytes(N, K, G), "packed"), (X, _rows(M, K), "X"), (Y, _rows(M, N), "Y"))
+    _check(fn, load().gemm_smallm_w4a16(pw, xp, yp, M, N, K, G, _stream(stream)))
 
 
 def gemm_smallm_binplane(packed, X, Y, M: int, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
-    _check("gemm_smallm_binplane",
-           load().gemm_smallm_binplane(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, P,
-                                       _stream(stream)))
+    fn = "gemm_smallm_binplane"
+    pw, xp, yp = _args(fn, (packed, _plane_bytes(N, K, P, G), "packed"), (X, _rows(M, K), "X"),
+                       (Y, _rows(M, N), "Y"))
+    _check(fn, load().gemm_smallm_binplane(pw, xp, yp, M, N, K, G, P, _stream(stream)))
 
 
 def gemv_sa(packed, x, y, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
-    _check("gemv_sa", load().gemv_sa(_dev_ptr(packed), _dev_ptr(x), _dev_ptr(y), N, K, G, P, _stream(stream)))
+    fn = "gemv_sa"
+    pw, xp, yp = _args(fn, (packed, _sa_bytes(N, K, P, G), "packed"), (x, _rows(1, K), "x"), (y, _rows(1, N), "y"))
+    _check(fn, load().gemv_sa(pw, xp, yp, N, K, G, P, _stream(stream)))
 
 
 def gemm_smallm_sa(packed, X, Y, M: int, N: int, K: int, P: int, G: int = GROUP, stream=None) -> None:
-    _check("gemm_smallm_sa",
-           load().gemm_smallm_sa(_dev_ptr(packed), _dev_ptr(X), _dev_ptr(Y), M, N, K, G, P, _stream(stream)))
+    fn = "gemm_smallm_sa"
+    pw, xp, yp = _args(fn, (packed, _sa_bytes(N, K, P, G), "packed"), (X, _rows(M, K), "X"), (Y, _rows(M, N), "Y"))
+    _check(fn, load().gemm_smallm_sa(pw, xp, yp, M, N, K, G, P, _stream(stream)))
+
+
+def _head_specs(M, N, K, X, argmax, maxlogit, row_ids):
+    m = M if M >= 1 else 0
+    return ((X, _rows(M, K), "X"), (row_ids, 4 * N if N >= 1 else 0, "row_ids"), (argmax, 4 * m, "argmax"),
+            (maxlogit, 4 * m, "maxlogit"))
+
+
+def _ws_size(workspace):
+    return 0 if workspace is None else _nbytes(workspace)
 
 
 def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace,
                   row_ids=None, G: int = GROUP, stream=None) -> None:
-    _check("lmhead_argmax",
-           load().lmhead_argmax(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, _dev_ptr(row_ids),
-                                _dev_ptr(argmax), _dev_ptr(maxlogit), _dev_ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    fn = "lmhead_argmax"
+    pw, xp, rp, ip, mp, wp = _args(fn, (packed, _int4_bytes(N, K, G), "packed"),
+                                   *_head_specs(M, N, K, X, argmax, maxlogit, row_ids), (workspace, 0, "workspace"))
+    _check(fn, load().lmhead_argmax(pw, xp, M, N, K, G, rp, ip, mp, wp, _ws_size(workspace), _stream(stream)))
 
 
 def lmhead_argmax_binplane(packed, X, M: int, N: int, K: int, P: int, argmax, maxlogit, workspace,
                            row_ids=None, G: int = GROUP, stream=None) -> None:
-    _check("lmhead_argmax_binplane",
-           load().lmhead_argmax_binplane(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, P, _dev_ptr(row_ids),
-                                         _dev_ptr(argmax), _dev_ptr(maxlogit), _dev_ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    fn = "lmhead_argmax_binplane"
+    pw, xp, rp, ip, mp, wp = _args(fn, (packed, _plane_bytes(N, K, P, G), "packed"),
+                                   *_head_specs(M, N, K, X, argmax, maxlogit, row_ids), (workspace, 0, "workspace"))
+    _check(fn, load().lmhead_argmax_binplane(pw, xp, M, N, K, G, P, rp, ip, mp, wp, _ws_size(workspace),
+                                             _stream(stream)))
 
 
 def lmhead_verify_greedy(packed, X, M: int, N: int, K: int, draft_ids, argmax, maxlogit, accept_len,
                          workspace, row_ids=None, G: int = GROUP, stream=None) -> None:
-    _check("lmhead_verify_greedy",
-           load().lmhead_verify_greedy(_dev_ptr(packed), _dev_ptr(X), M, N, K, G, _dev_ptr(row_ids),
-                                       _dev_ptr(draft_ids), _dev_ptr(argmax), _dev_ptr(maxlogit),
-                                       _dev_ptr(accept_len), _dev_ptr(workspace),
-                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+    fn = "lmhead_verify_greedy"
+    pw, xp, rp, ip, mp, dp, ap, wp = _args(
+        fn, (packed, _int4_bytes(N, K, G), "packed"), *_head_specs(M, N, K, X, argmax, maxlogit, row_ids),
+        (draft_ids, 4 * (M - 1) if M > 1 else 0, "draft_ids"), (accept_len, 4, "accept_len"),
+        (workspace, 0, "workspace"))
+    _check(fn, load().lmhead_verify_greedy(pw, xp, M, N, K, G, rp, dp, ip, mp, ap, wp, _ws_size(workspace),
+                                           _stream(stream)))
 
 
 def verify_greedy(target_ids, draft_ids, M: int, accept_len, stream=None) -> None:
-    _check("verify_greedy", load().verify_greedy(_dev_ptr(target_ids), _dev_ptr(draft_ids), M,
-                                                 _dev_ptr(accept_len), _stream(stream)))
+    fn = "verify_greedy"
+    tp, dp, ap = _args(fn, (target_ids, 4 * M if M >= 1 else 0, "target_ids"),
+                       (draft_ids, 4 * (M - 1) if M > 1 else 0, "draft_ids"), (accept_len, 4, "accept_len"))
+    _check(fn, load().verify_greedy(tp, dp, M, ap, _stream(stream)))
 
 
 def svq_stream_read(src, nbytes: int, sink, wgs_per_cu: int = 0, stream=None) -> None:
-    _check("svq_stream_read", load().svq_stream_read(_dev_ptr(src), nbytes, _dev_ptr(sink), wgs_per_cu,
-                                                     _stream(stream)))
+    fn = "svq_stream_read"
+    cus = 0
+    if sink is not None and getattr(sink, "is_cuda", False):
+        import torch
+        cus = torch.cuda.get_device_properties(sink.device).multi_processor_count
+    sp, kp = _args(fn, (src, nbytes if nbytes > 0 else 0, "src"), (sink, 8 * cus * 4, "sink"))
+    _check(fn, load().svq_stream_read(sp, nbytes, kp, wgs_per_cu, _stream(stream)))

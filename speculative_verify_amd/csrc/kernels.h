@@ -26,8 +26,11 @@
 //
 // Exact operands.  A nibble u = c + 8 becomes the bf16 value 128 + u with one
 // AND-OR (the high bits 0x43 form 2^7, the nibble fills the mantissa), so the
-// dot products see 136 + c exactly; the group sum of x times 136 is taken
-// back out before the group scale is applied in fp32.  A sign bit becomes the
+// dot products see 136 + c exactly.  The 136 is taken back out per group
+// before the scale is applied: the same chain of instructions, in the same
+// order, run once on the constant operand 136 gives the value subtracted, so
+// a group whose codes are all zero (decoded 136) cancels to exactly 0 and
+// otherwise only the two chains' fp32 rounding remains.  A sign bit becomes the
 // bf16 value +1 or -1 (0x3F80 with the sign bit set for b = -1) with one
 // shift and one AND-OR; the M <= 16 sign-plane tiles skip the shift (see
 // plane_operands) and the M = 1 ones read precomputed signed sums from LDS.
@@ -53,8 +56,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 constexpr uint32_t kInt4Magic = 0x43004300u;  // bf16 pair (128, 128)
-constexpr float kInt4Bias = 136.0f;           // 128 + 8: decoded value = 136 + c
 constexpr uint32_t kOnePair = 0x3F803F80u;    // bf16 pair (1, 1)
+constexpr uint32_t kInt4ZeroPair = 0x43084308u;  // bf16 pair (136, 136): two decoded zero codes
 
 struct ArgBest {
   float v;
@@ -312,15 +315,18 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Sum of the 32 activations a lane holds for each of its groups.
+// The M = 1 W4A16 chain of each of the lane's groups run on decoded zero
+// codes: 136 * (the lane's sum of x over the group), formed by exactly the
+// dot2 sequence w4a16_tile_partial applies to a tile, so the two agree bit
+// for bit wherever the tile's codes are zero.
 template <int GPW>
-__device__ __forceinline__ void lane_group_sums(const uint32_t (&xp)[GPW][16], float (&xs)[GPW]) {
+__device__ __forceinline__ void lane_zero_code_chains(const uint32_t (&xp)[GPW][16], float (&z)[GPW]) {
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s = dot2(xp[gi][j], kOnePair, s);
-    xs[gi] = s;
+    for (int j = 0; j < 16; ++j) s = dot2(kInt4ZeroPair, xp[gi][j], s);
+    z[gi] = s;
   }
 }
 
@@ -626,22 +632,22 @@ __device__ __forceinline__ int row_tile(int i) { return blockIdx.x + i * gridDim
 
 // ---------------------------------------------------------------------------
 // M = 1 mat-vec cores.  Each returns the lane's partial sum for row r over its
-// k sub-ranges of the wave's groups.  nxs[g] = -136 * (the lane's sum of x
-// over group g) starts each group's accumulator, which removes the +136
-// carried by every decoded code.
+// k sub-ranges of the wave's groups.  zc[g] (lane_zero_code_chains) is the
+// group's chain on zero codes; subtracting it removes the +136 carried by
+// every decoded code.
 template <int GPW>
 __device__ __forceinline__ float w4a16_tile_partial(const Int4Slot<GPW>& sl, const uint32_t (&xp)[GPW][16],
-                                                    const float (&nxs)[GPW], const PairDecode& magic) {
+                                                    const float (&zc)[GPW], const PairDecode& magic) {
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const uint32_t w[4] = {sl.c[gi].x, sl.c[gi].y, sl.c[gi].z, sl.c[gi].w};
-    float acc = nxs[gi];
+    float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc = dot2(int4_pair(w[t], i, magic), xp[gi][4 * t + i], acc);
-    part = fmaf(sl.s.bf16(gi), acc, part);
+    part = fmaf(sl.s.bf16(gi), acc - zc[gi], part);
   }
   return part;
 }
@@ -897,10 +903,8 @@ __global__ void __launch_bounds__(64 * MAXW)
   __shared__ ChunkStage<float, kChunkGemv, MAXW, 16> stage;
   uint32_t xp[GPW][16];
   expand_x<GPW>(xo, xp);
-  float nxs[GPW];
-  lane_group_sums<GPW>(xp, nxs);
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) nxs[gi] *= -kInt4Bias;
+  float zc[GPW];
+  lane_zero_code_chains<GPW>(xp, zc);
   const PairDecode magic = int4_decode();
 
   float best_v = -FLT_MAX;
@@ -909,7 +913,7 @@ __global__ void __launch_bounds__(64 * MAXW)
   auto step = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
     const int i = i0 + j;
-    const float part = sum_over_q(w4a16_tile_partial<GPW>(ring[j], xp, nxs, magic));
+    const float part = sum_over_q(w4a16_tile_partial<GPW>(ring[j], xp, zc, magic));
     stage.put(i, i < T, wave, lane, part);
     // Slot j is refilled only after its last use, so it keeps its registers.
     __builtin_amdgcn_sched_barrier(0);
@@ -1448,24 +1452,21 @@ __global__ void __launch_bounds__(64 * MAXW)
 // A = X[m = r][k = 32t + 8q + 0..7] (lane q, r) and B = W^T[k][n = r] from the
 // tile's dword t; D lands as D[m = 4q + i][n = r], i = 0..3.
 
-// Accumulator start per group: -136 * sum_k X[m][k] over the group for the
-// rows m = 4q + i (i = 0..3) whose outputs this lane's MFMA result holds.
-// Lane (q, r) sums its own 32 values of row r; sum_over_q completes row r's
-// group sum in every lane of that row; lane (q, r) then reads rows 4q + i
-// from lanes 4q + i (whose r is 4q + i).
+// The W4A16 MFMA chain of each group run on decoded zero codes (B = 136
+// everywhere): 136 * sum_k X[m][k] over the group for the rows m = 4q + i
+// whose outputs this lane's result holds, formed by the same four MFMAs, in
+// the same order and from the same zero start, as a tile's chain, so the two
+// agree bit for bit wherever the tile's codes are zero.  The value does not
+// depend on the row tile, so it is formed once per kernel.
 template <int GPW>
-__device__ __forceinline__ void x_row_group_init(const uint32_t (&xa)[GPW][16], int q, int g0, int KT,
-                                                 f32x4_t (&cinit)[GPW]) {
-  float xs[GPW];
-  lane_group_sums<GPW>(xa, xs);
+__device__ __forceinline__ void zero_code_chains(const uint32_t (&xa)[GPW][16], f32x4_t (&z)[GPW]) {
+  const uint32_t b[4] = {kInt4ZeroPair, kInt4ZeroPair, kInt4ZeroPair, kInt4ZeroPair};
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const float srow = sum_over_q(xs[gi]);
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = __shfl(srow, 4 * q + i);
-      cinit[gi][i] = g0 + gi < KT ? -kInt4Bias * v : 0.f;
-    }
+    for (int t = 0; t < 4; ++t) c = mfma16x16x32(&xa[gi][4 * t], b, c);
+    z[gi] = c;
   }
 }
 
@@ -1559,8 +1560,8 @@ __global__ void __launch_bounds__(64 * MAXW)
   } else {
     mask_x_pairs<GPW>(r, M, g0, KT, xa);
   }
-  f32x4_t cinit[GPW];
-  x_row_group_init<GPW>(xa, q, g0, KT, cinit);
+  f32x4_t zc[GPW];
+  zero_code_chains<GPW>(xa, zc);
   const PairDecode magic = int4_decode();
 
   RowBest4 best;
@@ -1583,7 +1584,7 @@ __global__ void __launch_bounds__(64 * MAXW)
     for (int g0c = 0; g0c < GPW; g0c += IL) {
       f32x4_t c[IL];
 #pragma unroll
-      for (int u = 0; u < IL; ++u) c[u] = cinit[g0c + u];
+      for (int u = 0; u < IL; ++u) c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1596,10 +1597,11 @@ __global__ void __launch_bounds__(64 * MAXW)
 #pragma unroll
       for (int u = 0; u < IL; ++u) {
         const float sc = ring[j].s.bf16(g0c + u);
-        yv.x = fmaf(sc, c[u][0], yv.x);
-        yv.y = fmaf(sc, c[u][1], yv.y);
-        yv.z = fmaf(sc, c[u][2], yv.z);
-        yv.w = fmaf(sc, c[u][3], yv.w);
+        const f32x4_t& z = zc[g0c + u];
+        yv.x = fmaf(sc, c[u][0] - z[0], yv.x);
+        yv.y = fmaf(sc, c[u][1] - z[1], yv.y);
+        yv.z = fmaf(sc, c[u][2] - z[2], yv.z);
+        yv.w = fmaf(sc, c[u][3] - z[3], yv.w);
       }
     }
     stage.put(i, i < T, wave, lane, yv);
@@ -1662,9 +1664,9 @@ __global__ void __launch_bounds__(64 * 8)
   uint32_t xa[2][GPW][16];
   transpose_x_rows<GPW>(xr0, xt[wave][0], lane, q, r, xa[0]);
   transpose_x_rows<GPW>(xr1, xt[wave][1], lane, q, r, xa[1]);
-  f32x4_t cinit[2][GPW];
-  x_row_group_init<GPW>(xa[0], q, g0, KT, cinit[0]);
-  x_row_group_init<GPW>(xa[1], q, g0, KT, cinit[1]);
+  f32x4_t zc[2][GPW];
+  zero_code_chains<GPW>(xa[0], zc[0]);
+  zero_code_chains<GPW>(xa[1], zc[1]);
   const PairDecode magic = int4_decode();
   RowBest4 unused;
 
@@ -1677,7 +1679,7 @@ __global__ void __launch_bounds__(64 * 8)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) c[mt][gi] = cinit[mt][gi];
+        for (int gi = 0; gi < GPW; ++gi) c[mt][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1694,10 +1696,11 @@ __global__ void __launch_bounds__(64 * 8)
         const float sc = ring[j].s.bf16(gi);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          yv[mt].x = fmaf(sc, c[mt][gi][0], yv[mt].x);
-          yv[mt].y = fmaf(sc, c[mt][gi][1], yv[mt].y);
-          yv[mt].z = fmaf(sc, c[mt][gi][2], yv[mt].z);
-          yv[mt].w = fmaf(sc, c[mt][gi][3], yv[mt].w);
+          const f32x4_t& z = zc[mt][gi];
+          yv[mt].x = fmaf(sc, c[mt][gi][0] - z[0], yv[mt].x);
+          yv[mt].y = fmaf(sc, c[mt][gi][1] - z[1], yv[mt].y);
+          yv[mt].z = fmaf(sc, c[mt][gi][2] - z[2], yv[mt].z);
+          yv[mt].w = fmaf(sc, c[mt][gi][3] - z[3], yv[mt].w);
         }
       }
       stage[0].put(i, i < T, wave, lane, yv[0]);

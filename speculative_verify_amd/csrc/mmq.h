@@ -26,9 +26,10 @@
 // needed until the block ends.
 //
 // Exact operands as in the M <= 16 kernel: nibble u = c + 8 decodes to the
-// bf16 value 136 + c, and each chain starts from -136 * sum_k X[m][k] over
-// the group, one MFMA chain per m-tile against the constant bf16 pair
-// (-136, -136), exact term by term.
+// bf16 value 136 + c, and the 136 is taken back out per group by subtracting
+// the same MFMA chain run on the constant pair (136, 136) (one chain per
+// m-tile and step, shared by the block's row tiles), so a group whose codes
+// are all zero cancels to exactly 0.
 #pragma once
 
 #include "kernels.h"
@@ -36,7 +37,6 @@
 namespace {
 
 constexpr int kMmqWaves = 8;
-constexpr uint32_t kMinus136Pair = 0xC308C308u;  // bf16 pair (-136, -136)
 
 // The R weight tiles of one step and their scales.
 template <int R>
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
   advance(xc);
 
   const PairDecode magic = int4_decode();
-  const uint32_t minus136[4] = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
+  const uint32_t zero_codes[4] = {kInt4ZeroPair, kInt4ZeroPair, kInt4ZeroPair, kInt4ZeroPair};
   f32x4_t acc[R][MT];
 #pragma unroll
   for (int rt = 0; rt < R; ++rt)
@@ -203,20 +203,23 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
             advance(wc);
           }
         }
-        f32x4_t corr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) corr = mfma16x16x32(a[t], minus136, corr);
+        // The zero-code chain and the R tiles' chains: the same four MFMAs
+        // from zero, so a tile's chain equals the zero-code one bit for bit
+        // where its codes are zero.
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         f32x4_t c[R];
 #pragma unroll
-        for (int rt = 0; rt < R; ++rt) c[rt] = corr;
+        for (int rt = 0; rt < R; ++rt) c[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+          z = mfma16x16x32(a[t], zero_codes, z);
 #pragma unroll
           for (int rt = 0; rt < R; ++rt) c[rt] = mfma16x16x32(a[t], bq[rt][t], c[rt]);
+        }
 #pragma unroll
         for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[rt][mi][e] = fmaf(sc[rt], c[rt][e], acc[rt][mi][e]);
+          for (int e = 0; e < 4; ++e) acc[rt][mi][e] = fmaf(sc[rt], c[rt][e] - z[e], acc[rt][mi][e]);
       }
       if (block_done) {
         // Every wave is at the same step, so this branch (and its barriers)

@@ -102,3 +102,57 @@ def test_no_device_is_a_hip_error_not_a_crash():
     rc = lib.gemv_w4a16(A, A, A, 16, 128, 128, None)
     assert rc == -6
     assert "hip" in lib.svq_last_error().decode().lower()
+
+
+# The Python binding checks every tensor's byte size against what the call
+# reads or writes before anything reaches the library: an undersized tensor
+# or a 1-byte dtype where 2-byte values are expected raises ValueError, and
+# no launch happens (these are CPU tensors, which never reach a launch).
+def _t(n, dtype=torch.int16):
+    return torch.zeros(n, dtype=dtype)
+
+
+N_, K_, P_ = 32, 256, 3
+
+
+@pytest.mark.parametrize("what,call", [
+    ("packed", lambda: svq.gemv_w4a16(_t(10, torch.uint8), _t(K_), _t(N_), N_, K_)),
+    ("x", lambda: svq.gemv_w4a16(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(K_, torch.uint8), _t(N_),
+                                 N_, K_)),
+    ("y", lambda: svq.gemv_w4a16(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(K_), _t(N_ - 1), N_, K_)),
+    ("packed", lambda: svq.gemv_binplane(_t(svq.binplane_packed_bytes(N_, K_, P_) - 1, torch.uint8), _t(K_),
+                                         _t(N_), N_, K_, P_)),
+    ("packed", lambda: svq.gemv_sa(_t(svq.sa_packed_bytes(N_, K_, P_) - 1, torch.uint8), _t(K_), _t(N_),
+                                   N_, K_, P_)),
+    ("X", lambda: svq.gemm_smallm_w4a16(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(16 * K_ - 1),
+                                        _t(16 * N_), 16, N_, K_)),
+    ("Y", lambda: svq.gemm_smallm_w4a16(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(16 * K_),
+                                        _t(16 * N_, torch.uint8), 16, N_, K_)),
+    ("Y", lambda: svq.gemm_smallm_binplane(_t(svq.binplane_packed_bytes(N_, K_, P_), torch.uint8), _t(40 * K_),
+                                           _t(39 * N_), 40, N_, K_, P_)),
+    ("X", lambda: svq.gemm_smallm_sa(_t(svq.sa_packed_bytes(N_, K_, P_), torch.uint8), _t(3 * K_), _t(4 * N_),
+                                     4, N_, K_, P_)),
+    ("argmax", lambda: svq.lmhead_argmax(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(4 * K_),
+                                         4, N_, K_, _t(3, torch.int32), _t(4, torch.float32), _t(4352, torch.uint8))),
+    ("maxlogit", lambda: svq.lmhead_argmax(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(4 * K_),
+                                           4, N_, K_, _t(4, torch.int32), _t(4, torch.int16),
+                                           _t(4352, torch.uint8))),
+    ("row_ids", lambda: svq.lmhead_argmax(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(4 * K_),
+                                          4, N_, K_, _t(4, torch.int32), _t(4, torch.float32),
+                                          _t(4352, torch.uint8), row_ids=_t(N_ - 1, torch.int32))),
+    ("packed", lambda: svq.lmhead_argmax_binplane(_t(100, torch.uint8), _t(K_), 1, N_, K_, P_,
+                                                  _t(1, torch.int32), _t(1, torch.float32), _t(4352, torch.uint8))),
+    ("draft_ids", lambda: svq.lmhead_verify_greedy(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(16 * K_),
+                                                   16, N_, K_, _t(14, torch.int32), _t(16, torch.int32),
+                                                   _t(16, torch.float32), _t(1, torch.int32),
+                                                   _t(4352, torch.uint8))),
+    ("accept_len", lambda: svq.lmhead_verify_greedy(_t(svq.int4_packed_bytes(N_, K_), torch.uint8), _t(16 * K_),
+                                                    16, N_, K_, _t(15, torch.int32), _t(16, torch.int32),
+                                                    _t(16, torch.float32), _t(0, torch.int32),
+                                                    _t(4352, torch.uint8))),
+    ("target_ids", lambda: svq.verify_greedy(_t(4, torch.int32), _t(4, torch.int32), 5, _t(1, torch.int32))),
+    ("src", lambda: svq.svq_stream_read(_t(8, torch.uint8), 16, _t(8, torch.int32))),
+])
+def test_binding_rejects_undersized_tensors(what, call):
+    with pytest.raises(ValueError, match=what):
+        call()
