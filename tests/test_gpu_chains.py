@@ -56,6 +56,30 @@ def check_close(y_gpu, y, a, what):
                            f"{(err / tol).max():.3g} at {np.unravel_index((err / tol).argmax(), err.shape)}")
 
 
+def check_close_or_rounded(y_gpu, y, a, what):
+    """The bound, or, where half a bf16 ulp of the exact value exceeds it (|y|
+    close to sum |w x|, so that no bf16 value can meet it), the bf16
+    round-to-nearest-even of the exact value; either bf16 neighbour only when
+    the exact value lies within the bound of their midpoint."""
+    tol = REL * a + ABS
+    ok = np.abs(y_gpu - y) <= tol
+    ay = np.abs(y)
+    pos = ay > 0
+    e = np.floor(np.log2(np.where(pos, ay, 1.0)))
+    ulp = np.exp2(e - 7)
+    lo = np.floor(ay / ulp) * ulp
+    hi = lo + ulp
+    mid = lo + ulp / 2
+    even_lo = (np.floor(ay / ulp) % 2) == 0
+    rne = np.where(ay < mid, lo, np.where(ay > mid, hi, np.where(even_lo, lo, hi)))
+    g = np.abs(y_gpu)
+    same_sign = np.sign(y_gpu) == np.sign(y)
+    rounded = pos & same_sign & ((g == rne) | ((np.abs(ay - mid) <= tol) & ((g == lo) | (g == hi))))
+    bad = ~(ok | rounded)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} neither within the bound nor correctly rounded; "
+                           f"first at {np.argwhere(bad)[0]}")
+
+
 def weights(rng, N, K, scale):
     """bf16 bits [N][K], w ~ N(0, scale^2): stands in for trained weights."""
     return synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * scale).astype(np.float32))
@@ -173,7 +197,9 @@ def test_zero_code_rows_are_exact(M):
     blob = dev(svq.pack_int4_grouped(codes, scales))
     got = run_w4a16(blob, X, N, K)
     assert (got[:, :128] == 0).all(), f"{int((got[:, :128] != 0).sum())} all-zero-code outputs are not 0"
-    check_close(got, Y, A, f"zero-code rows M={M}")
+    # A sparse row whose nonzero codes meet an outlier has |y| close to
+    # sum |w x|: there the bf16 output's own rounding can exceed the bound.
+    check_close_or_rounded(got, Y, A, f"zero-code rows M={M}")
 
 
 @pytest.mark.parametrize("M", [1, 16])
