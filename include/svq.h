@@ -322,6 +322,28 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * lmhead_argmax_noalloc -- DEVICE pointers, asynchronous on `stream`.
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call and results as lmhead_argmax, without the workspace argument.  The
+ * argmax completion state lives in a static device array of the library
+ * (4352 bytes per GPU, held until the process ends); the call itself
+ * allocates nothing.  On the first call on a device the array's address is
+ * looked up and the array is cleared by a kernel on `stream`, ordered before
+ * the head; every completed call leaves it zero again.
+ *   X, row_ids, argmax, maxlogit  as lmhead_argmax
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from different threads) race and must
+ * not be issued.
+ * Errors: as lmhead_argmax without WORKSPACE; SHAPE for M outside 1..16 (the
+ * largest block the array's state covers); HIP if the array's address cannot
+ * be obtained.
+ */
+int lmhead_argmax_noalloc(const uint8_t* packed, const uint16_t* X, int32_t M,
+                          int64_t N, int64_t K, int32_t G, const int32_t* row_ids,
+                          int32_t* argmax, float* maxlogit, void* stream);
+
+/*
  * lmhead_argmax_binplane -- DEVICE pointers, asynchronous on `stream`.
  * lmhead_argmax for a head stored as P sign planes (ShiftAddQwen README,
  * Method/Format; the MTP study sec. 3.3 for the trimmed head):

@@ -13,7 +13,8 @@ Functions (same names as the C ABI):
   snap_sa_scales                             host numpy arrays
   gemv_w4a16, gemv_binplane, gemv_sa, gemm_smallm_w4a16,
   gemm_smallm_binplane, gemm_smallm_sa,
-  lmhead_argmax, lmhead_argmax_binplane, lmhead_verify_greedy, verify_greedy,
+  lmhead_argmax, lmhead_argmax_noalloc, lmhead_argmax_binplane,
+  lmhead_verify_greedy, verify_greedy,
   svq_stream_read                            torch CUDA tensors
 """
 from __future__ import annotations
@@ -29,7 +30,7 @@ __all__ = [
     "pack_binary_planes", "unpack_binary_planes", "pack_sa", "unpack_sa", "quantize_int4_frozen",
     "fit_binary_planes", "snap_sa_scales", "gemv_w4a16",
     "gemv_binplane", "gemv_sa", "gemm_smallm_w4a16", "gemm_smallm_binplane", "gemm_smallm_sa", "lmhead_argmax", "lmhead_argmax_binplane",
-    "lmhead_verify_greedy",
+    "lmhead_verify_greedy", "lmhead_argmax_noalloc",
     "verify_greedy", "svq_stream_read",
 ]
 
@@ -83,6 +84,7 @@ def load():
         "gemm_smallm_w4a16": ([V, V, V, I32, I64, I64, I32, V], ctypes.c_int),
         "gemm_smallm_binplane": ([V, V, V, I32, I64, I64, I32, I32, V], ctypes.c_int),
         "lmhead_argmax": ([V, V, I32, I64, I64, I32, V, V, V, V, SZ, V], ctypes.c_int),
+        "lmhead_argmax_noalloc": ([V, V, I32, I64, I64, I32, V, V, V, V], ctypes.c_int),
         "lmhead_verify_greedy": ([V, V, I32, I64, I64, I32, V, V, V, V, V, V, SZ, V], ctypes.c_int),
         "lmhead_argmax_binplane": ([V, V, I32, I64, I64, I32, I32, V, V, V, V, SZ, V], ctypes.c_int),
         "verify_greedy": ([V, V, I32, V, V], ctypes.c_int),
@@ -320,6 +322,14 @@ def lmhead_argmax(packed, X, M: int, N: int, K: int, argmax, maxlogit, workspace
     pw, xp, rp, ip, mp, wp = _args(fn, (packed, _int4_bytes(N, K, G), "packed"),
                                    *_head_specs(M, N, K, X, argmax, maxlogit, row_ids), (workspace, 0, "workspace"))
     _check(fn, load().lmhead_argmax(pw, xp, M, N, K, G, rp, ip, mp, wp, _ws_size(workspace), _stream(stream)))
+
+
+def lmhead_argmax_noalloc(packed, X, M: int, N: int, K: int, argmax, maxlogit, row_ids=None, G: int = GROUP,
+                          stream=None) -> None:
+    fn = "lmhead_argmax_noalloc"
+    pw, xp, rp, ip, mp = _args(fn, (packed, _int4_bytes(N, K, G), "packed"),
+                               *_head_specs(M, N, K, X, argmax, maxlogit, row_ids))
+    _check(fn, load().lmhead_argmax_noalloc(pw, xp, M, N, K, G, rp, ip, mp, _stream(stream)))
 
 
 def lmhead_argmax_binplane(packed, X, M: int, N: int, K: int, P: int, argmax, maxlogit, workspace,

@@ -262,12 +262,19 @@ inline HeadOut with_levels(HeadOut ho, const Shape& sh) {
   return ho;
 }
 
-inline int check_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
-                      int32_t G, int32_t P, const HeadOut& ho, void* workspace, size_t workspace_bytes) {
+// The head's arguments other than its workspace.
+inline int check_head_args(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
+                           int32_t G, int32_t P, const HeadOut& ho) {
   if (int rc = check_linear(fn, packed, X, ho.idx, M, N, K, G, P)) return rc;
   if (!ho.max) return svq::fail(SVQ_ERR_NULL, "%s: NULL maxlogit", fn);
   if (misaligned(ho.idx, 4) || misaligned(ho.max, 4) || (ho.row_ids && misaligned(ho.row_ids, 4)))
     return svq::fail(SVQ_ERR_ALIGN, "%s: argmax, maxlogit and row_ids must be 4-byte aligned", fn);
+  return SVQ_OK;
+}
+
+inline int check_head(const char* fn, const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K,
+                      int32_t G, int32_t P, const HeadOut& ho, void* workspace, size_t workspace_bytes) {
+  if (int rc = check_head_args(fn, packed, X, M, N, K, G, P, ho)) return rc;
   if (!workspace || workspace_bytes < svq_lmhead_workspace_bytes(M))
     return svq::fail(SVQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, svq_lmhead_workspace_bytes(M),
                      workspace ? workspace_bytes : (size_t)0);

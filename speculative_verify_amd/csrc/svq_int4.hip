@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "launch.h"
@@ -37,6 +38,47 @@ int launch_head_w4a16(const char* fn, const uint8_t* packed, const uint16_t* X, 
     });
   }
   return launched(fn);
+}
+
+// Scratch of lmhead_argmax_noalloc: the argmax completion state (per-row
+// keys and counters, the layout of a head workspace) in device memory the
+// library owns, one copy per GPU, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, and that pointer is what the
+// kernels receive.
+constexpr size_t kScratchBytes = kWsBytes;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void __launch_bounds__(256) k_clear_scratch(uint4* __restrict__ p, int n16) {
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The current device's scratch address.  On the first call on a device the
+// address is looked up and the scratch is cleared by a kernel on `st`,
+// ordered before the caller's launch; every head launch leaves it zero again.
+int device_scratch(const char* fn, hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return svq::fail(SVQ_ERR_HIP, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return svq::fail(SVQ_ERR_HIP, "%s: hipGetSymbolAddress: %s", fn, hipGetErrorString(e));
+    hipLaunchKernelGGL(k_clear_scratch, dim3(1), dim3(256), 0, st, reinterpret_cast<uint4*>(p),
+                       (int)(kScratchBytes / 16));
+    if (int rc = launched(fn)) return rc;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SVQ_OK;
 }
 
 }  // namespace
@@ -130,6 +172,21 @@ int lmhead_argmax(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N
                   void* stream) {
   return launch_head_w4a16("lmhead_argmax", packed, X, M, N, K, G, HeadOut{row_ids, argmax, maxlogit, nullptr, nullptr},
                      workspace, workspace_bytes, stream);
+}
+
+int lmhead_argmax_noalloc(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,
+                          const int32_t* row_ids, int32_t* argmax, float* maxlogit, void* stream) {
+  const char* fn = "lmhead_argmax_noalloc";
+  svq::clear_error();
+  if (M < 1 || M > SVQ_MAX_M || svq_lmhead_workspace_bytes(M) > kScratchBytes)
+    return svq::fail(SVQ_ERR_SHAPE, "%s: M=%d must be in 1..%d (the static scratch holds %zu bytes of argmax state)",
+                     fn, M, SVQ_MAX_M, kScratchBytes);
+  // Every argument check runs before the scratch is touched.
+  const HeadOut ho{row_ids, argmax, maxlogit, nullptr, nullptr};
+  if (int rc = check_head_args(fn, packed, X, M, N, K, G, 0, ho)) return rc;
+  void* ws = nullptr;
+  if (int rc = device_scratch(fn, reinterpret_cast<hipStream_t>(stream), &ws)) return rc;
+  return launch_head_w4a16(fn, packed, X, M, N, K, G, ho, ws, kScratchBytes, stream);
 }
 
 int lmhead_verify_greedy(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,

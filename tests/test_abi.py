@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["pack_int4_grouped", "pack_binary_planes", "gemv_w4a16", "gemv_binplane",
                  "gemm_smallm_w4a16", "gemm_smallm_binplane", "lmhead_argmax", "lmhead_verify_greedy",
-                 "verify_greedy", "svq_last_error", "pack_sa", "gemv_sa", "gemm_smallm_sa"]:
+                 "verify_greedy", "svq_last_error", "pack_sa", "gemv_sa", "gemm_smallm_sa", "lmhead_argmax_noalloc"]:
         assert want in names
 
 
@@ -87,6 +87,10 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.gemm_smallm_sa(A, A, A, 65, 16, 256, 64, 2, None), -2),
     (lambda l: l.gemm_smallm_sa(A, A, A, 4, 16, 256, 512, 2, None), -2),
     (lambda l: l.gemm_smallm_sa(A, A + 2, A, 4, 16, 256, 256, 2, None), -3),
+    (lambda l: l.lmhead_argmax_noalloc(A, A, 17, 16, 128, 128, None, A, A, None), -2),
+    (lambda l: l.lmhead_argmax_noalloc(A, A, 0, 16, 128, 128, None, A, A, None), -2),
+    (lambda l: l.lmhead_argmax_noalloc(A, A, 2, 16, 128, 128, None, A, None, None), -1),
+    (lambda l: l.lmhead_argmax_noalloc(A, A, 2, 16, 128, 128, A + 2, A, A, None), -3),
     (lambda l: l.svq_stream_read(A, 100, A, 0, None), -2),
     (lambda l: l.svq_stream_read(A, 1024, A, 9, None), -2),
 ])
