@@ -18,7 +18,8 @@ step.  Each step reads ~1.3 GB of distinct weights, far more than the 256 MB
 last-level cache, so every call streams its weights from HBM.
 
 Also timed, each call on its own but outside the step (so the step and its
-`value` keep their definition): the sa* storage of sign planes (u8 scale
+`value` keep their definition): the tiny W4A16 mat-vec (M=1 K=256 N=512,
+69 KB: launch-bound, so microseconds only); the sa* storage of sign planes (u8 scale
 codes per plane and group, one fp16 d per 256-weight super-block) for
 decode and verify, P=3, groups of 64 and 128; and W4A16 blocks of M=32 and
 M=64 rows (a prefill chunk, the kernel for 16 < M <= 64).
@@ -39,6 +40,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+# The GPU's clocks settle over tens of milliseconds of load, so every timed
+# series follows at least this much untimed load of the same work, whatever
+# --warmup says (a few warm-up steps alone time part of the ramp).
+WARM_S = 0.05
+# Copies of a launch-bound call's inputs: it is timed for its latency, not
+# for bandwidth, so its inputs are not spread beyond the last-level cache.
+LAUNCH_BOUND_COPIES = 64
 K = 4096
 G = 128
 
@@ -147,10 +155,29 @@ def build_step(svq, synth, torch):
 
 
 def build_extra(svq, synth, torch):
-    """The calls timed alone, outside the step, in build_step's format: sa*
-    storage, W4A16 blocks of 32 and 64 rows, and the sign-plane LM head."""
+    """The calls timed alone, outside the step, in build_step's format: the
+    tiny W4A16 mat-vec (M=1 K=256 N=512, launch-bound: microseconds only),
+    sa* storage, W4A16 blocks of 32 and 64 rows, and the sign-plane LM head."""
+    import numpy as np
+
     calls = []
     seed = [500]
+
+    def tiny():
+        # Drawn on the host (the device generator needs K/128 a multiple of
+        # 4) with the workload's distributions, packed by the library.
+        case = synth.TINY_W4A16
+        codes, scales, x = synth.make_w4a16(case, 0)
+        blob0 = torch.from_numpy(svq.pack_int4_grouped(codes, scales)).cuda()
+        x0 = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+
+        def make():
+            blob, xd = blob0.clone(), x0.clone()
+            y = torch.empty((1, case.N), dtype=torch.int16, device="cuda")
+            return lambda: svq.gemv_w4a16(blob, xd, y, case.N, case.K)
+
+        nbytes = case.N * case.K // 2 + case.N * (case.K // G) * 2 + case.K * 2 + case.N * 2
+        calls.append((f"gemv_w4a16_m1_k{case.K}_n{case.N}", nbytes, make(), make))
 
     def sa(M, N, P, Gs):
         def make():
@@ -204,6 +231,7 @@ def build_extra(svq, synth, torch):
 
         calls.append((f"lmhead_argmax_binplane_p{P}_m{M}_n{N}", alg_bytes_head_binplane(M, N, P), make(), make))
 
+    tiny()
     sa(1, 12288, 3, 128)
     sa(16, 4096, 3, 128)
     sa(16, 12288, 3, 128)
@@ -219,6 +247,21 @@ def build_extra(svq, synth, torch):
     w4(1, 4096)
     bp1(4096, 3)
     return calls
+
+
+def warm_up(torch, run, min_iters=0, min_s=WARM_S):
+    """Untimed runs of `run` until at least min_iters of them and min_s
+    seconds have passed; returns (seconds, runs)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_iters or time.perf_counter() - t0 < min_s:
+        run()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()  # keep the host within a few runs of the GPU
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, n
 
 
 def capture_series(torch, fns, n):
@@ -267,6 +310,7 @@ def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 
         torch.cuda.synchronize()
         runs = [lambda v=v: svq.svq_stream_read(v, nbytes, sink, w) for v in views]
         graph = capture_series(torch, runs, iters)
+        warm_up(torch, graph.replay, min_s=WARM_S / 5)
         us = time_replay(torch, graph, stream, iters)
         del graph
         best = max(best, nbytes / (us * 1e-6) / 1e9)
@@ -362,8 +406,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # About 50 ms of untimed steps: the GPU's clocks settle over tens of
-    # milliseconds of load, and a short warm-up times part of that ramp.
+    # Untimed steps before the timed ones; at least WARM_S seconds of steps
+    # run in any case.
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -386,10 +430,11 @@ def main():
     step_bytes = sum(c[1] for c in calls)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
+    def one_step():
         for c in calls:
             c[2]()
-    torch.cuda.synchronize()
+
+    warm_step_s, warm_steps = warm_up(torch, one_step, min_iters=args.warmup)
 
     # The step throughput: K steps back to back, no events between calls.
     stream = torch.cuda.current_stream()
@@ -414,13 +459,17 @@ def main():
     # host path (argument marshalling, the runtime's launch) can take longer
     # than a small kernel runs, and the series would time the host.
     kernels = {}
+    launch_bound = {c[0] for c in extra if c[0].startswith("gemv_w4a16_m1_k256")}
     for name, nbytes, fn, fresh in calls + extra:
         copies = max(2, -(-2 * LLC_BYTES // nbytes))
+        if name in launch_bound:
+            copies = LAUNCH_BOUND_COPIES
         rot = [fn] + [fresh() for _ in range(copies - 1)]
         for f in rot[:3]:
             f()
         torch.cuda.synchronize()
         graph = capture_series(torch, rot, args.steps)
+        warm_up(torch, graph.replay)
         # Five timed replays; the median is reported (one alone varies by a
         # few percent from run to run).
         us = sorted(time_replay(torch, graph, stream, args.steps) for _ in range(5))[2]
@@ -432,6 +481,7 @@ def main():
             fn()
         torch.cuda.synchronize()
         graph = capture_series(torch, [fn], args.steps)
+        warm_up(torch, graph.replay, min_s=WARM_S / 5)
         hot_us = time_replay(torch, graph, stream, args.steps)
         del graph
         gbps = nbytes / (us * 1e-6) / 1e9
@@ -441,6 +491,11 @@ def main():
     extra_names = {c[0] for c in extra}
     for name in extra_names:
         kernels[name]["in_step"] = False
+    for name in launch_bound:
+        # Launch-bound: a latency figure; its bytes per second mean nothing.
+        kernels[name]["launch_bound"] = True
+        for k in ("GBps", "frac_hbm_peak"):
+            kernels[name].pop(k, None)
     dom = max((n for n in kernels if n not in extra_names), key=lambda n: kernels[n]["us"])
     dom_us, dom_bytes = kernels[dom]["us"], kernels[dom]["bytes"]
     dom_gbps = kernels[dom]["GBps"]
@@ -455,6 +510,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": {"steps": warm_steps, "step_s": round(warm_step_s, 4), "per_call_series_s": WARM_S},
         "ms_per_step": round(ms_per_step, 4),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
@@ -503,6 +559,8 @@ def main():
         # The same-size cold streaming read: what a pure read of each call's
         # bytes achieves with this launch overhead and start-up latency.
         for name, nbytes, _, _ in calls + extra:
+            if name in launch_bound:
+                continue
             ceil = stream_read_ceiling(svq, torch, nbytes)
             kernels[name]["ceiling_GBps"] = round(ceil, 1)
             kernels[name]["frac_of_ceiling"] = round(kernels[name]["GBps"] / ceil, 4)
