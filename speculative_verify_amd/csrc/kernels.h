@@ -571,8 +571,8 @@ __device__ __forceinline__ void load_sa_tile(SaSlot<GPW, P, G>& sl, const SaView
   load_run<GPW >= 4 ? 4 : 2>(b.d, ((uint32_t)(row * (b.KT4 / 2) + g0 / 2) * 2u) | oob, &sl.d);
 }
 
-// Activation staging for the 8-wave M <= 16 mat-muls (the 16-wave shapes,
-// with 128 registers a lane, keep load_x_pairs above).  Loading xp directly
+// Activation staging for the full-register M <= 16 mat-muls (the lean
+// shapes keep load_x_pairs above).  Loading xp directly
 // gives the 16 lanes of a quarter-wave 16 different rows, i.e. 16 cache
 // lines per quarter; instead a quarter-wave loads one row's 256 bytes
 // of a column tile (lane: row 4 u + lane / 16, 16-byte chunk lane % 16), and
@@ -724,6 +724,15 @@ constexpr int kChunkGemv = 16;  // tiles per chunk, M = 1 kernels
 // Tiles per chunk of the M <= 16 kernels (bounded by LDS: 1 KiB per wave and tile).
 template <int MAXW>
 constexpr int chunk_gemm() { return MAXW <= 8 ? 4 : 2; }
+
+// The M <= 16 mat-muls' full-register forms (X loaded coalesced and
+// transposed through LDS, interleaved MFMA chains, the one-instruction sign
+// decode) need the activations of GPW column tiles and the ring in the
+// registers of a wave: 256 a lane at eight waves.  The sixteen-wave shapes
+// (K above 4096, four column tiles a wave, 128 registers a lane) use the
+// lean forms.
+template <int GPW, int MAXW>
+constexpr bool mma_fast_shape() { return GPW * MAXW <= 32; }
 
 template <class V, int C, int MAXW, int L>
 struct ChunkStage {
@@ -1106,11 +1115,11 @@ struct PlaneFmt {
                                                   const PairDecode& one) {
     return binplane_tile_partial<GPW, P>(sl, xp, one);
   }
-  // MFMA tiles.  Up to eight waves (256 registers a lane): the activations
+  // MFMA tiles.  Full-register shapes (mma_fast_shape): the activations
   // with the pairs at the +-1 positions negated, and per group the chain
   // start -(sum x + sum c x) of the rows 4q + i this lane's results hold
-  // (see plane_operands).  The 16-wave shapes (128 registers) keep the two
-  // instructions per pair of sign_pair and chains started at zero.
+  // (see plane_operands).  The lean shapes keep the two instructions per
+  // pair of sign_pair and chains started at zero.
   template <int GPW>
   struct MmaFast {
     f32x4_t cinit[GPW];
@@ -1120,11 +1129,11 @@ struct PlaneFmt {
     PairDecode one;
   };
   template <int GPW, int MAXW>
-  using MmaX = std::conditional_t<(MAXW <= 8), MmaFast<GPW>, MmaLean>;
+  using MmaX = std::conditional_t<mma_fast_shape<GPW, MAXW>(), MmaFast<GPW>, MmaLean>;
 
   template <int GPW, int MAXW>
   static __device__ __forceinline__ void prepare_mma(uint32_t (&xa)[GPW][16], int q, MmaX<GPW, MAXW>& mx) {
-    if constexpr (MAXW <= 8) {
+    if constexpr (mma_fast_shape<GPW, MAXW>()) {
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi) {
         xa[gi][11] ^= 0x80008000u;
@@ -1151,7 +1160,7 @@ struct PlaneFmt {
   static __device__ __forceinline__ float4 mma(const Slot<GPW>& sl, const uint32_t (&xa)[GPW][16],
                                                const MmaX<GPW, MAXW>& mx) {
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (MAXW <= 8) {
+    if constexpr (mma_fast_shape<GPW, MAXW>()) {
       if constexpr (P <= 4) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
@@ -1251,11 +1260,11 @@ struct SaFmt {
                                                   const PairDecode& one) {
     return sa_tile_partial<GPW, P, G>(sl, xp, one);
   }
-  // MFMA tiles.  Up to eight waves: the sign decode of PlaneFmt (one AND-OR
+  // MFMA tiles.  Full-register shapes: the sign decode of PlaneFmt (one AND-OR
   // per pair, chains ending at minus each plane's signed sum over a group,
   // or over each half of a group at G = 64, where the two halves take their
   // own codes), each chain weighted by its code and the super-block's sum by
-  // d.  The 16-wave shapes keep the B = a * b pairs: there every plane and
+  // d.  The lean shapes keep the B = a * b pairs: there every plane and
   // group of a super-block accumulates in one chain that d scales once (a
   // code a <= 255 is exact in bf16, so a * b * x is an exact product).
   template <int GPW>
@@ -1267,11 +1276,11 @@ struct SaFmt {
     PairDecode one;
   };
   template <int GPW, int MAXW>
-  using MmaX = std::conditional_t<(MAXW <= 8), MmaFast<GPW>, MmaLean>;
+  using MmaX = std::conditional_t<mma_fast_shape<GPW, MAXW>(), MmaFast<GPW>, MmaLean>;
 
   template <int GPW, int MAXW>
   static __device__ __forceinline__ void prepare_mma(uint32_t (&xa)[GPW][16], int q, MmaX<GPW, MAXW>& mx) {
-    if constexpr (MAXW <= 8) {
+    if constexpr (mma_fast_shape<GPW, MAXW>()) {
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi) {
         xa[gi][11] ^= 0x80008000u;
@@ -1297,7 +1306,7 @@ struct SaFmt {
                                                const MmaX<GPW, MAXW>& mx) {
     constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (MAXW <= 8) {
+    if constexpr (mma_fast_shape<GPW, MAXW>()) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1532,9 +1541,10 @@ __global__ void __launch_bounds__(64 * MAXW)
   const BlobView bv = int4_view(blob, KT, NT);
   const int T = tiles_of_wg(NT);
 
-  // Up to 8 waves, X comes in coalesced and is transposed through LDS; the
-  // 16-wave shapes (128 registers a lane) load it in operand order directly.
-  constexpr bool kRowsX = MAXW <= 8;
+  // In the full-register shapes X comes in coalesced and is transposed
+  // through LDS; the lean ones (16 waves of four column tiles, 128
+  // registers a lane) load it in operand order directly.
+  constexpr bool kRowsX = mma_fast_shape<GPW, MAXW>();
   XRows<kRowsX ? GPW : 1> xrows;
   uint32_t xa[GPW][16];
   if constexpr (kRowsX)
@@ -1575,11 +1585,11 @@ __global__ void __launch_bounds__(64 * MAXW)
     constexpr int j = decltype(jc)::value;
     const int i = i0 + j;
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
-    // One MFMA chain per group.  Up to eight waves the groups' chains are
-    // interleaved k block by k block, so consecutive MFMAs are independent
-    // and the matrix core need not wait for each result before the next
-    // issue; the 16-wave shapes (128 registers) run them one after another.
-    constexpr int IL = MAXW <= 8 ? GPW : 1;  // chains in flight
+    // One MFMA chain per group.  In the full-register shapes the groups'
+    // chains are interleaved k block by k block, so consecutive MFMAs are
+    // independent and the matrix core need not wait for each result before
+    // the next issue; the lean shapes run them one after another.
+    constexpr int IL = mma_fast_shape<GPW, MAXW>() ? GPW : 1;  // chains in flight
 #pragma unroll
     for (int g0c = 0; g0c < GPW; g0c += IL) {
       f32x4_t c[IL];
@@ -1733,9 +1743,10 @@ __global__ void __launch_bounds__(64 * MAXW)
   const typename F::View bv = F::view(blob, KT, NT);
   const int T = tiles_of_wg(NT);
 
-  // Up to 8 waves, X comes in coalesced and is transposed through LDS; the
-  // 16-wave shapes (128 registers a lane) load it in operand order directly.
-  constexpr bool kRowsX = MAXW <= 8;
+  // In the full-register shapes X comes in coalesced and is transposed
+  // through LDS; the lean ones (16 waves of four column tiles, 128
+  // registers a lane) load it in operand order directly.
+  constexpr bool kRowsX = mma_fast_shape<GPW, MAXW>();
   XRows<kRowsX ? GPW : 1> xrows;
   uint32_t xa[GPW][16];
   if constexpr (kRowsX)

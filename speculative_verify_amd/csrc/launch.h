@@ -89,6 +89,12 @@ inline int env_int(const char* name, int lo, int hi, int dflt) {
 // * two tiles (N = 8192): no ring wins (the ring costs +1.1%, +2.7% and
 //   +3.4 to +4.6%), as the prefetch of the second tile delays the first
 //   tile's activations and weights.
+// K up to 4096 runs on eight waves of four column tiles.  Sixteen waves of
+// two column tiles (the full-register form at 128 registers a lane) were
+// measured and dropped: every M <= 16 mat-mul ran 7-16% slower (interleaved
+// A/B runs after a 50 ms warm-up, W4A16, sign planes and sa* at N = 4096 and
+// 12288): VALU and MFMA already keep the SIMDs busy once the data arrives,
+// and twice the waves double the per-wave prologue and the cross-wave sums.
 struct LaunchPref {
   int wgs_per_cu, max_depth, shallow;
 };
@@ -119,7 +125,15 @@ inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* 
   return SVQ_OK;
 }
 
+// Set by dispatch() when a planned launch is wider than every kernel shape it
+// may instantiate (the launch is then skipped); reported by launched().
+inline thread_local bool g_shape_mismatch = false;
+
 inline int launched(const char* fn) {
+  if (g_shape_mismatch) {
+    g_shape_mismatch = false;
+    return svq::fail(SVQ_ERR_SHAPE, "%s: no kernel shape for the planned launch", fn);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return svq::fail(SVQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return SVQ_OK;
@@ -172,6 +186,10 @@ void dispatch_r(int R, L&& launch) {
 template <int MAXD = 6, int MAXD16 = 1, class L>
 void dispatch(const Shape& sh, L&& launch) {
   auto depth = [&](auto G, auto W, auto DM) {
+    if (sh.waves > decltype(W)::value) {  // the kernel's launch bounds would not hold
+      g_shape_mismatch = true;
+      return;
+    }
     constexpr int dm = decltype(DM)::value < MAXD ? decltype(DM)::value : MAXD;
     if constexpr (dm >= 6)
       if (sh.depth >= 6) return launch(G, W, ic<6>{});
@@ -220,12 +238,15 @@ void dispatch_group(int G, L&& launch) {
 #define SVQ_KARGS(G, W, D) decltype(G)::value, decltype(W)::value, decltype(D)::value
 
 // Deepest ring the sign-plane kernels keep in registers without spilling:
-// a slot holds P sign dwords and P scale runs per group.
-constexpr int max_depth_planes(int P) { return P <= 4 ? 6 : P == 5 ? 5 : 4; }
+// a slot holds P sign dwords and P scale runs per group.  The sixteen-wave
+// shapes (K above 4096) take MAXD16 (one slot).
+constexpr int max_depth_planes(int P, int W) { return W > 8 ? 1 : P <= 4 ? 6 : P == 5 ? 5 : 4; }
 // Template arguments of the sign-plane kernels for format F.
 #define SVQ_KARGS_F(F, G, W, D)                                                                     \
   F, decltype(G)::value, decltype(W)::value,                                                       \
-      (decltype(D)::value < max_depth_planes(F::P) ? decltype(D)::value : max_depth_planes(F::P))
+      (decltype(D)::value < max_depth_planes(F::P, decltype(W)::value)                            \
+           ? decltype(D)::value                                                                     \
+           : max_depth_planes(F::P, decltype(W)::value))
 
 // The sa* kernels and the sign-plane mat-muls are instantiated with rings of
 // at most three tiles (deeper rings would spill registers); the launch

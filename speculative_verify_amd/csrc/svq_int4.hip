@@ -104,7 +104,7 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
   if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0, SVQ_MAX_M_GEMM)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096) {
-    // Two m-tiles held in registers: the M <= 16 kernel's launch shape.
+    // Two m-tiles held in registers: the M <= 16 kernel's eight-wave shape.
     Shape sh;
     if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
     auto launch = [&](auto Gc, auto Dc) {
