@@ -21,8 +21,9 @@ Also timed, each call on its own but outside the step (so the step and its
 `value` keep their definition): the tiny W4A16 mat-vec (M=1 K=256 N=512,
 69 KB: launch-bound, so microseconds only); the sa* storage of sign planes (u8 scale
 codes per plane and group, one fp16 d per 256-weight super-block) for
-decode and verify, P=3, groups of 64 and 128; and W4A16 blocks of M=32 and
-M=64 rows (a prefill chunk, the kernel for 16 < M <= 64).
+decode and verify, P=3, groups of 64 and 128; and W4A16, sign-plane and
+sa* blocks of M=32 and M=64 rows (a prefill chunk, the kernels for
+16 < M <= 64).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one
 GPU's share.
@@ -207,6 +208,17 @@ def build_extra(svq, synth, torch):
         name = f"gemv_w4a16_m1_n{N}" if M == 1 else f"gemm_smallm_w4a16_m{M}_n{N}"
         calls.append((name, alg_bytes_linear("w4a16", M, N), make(), make))
 
+    def bpm(M, N, P):
+        def make():
+            seed[0] += 1
+            blob = synth.device_binplane_blob(N, K, P, seed[0])
+            seed[0] += 1
+            X = synth.device_activations(M, K, seed[0]).view(torch.int16)
+            Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+            return lambda: svq.gemm_smallm_binplane(blob, X, Y, M, N, K, P)
+
+        calls.append((f"gemm_smallm_binplane_p{P}_m{M}_n{N}", alg_bytes_linear("binplane", M, N, P), make(), make))
+
     def bp1(N, P):
         def make():
             seed[0] += 1
@@ -241,6 +253,11 @@ def build_extra(svq, synth, torch):
     w4(32, 12288)
     w4(64, 4096)
     w4(64, 12288)
+    bpm(32, 12288, 3)
+    bpm(64, 4096, 3)
+    bpm(64, 12288, 3)
+    sa(32, 12288, 3, 128)
+    sa(64, 12288, 3, 128)
     bphead(1, 32768, 3)
     bphead(16, 32768, 3)
     # M = 1 at N = 4096, so the verify/decode ratio exists for both widths.

@@ -10,6 +10,7 @@
 
 #include "kernels.h"
 #include "launch.h"
+#include "mmq_planes.h"
 #include "svq.h"
 #include "svq_internal.h"
 
@@ -19,25 +20,27 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
                          int32_t G, int32_t P, void* stream) {
   if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemm_smallm_binplane: P=0 must be in 1..6");
   if (int rc = check_linear("gemm_smallm_binplane", packed, X, Y, M, N, K, G, P, SVQ_MAX_M_GEMM)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M > SVQ_MAX_M) {
+    // Blocks of 17..64 rows: the weights are read and decoded once for the
+    // whole block (mmq_planes.h).
+    int rc = SVQ_OK;
+    dispatch_p(P, [&](auto Pc) {
+      rc = launch_mmq_planes<MmqPlanes<decltype(Pc)::value>>("gemm_smallm_binplane", packed, X, Y, M, N, K, st);
+    });
+    return rc;
+  }
   Shape sh;
   if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // Blocks above 16 rows: one launch per 16-row block of X (the same sum per
-  // row; the weights are read once per block).
-  for (int32_t m0 = 0; m0 < M; m0 += SVQ_MAX_M) {
-    const int Mb = M - m0 < SVQ_MAX_M ? M - m0 : SVQ_MAX_M;
-    const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X + (size_t)m0 * K);
-    uint16_t* Yb = Y + (size_t)m0 * N;
-    dispatch_p(P, [&](auto Pc) {
-      using F = PlaneFmt<decltype(Pc)::value>;
-      dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
-        hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                           packed, Xw, Yb, (uint8_t*)nullptr, HeadOut{}, Mb, (int)N, sh.KT, sh.NT);
-      });
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  dispatch_p(P, [&](auto Pc) {
+    using F = PlaneFmt<decltype(Pc)::value>;
+    dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                         packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
     });
-    if (int rc = launched("gemm_smallm_binplane")) return rc;
-  }
-  return SVQ_OK;
+  });
+  return launched("gemm_smallm_binplane");
 }
 
 int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, int64_t N, int64_t K, int32_t G,

@@ -1,6 +1,7 @@
 // svq_sa_gemm.hip -- small-M device entry point for the sa* storage of sign
 // planes (ShiftAddQwen README, "Method / Format"): the verify mat-mul over a
-// drafted block of M <= 16 rows, on 16x16x32 bf16 MFMA with B = a * b exact.
+// drafted block of M <= 16 rows on 16x16x32 bf16 MFMA, and blocks of up to
+// 64 rows on the streaming kernel of mmq_planes.h.
 //   Y = X W^T with W[n][k] = d[n][k/256] * sum_p a[p][n][k/G] * b[p][n][k]
 #include <hip/hip_runtime.h>
 
@@ -8,6 +9,7 @@
 
 #include "kernels.h"
 #include "launch.h"
+#include "mmq_planes.h"
 #include "svq.h"
 #include "svq_internal.h"
 
@@ -16,29 +18,35 @@ extern "C" {
 int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
                    int32_t G, int32_t P, void* stream) {
   if (int rc = check_sa("gemm_smallm_sa", packed, X, Y, M, N, K, G, P, SVQ_MAX_M_GEMM)) return rc;
-  Shape sh;
-  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // Blocks above 16 rows: one launch per 16-row block of X (the same sum per
-  // row; the weights are read once per block).
-  for (int32_t m0 = 0; m0 < M; m0 += SVQ_MAX_M) {
-    const int Mb = M - m0 < SVQ_MAX_M ? M - m0 : SVQ_MAX_M;
-    const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X + (size_t)m0 * K);
-    uint16_t* Yb = Y + (size_t)m0 * N;
+  if (M > SVQ_MAX_M) {
+    // Blocks of 17..64 rows: the weights are read and decoded once for the
+    // whole block (mmq_planes.h).
+    int rc = SVQ_OK;
     dispatch_group(G, [&](auto Gc) {
       dispatch_p(P, [&](auto Pc) {
-        if constexpr (decltype(Pc)::value >= 2) {
-          using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
-          dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
-            hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves),
-                               0, st, packed, Xw, Yb, (uint8_t*)nullptr, HeadOut{}, Mb, (int)N, sh.KT, sh.NT);
-          });
-        }
+        if constexpr (decltype(Pc)::value >= 2)
+          rc = launch_mmq_planes<MmqSa<decltype(Pc)::value, decltype(Gc)::value>>("gemm_smallm_sa", packed, X, Y, M, N,
+                                                                                   K, st);
       });
     });
-    if (int rc = launched("gemm_smallm_sa")) return rc;
+    return rc;
   }
-  return SVQ_OK;
+  Shape sh;
+  if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  dispatch_group(G, [&](auto Gc) {
+    dispatch_p(P, [&](auto Pc) {
+      if constexpr (decltype(Pc)::value >= 2) {
+        using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
+        dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
+          hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+                             st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
+        });
+      }
+    });
+  });
+  return launched("gemm_smallm_sa");
 }
 
 }  // extern "C"

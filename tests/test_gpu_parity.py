@@ -322,8 +322,9 @@ def test_gemm_w4a16_two_mtiles_many_tiles_per_workgroup(M, N, K):
 
 @pytest.mark.parametrize("M,N,K,P", [(17, 300, 512, 3), (40, 1000, 1024, 2), (64, 4096, 4096, 3), (64, 77, 2048, 6)])
 def test_gemm_planes_midm(M, N, K, P):
-    # Sign planes (fp16 alphas and sa* codes) above 16 rows: one pass of the
-    # M <= 16 kernel per 16-row block, each row against the oracle.
+    # Sign planes (fp16 alphas and sa* codes) above 16 rows: the streaming
+    # kernel that decodes each weight tile once for all m-tiles, each row
+    # against the oracle.
     rng = np.random.default_rng(M * 7 + N + K + P)
     signs, alpha = synth.binplane_weights(rng, N, K, P=P)
     X = synth.activations(rng, M, K)
@@ -334,6 +335,61 @@ def test_gemm_planes_midm(M, N, K, P):
     s2, codes, d = synth.sa_weights(rng, N, K, max(P, 2), G)
     Y, A = oracle.linear_sa(s2, codes, d, X, G=G)
     check_close(run_gemm_sa(s2, codes, d, X, G), Y, A, f"sa M={M} G={G}")
+
+
+@pytest.mark.parametrize("kind", ["planes", "sa"])
+def test_gemm_planes_midm_every_m(kind):
+    # Every block height 17..64 (two, three and four m-tiles, ragged last
+    # m-tile) on a ragged N, P cycling through 1..6 (2..6 for sa*) and G
+    # through 64, 128, 256.
+    rng = np.random.default_rng(4100 + len(kind))
+    N, K = 333, 1024
+    for M in range(17, 65):
+        P = 1 + M % 6 if kind == "planes" else 2 + M % 5
+        X = synth.activations(rng, M, K)
+        if kind == "planes":
+            signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+            Y, A = oracle.linear_binplane(signs, alpha, X)
+            got = run_gemm_binplane(signs, alpha, X)
+        else:
+            G = (64, 128, 256)[M % 3]
+            signs, codes, d = synth.sa_weights(rng, N, K, P, G)
+            Y, A = oracle.linear_sa(signs, codes, d, X, G=G)
+            got = run_gemm_sa(signs, codes, d, X, G)
+        check_close(got, Y, A, f"{kind} M={M} P={P}")
+
+
+@pytest.mark.parametrize("M,N,K,P", [(40, 40000, 1024, 3), (64, 20000, 2048, 2), (24, 33333, 512, 4)])
+def test_gemm_planes_midm_many_blocks_per_workgroup(M, N, K, P):
+    # Enough row tiles that every workgroup walks several blocks (grid-stride
+    # over blocks, the X and weight cursors crossing block boundaries).
+    rng = np.random.default_rng(M + N + K + P)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+    X = synth.activations(rng, M, K)
+    Y, A = oracle.linear_binplane(signs, alpha, X)
+    print(f"planes midm many blocks M={M} N={N} K={K} P={P}", flush=True)
+    check_close(run_gemm_binplane(signs, alpha, X), Y, A, f"planes M={M} N={N}")
+    G = 64 if P % 2 else 128
+    s2, codes, d = synth.sa_weights(rng, N, K, max(P, 2), G)
+    Y, A = oracle.linear_sa(s2, codes, d, X, G=G)
+    check_close(run_gemm_sa(s2, codes, d, X, G), Y, A, f"sa M={M} N={N}")
+
+
+@pytest.mark.parametrize("M,P", [(20, 1), (33, 3), (64, 6)])
+def test_gemm_planes_midm_onehot_unit_alpha_is_exact(M, P):
+    # Unit alphas and x = one-hot rows: each output is sum_p b_p[n][k_m], a
+    # small integer, exactly -- pins every (row, k) position and m-tile of
+    # the block kernel.
+    rng = np.random.default_rng(M * 10 + P)
+    N, K = 96, 2048
+    signs = (1 - 2 * rng.integers(0, 2, size=(P, N, K))).astype(np.int8)
+    alpha = np.full((P, N, K // 128), 0x3C00, np.uint16)  # fp16 1.0
+    ks = rng.choice(K, size=M, replace=False)
+    X = np.zeros((M, K), np.uint16)
+    X[np.arange(M), ks] = 0x3F80  # bf16 1.0
+    want = signs[:, :, ks].sum(axis=0).T.astype(np.float64)  # [M][N]
+    got = run_gemm_binplane(signs, alpha, X)
+    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("M", [33, 64])
