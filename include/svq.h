@@ -92,7 +92,8 @@ enum {
 
 #define SVQ_GROUP 128     /* the only supported group size */
 #define SVQ_MAX_M 16      /* rows of a verify block (heads, acceptance) */
-#define SVQ_MAX_M_GEMM 64 /* rows of X a gemm_smallm_* call takes */
+#define SVQ_MAX_M_GEMM 65536 /* rows of X a gemm_smallm_* call takes */
+#define SVQ_BLOCK_M 64       /* rows of X one launch of gemm_smallm_* covers */
 #define SVQ_MAX_P 6       /* sign planes per weight */
 #define SVQ_MAX_K 8192    /* largest input dimension the kernels accept */
 
@@ -252,17 +253,20 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y,
  * Blocks of 16 < M <= 64 rows (a prefill chunk; the ShiftAddQwen README
  * places batches below 64 in the quantized mat-mul regime) take the same
  * kernel with two 16-row tiles of X (M <= 32, K <= 4096) or a kernel that
- * streams X with the weights; the result is defined the same way.
+ * streams X with the weights; the result is defined the same way.  Larger
+ * blocks (up to SVQ_MAX_M_GEMM rows) run as consecutive launches of
+ * SVQ_BLOCK_M rows each, each reading the weights once.
  *   X  [M][K] bf16 bits, 16-byte aligned;  Y [M][N] bf16 bits, 2-byte aligned.
- * Errors: as gemv_w4a16, plus SHAPE for M outside 1..64.
+ * Errors: as gemv_w4a16, plus SHAPE for M outside 1..SVQ_MAX_M_GEMM.
  */
 int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                       int32_t M, int64_t N, int64_t K, int32_t G, void* stream);
 
 /*
  * gemm_smallm_binplane -- DEVICE pointers, asynchronous on `stream`.
- * Y[m][n] = the binary-plane result for row m of X, M in 1..64 (above 16
- * rows, one pass of the M <= 16 kernel per 16-row block of X).
+ * Y[m][n] = the binary-plane result for row m of X, M in 1..SVQ_MAX_M_GEMM
+ * (17..64 rows: a kernel that streams X and decodes each weight tile once for
+ * the block; above 64, consecutive launches of SVQ_BLOCK_M rows).
  */
 int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                          int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,
@@ -283,10 +287,11 @@ int gemv_sa(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
 
 /*
  * gemm_smallm_sa -- DEVICE pointers, asynchronous on `stream`.
- * Y[m][n] = the sa* result for row m of X, M in 1..64 (the verify pass over
- * a drafted block, as gemm_smallm_w4a16; the README's batches below 64 run
- * its quantized mat-mul; above 16 rows, one pass of the M <= 16 kernel per
- * 16-row block of X).  Errors: as gemv_sa, plus SHAPE for M outside 1..64.
+ * Y[m][n] = the sa* result for row m of X, M in 1..SVQ_MAX_M_GEMM (the
+ * verify pass over a drafted block, as gemm_smallm_w4a16; the README's
+ * batches below 64 run its quantized mat-mul: 17..64 rows take the streaming
+ * block kernel, larger blocks consecutive launches of SVQ_BLOCK_M rows).
+ * Errors: as gemv_sa, plus SHAPE for M outside 1..SVQ_MAX_M_GEMM.
  */
 int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                    int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,

@@ -102,6 +102,15 @@ int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
 int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N, int64_t K,
                       int32_t G, void* stream) {
   if (int rc = check_linear("gemm_smallm_w4a16", packed, X, Y, M, N, K, G, 0, SVQ_MAX_M_GEMM)) return rc;
+  if (M > SVQ_BLOCK_M) {
+    // Consecutive launches of at most SVQ_BLOCK_M rows (the exact-operand
+    // kernels below; each reads the weights once).
+    for (int32_t m0 = 0; m0 < M; m0 += SVQ_BLOCK_M) {
+      const int32_t Mb = M - m0 < SVQ_BLOCK_M ? M - m0 : SVQ_BLOCK_M;
+      if (int rc = gemm_smallm_w4a16(packed, X + (size_t)m0 * K, Y + (size_t)m0 * N, Mb, N, K, G, stream)) return rc;
+    }
+    return SVQ_OK;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096) {
     // Two m-tiles held in registers: the M <= 16 kernel's eight-wave shape.

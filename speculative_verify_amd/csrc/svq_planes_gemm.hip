@@ -20,6 +20,16 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
                          int32_t G, int32_t P, void* stream) {
   if (P == 0) return svq::fail(SVQ_ERR_SHAPE, "gemm_smallm_binplane: P=0 must be in 1..6");
   if (int rc = check_linear("gemm_smallm_binplane", packed, X, Y, M, N, K, G, P, SVQ_MAX_M_GEMM)) return rc;
+  if (M > SVQ_BLOCK_M) {
+    // Consecutive launches of at most SVQ_BLOCK_M rows, each reading the
+    // weights once.
+    for (int32_t m0 = 0; m0 < M; m0 += SVQ_BLOCK_M) {
+      const int32_t Mb = M - m0 < SVQ_BLOCK_M ? M - m0 : SVQ_BLOCK_M;
+      if (int rc = gemm_smallm_binplane(packed, X + (size_t)m0 * K, Y + (size_t)m0 * N, Mb, N, K, G, P, stream))
+        return rc;
+    }
+    return SVQ_OK;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (M > SVQ_MAX_M) {
     // Blocks of 17..64 rows: the weights are read and decoded once for the

@@ -59,8 +59,8 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.gemv_binplane(A, A, A, 16, 128, 128, 0, None), -2),
     (lambda l: l.gemv_binplane(A, A, A, 16, 128, 128, 7, None), -2),
     (lambda l: l.gemm_smallm_w4a16(A, A, A, 0, 16, 128, 128, None), -2),
-    (lambda l: l.gemm_smallm_w4a16(A, A, A, 65, 16, 128, 128, None), -2),
-    (lambda l: l.gemm_smallm_binplane(A, A, A, 65, 16, 128, 128, 3, None), -2),
+    (lambda l: l.gemm_smallm_w4a16(A, A, A, 65537, 16, 128, 128, None), -2),
+    (lambda l: l.gemm_smallm_binplane(A, A, A, 65537, 16, 128, 128, 3, None), -2),
     (lambda l: l.gemm_smallm_binplane(A, A, A, 4, 16, 128, 128, 0, None), -2),
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, A, None, 0, None), -5),
     (lambda l: l.lmhead_argmax(A, A, 2, 16, 128, 128, None, A, A, A, 8, None), -5),
@@ -84,7 +84,7 @@ A = 0x100000  # an aligned address that is never dereferenced: validation fails 
     (lambda l: l.gemv_sa(A, A, A, 16, 256, 128, 7, None), -2),
     (lambda l: l.gemv_sa(A, A, A, 16, 256 * 33, 128, 3, None), -2),
     (lambda l: l.gemv_sa(A + 8, A, A, 16, 256, 128, 3, None), -3),
-    (lambda l: l.gemm_smallm_sa(A, A, A, 65, 16, 256, 64, 2, None), -2),
+    (lambda l: l.gemm_smallm_sa(A, A, A, 65537, 16, 256, 64, 2, None), -2),
     (lambda l: l.gemm_smallm_sa(A, A, A, 4, 16, 256, 512, 2, None), -2),
     (lambda l: l.gemm_smallm_sa(A, A + 2, A, 4, 16, 256, 256, 2, None), -3),
     (lambda l: l.lmhead_argmax_noalloc(A, A, 17, 16, 128, 128, None, A, A, None), -2),

@@ -359,6 +359,26 @@ def test_gemm_planes_midm_every_m(kind):
         check_close(got, Y, A, f"{kind} M={M} P={P}")
 
 
+@pytest.mark.parametrize("M", [65, 100, 128, 193])
+def test_gemm_above_64_rows(M):
+    # Blocks above 64 rows (prefill chunks) run as consecutive launches of 64
+    # rows; every row against the oracle, all three storages.
+    rng = np.random.default_rng(4200 + M)
+    N, K = 203, 1024
+    X = synth.activations(rng, M, K)
+    codes, scales = synth.int4_weights(rng, N, K)
+    Y, A = oracle.linear_w4a16(codes, scales, X)
+    print(f"M={M} above one launch: w4a16", flush=True)
+    check_close(run_gemm_w4a16(codes, scales, X), Y, A, f"w4a16 M={M}")
+    signs, alpha = synth.binplane_weights(rng, N, K, P=3)
+    Y, A = oracle.linear_binplane(signs, alpha, X)
+    check_close(run_gemm_binplane(signs, alpha, X), Y, A, f"planes M={M}")
+    G = (64, 128, 256)[M % 3]
+    s2, c2, d2 = synth.sa_weights(rng, N, K, 4, G)
+    Y, A = oracle.linear_sa(s2, c2, d2, X, G=G)
+    check_close(run_gemm_sa(s2, c2, d2, X, G), Y, A, f"sa M={M} G={G}")
+
+
 @pytest.mark.parametrize("M,N,K,P", [(40, 40000, 1024, 3), (64, 20000, 2048, 2), (24, 33333, 512, 4)])
 def test_gemm_planes_midm_many_blocks_per_workgroup(M, N, K, P):
     # Enough row tiles that every workgroup walks several blocks (grid-stride
