@@ -266,6 +266,17 @@ def build_extra(svq, synth, torch):
     return calls
 
 
+# Launch log: (call, phase, kernel launches) in the order bench.py issues
+# them, written with --launch-log so that a profiler's dispatch list can be
+# mapped back to calls and phases (every call is one kernel launch; "step"
+# entries are whole steps, one launch of every step call each).
+LAUNCHES = []
+
+
+def log_launches(call, phase, n):
+    LAUNCHES.append({"call": call, "phase": phase, "launches": int(n)})
+
+
 def warm_up(torch, run, min_iters=0, min_s=WARM_S):
     """Untimed runs of `run` until at least min_iters of them and min_s
     seconds have passed; returns (seconds, runs)."""
@@ -327,8 +338,9 @@ def stream_read_ceiling(svq, torch, nbytes=1 << 30, iters=20, wgs_per_cu=(1, 2, 
         torch.cuda.synchronize()
         runs = [lambda v=v: svq.svq_stream_read(v, nbytes, sink, w) for v in views]
         graph = capture_series(torch, runs, iters)
-        warm_up(torch, graph.replay, min_s=WARM_S / 5)
+        _, nw = warm_up(torch, graph.replay, min_s=WARM_S / 5)
         us = time_replay(torch, graph, stream, iters)
+        log_launches(f"read_{nbytes}", f"wgs{w}", 3 + iters * (2 + nw))
         del graph
         best = max(best, nbytes / (us * 1e-6) / 1e9)
     del views, buf
@@ -428,6 +440,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--launch-log", default=None,
+                    help="write the (call, phase, launches) sequence to this JSON file (for profiler summaries)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only; --gpus {args.gpus} is not supported "
@@ -452,6 +466,7 @@ def main():
             c[2]()
 
     warm_step_s, warm_steps = warm_up(torch, one_step, min_iters=args.warmup)
+    log_launches("step", "warm", warm_steps)
 
     # The step throughput: K steps back to back, no events between calls.
     stream = torch.cuda.current_stream()
@@ -466,6 +481,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    log_launches("step", "timed", args.steps)
 
     # Per-call durations, each call on its own: K launches back to back,
     # rotating over copies of the call's inputs that together hold at least
@@ -486,10 +502,12 @@ def main():
             f()
         torch.cuda.synchronize()
         graph = capture_series(torch, rot, args.steps)
-        warm_up(torch, graph.replay)
+        _, nw = warm_up(torch, graph.replay)
+        log_launches(name, "warm", len(rot[:3]) + args.steps * (1 + nw))
         # Five timed replays; the median is reported (one alone varies by a
         # few percent from run to run).
         us = sorted(time_replay(torch, graph, stream, args.steps) for _ in range(5))[2]
+        log_launches(name, "timed", 5 * args.steps)
         del graph, rot
         # Hot: the same launches on one copy of the inputs, which stays in
         # the caches between launches when it fits (a lower bound on the
@@ -498,8 +516,9 @@ def main():
             fn()
         torch.cuda.synchronize()
         graph = capture_series(torch, [fn], args.steps)
-        warm_up(torch, graph.replay, min_s=WARM_S / 5)
+        _, nw = warm_up(torch, graph.replay, min_s=WARM_S / 5)
         hot_us = time_replay(torch, graph, stream, args.steps)
+        log_launches(name, "hot", 3 + args.steps * (2 + nw))
         del graph
         gbps = nbytes / (us * 1e-6) / 1e9
         kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(gbps, 1),
@@ -584,6 +603,9 @@ def main():
         result["stream_read_ceiling_GBps"] = round(stream_read_ceiling(svq, torch, wgs_per_cu=(1,)), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
+    if args.launch_log:
+        with open(args.launch_log, "w") as f:
+            json.dump({"steps": args.steps, "step_calls": [c[0] for c in calls], "launches": LAUNCHES}, f, indent=0)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -10,9 +10,9 @@
  *   Binary planes: y[m][n] = sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] * x[m][k]
  *           b in {-1, +1}, alpha fp16, one scale per (plane, row, group).
  *           (ShiftAddQwen README, intro and "Method / Format".)
- *   sa* storage of the same sum: alpha[p][n][g] = d[n][j] * a[p][n][g] with
- *           a u8 scale code per (plane, row, group of G in {64, 128, 256})
- *           and one fp16 d per (row, super-block j of 256 weights along k).
+ *   sa* storage of the same sum: alpha[p][n][g] = d[n][j] * a[p][n][g],
+ *           a a u8 code per (plane, row, group of G in {64, 128, 256}) and
+ *           d an fp16 value per (row, j = the 256-wide k range holding g).
  *           (ShiftAddQwen README, "Method / Format", the sa{2..6} types.)
  *   Greedy verify head: argmax over the W4A16 logits of a (possibly
  *           vocabulary-trimmed) head, lowest index on ties, optionally mapped
@@ -151,11 +151,10 @@ int unpack_binary_planes(const uint8_t* packed, int64_t N, int64_t K, int32_t G,
 
 /*
  * pack_sa -- HOST pointers, synchronous, CPU only.
- * Stores P sign planes with their u8 scale codes and fp16 super-block scales
- * in the sa blob layout above (ShiftAddQwen README, "Method / Format": the
- * sa{P}[_128|_256] types keep, per super-block of 256 weights along the
- * input dimension, the P sign planes, one u8 scale code per plane and group
- * of G weights and one fp16 scale d, with alpha = d * a).
+ * Writes the sa* storage of P sign planes (ShiftAddQwen README, "Method /
+ * Format") as the sa blob above: the signs into its sign section, code
+ * a[p][n][g] into its code section and d[n][j] into its d section; the scale
+ * of plane p, row n, group g is then d[n][g * G / 256] * a[p][n][g].
  *   signs   [P][N][K] int8, each -1 or +1
  *   codes   [P][N][K/G] uint8 scale codes a
  *   d_f16   [N][K/256] fp16 bits
