@@ -970,45 +970,55 @@ __global__ void __launch_bounds__(64 * MAXW)
 // odd k's (+1).  For every (group, t, parity) the table holds, for each of
 // the 16 nibble values v, the sum over i of (bit i of v set ? -x : +x) over
 // those four activations, so a plane's sum over 128 k is eight table reads
-// instead of 64 sign decodes and 64 multiply-adds.  Lane (q, r) builds entry
-// v = r of the tables of its own q (the 16 lanes of a row share their
-// activations), and every wave builds and reads only its own tables, so no
-// barrier is needed.  In a read, the 16 lanes of a row q address the 16
-// consecutive entries of one table and the four rows use disjoint 16-bank
-// ranges, so a read is free of bank conflicts.
+// instead of 64 sign decodes and 64 multiply-adds.  Every wave builds and
+// reads only its own tables, so no barrier is needed.  In a read, the 16
+// lanes of a row q address the 16 consecutive entries of one table and the
+// four rows use disjoint 16-bank ranges, so a read is free of bank
+// conflicts.
 template <int GPW>
 struct SignLut {
   float e[GPW][4][2][64];  // [group][t][parity][16 q + v]
 };
 
+// The tables are built on the matrix cores, from the activations as loaded
+// (lane (q, r) holds the pair (t = r / 4, i = r % 4) of its row q, see
+// load_x_own).  For one group and parity the 256 entries of its four k
+// blocks and four rows are one 16 x 16 product D = S B over 32 k slots
+// (8 h + 2 i + p: lane row h, pair i, half p):
+//   S[v][k] = (p == parity) ? (bit i of v set ? -1 : +1) : 0
+//   B[k][n] = x of row n % 4, block n / 4, pair i, half p  if h == n % 4, else 0
+// so D[v][n] is entry v of table (block n / 4, row n % 4).  The B operand of
+// lane (q, r) is the four pairs of its own quad (a DPP quad broadcast each),
+// kept where r % 4 == q and zero elsewhere; every product is exact and each
+// entry sums four of them in fp32.  Per wave: 8 MFMAs and 32 VALU
+// instructions (one dot2 chain per entry took 128 instructions, plus 64
+// moves to spread the activations over the row).  Lane (q, r) receives
+// entries 4q .. 4q + 3 of table (r / 4, r % 4) and writes them as one
+// 16-byte store.
 template <int GPW>
-__device__ __forceinline__ void build_sign_lut(SignLut<GPW>& lut, const uint32_t (&xp)[GPW][16], int q, int r) {
-  // The first term's sign is an XOR into the widened activation; for the
-  // other three, bf16 pairs (s_i, 0) and (0, s_i) (s_i = -1 where bit i of
-  // the entry index r is set) let one dot2 add the even (odd) activation of
-  // a pair with its sign: four instructions per entry.
-  const uint32_t f0 = (uint32_t)(r & 1) << 31;
-  uint32_t se[4], so[4];
+__device__ __forceinline__ void build_sign_lut(SignLut<GPW>& lut, const uint32_t (&xo)[GPW], int q, int r) {
+  uint32_t s0[4], s1[4];
 #pragma unroll
-  for (int i = 1; i < 4; ++i) {
-    se[i] = ((r >> i) & 1) ? 0xBF80u : 0x3F80u;
-    so[i] = se[i] << 16;
+  for (int i = 0; i < 4; ++i) {
+    s0[i] = ((r >> i) & 1) ? 0xBF80u : 0x3F80u;
+    s1[i] = s0[i] << 16;
   }
+  const bool own = (r & 3) == q;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
+  for (int gi = 0; gi < GPW; ++gi) {
+    uint32_t b[4];
+    b[0] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x00, 0xF, 0xF, false);  // quad_perm [0, 0, 0, 0]
+    b[1] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x55, 0xF, 0xF, false);  // quad_perm [1, 1, 1, 1]
+    b[2] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0xAA, 0xF, 0xF, false);  // quad_perm [2, 2, 2, 2]
+    b[3] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0xFF, 0xF, 0xF, false);  // quad_perm [3, 3, 3, 3]
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t* pr = &xp[gi][4 * t];
-      float e0 = __uint_as_float((pr[0] << 16) ^ f0);
-      float e1 = __uint_as_float((pr[0] & 0xFFFF0000u) ^ f0);
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        e0 = dot2(pr[i], se[i], e0);
-        e1 = dot2(pr[i], so[i], e1);
-      }
-      lut.e[gi][t][0][16 * q + r] = e0;
-      lut.e[gi][t][1][16 * q + r] = e1;
-    }
+    for (int i = 0; i < 4; ++i) b[i] = own ? b[i] : 0u;
+    const f32x4_t e0 = mfma16x16x32(s0, b, zero);
+    const f32x4_t e1 = mfma16x16x32(s1, b, zero);
+    *reinterpret_cast<float4*>(&lut.e[gi][r >> 2][0][16 * (r & 3) + 4 * q]) = make_float4(e0[0], e0[1], e0[2], e0[3]);
+    *reinterpret_cast<float4*>(&lut.e[gi][r >> 2][1][16 * (r & 3) + 4 * q]) = make_float4(e1[0], e1[1], e1[2], e1[3]);
+  }
 }
 
 // ((w >> shift) & 15) * 4: a nibble as the byte offset of a table entry.
@@ -1403,9 +1413,11 @@ __global__ void __launch_bounds__(64 * MAXW)
   __shared__ ChunkStage<float, C, MAXW, 16> stage;
   __shared__ SignLut<kLut ? GPW : 1> luts[kLut ? MAXW : 1];
   uint32_t xp[GPW][16];
-  expand_x<GPW>(xo, xp);
+  if constexpr (kLut)
+    build_sign_lut<GPW>(luts[wave], xo, q, r);
+  else
+    expand_x<GPW>(xo, xp);
   const PairDecode one = sign_decode();
-  if constexpr (kLut) build_sign_lut<GPW>(luts[wave], xp, q, r);
   // Opaque copy: the compiler would otherwise turn the OR of disjoint bits in
   // every address into an ADD and lose the one-instruction AND-OR form.
   const uint32_t lut_off =
