@@ -974,10 +974,20 @@ __global__ void __launch_bounds__(64 * MAXW)
 // reads only its own tables, so no barrier is needed.  In a read, the 16
 // lanes of a row q address the 16 consecutive entries of one table and the
 // four rows use disjoint 16-bank ranges, so a read is free of bank
-// conflicts.
+// conflicts.  Table (group, t, parity) holds entry v of row q at word
+// base + 16 q + v; its base is shifted by 4 t words from the 64-word grid,
+// so that the 16-byte stores of a table build, where the 16 lanes of a pass
+// write four entries of the four rows of four blocks t, meet 16 distinct
+// bank quads (on the plain grid they met four, four stores to each).  A
+// group's eight tables then span 8 x 64 + 12 words; groups are 528 words
+// apart, and the size is rounded up to a multiple of 256 bytes: a wave's
+// tables start at a multiple of 256, whose low bits the read addresses fill
+// by OR.
 template <int GPW>
 struct SignLut {
-  float e[GPW][4][2][64];  // [group][t][parity][16 q + v]
+  static constexpr int kGroupWords = 8 * 64 + 16;
+  float e[(GPW * kGroupWords + 63) / 64 * 64];
+  static constexpr int base(int gi, int t, int par) { return kGroupWords * gi + 64 * (2 * t + par) + 4 * t; }
 };
 
 // The tables are built on the matrix cores, from the activations as loaded
@@ -1016,8 +1026,9 @@ __device__ __forceinline__ void build_sign_lut(SignLut<GPW>& lut, const uint32_t
     for (int i = 0; i < 4; ++i) b[i] = own ? b[i] : 0u;
     const f32x4_t e0 = mfma16x16x32(s0, b, zero);
     const f32x4_t e1 = mfma16x16x32(s1, b, zero);
-    *reinterpret_cast<float4*>(&lut.e[gi][r >> 2][0][16 * (r & 3) + 4 * q]) = make_float4(e0[0], e0[1], e0[2], e0[3]);
-    *reinterpret_cast<float4*>(&lut.e[gi][r >> 2][1][16 * (r & 3) + 4 * q]) = make_float4(e1[0], e1[1], e1[2], e1[3]);
+    float* row = &lut.e[SignLut<GPW>::base(gi, r >> 2, 0) + 16 * (r & 3) + 4 * q];
+    *reinterpret_cast<float4*>(row) = make_float4(e0[0], e0[1], e0[2], e0[3]);
+    *reinterpret_cast<float4*>(row + 64) = make_float4(e1[0], e1[1], e1[2], e1[3]);  // parity 1: the next table
   }
 }
 
@@ -1046,7 +1057,8 @@ __device__ __forceinline__ float binplane_tile_partial_lut(const SignSlot<GPW, P
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
-          const uint32_t off = (nibble_offset(w, 16 * par + 4 * t) | lane_off) + ((gi * 4 + t) * 2 + par) * 256;
+          const uint32_t off =
+              (nibble_offset(w, 16 * par + 4 * t) | lane_off) + 4 * SignLut<GPW>::base(gi, t, par);
           const float v = *reinterpret_cast<const float*>(base + off);
           acc = (t == 0 && par == 0) ? v : acc + v;
         }
@@ -1077,7 +1089,8 @@ __device__ __forceinline__ float sa_tile_partial_lut(const SaSlot<GPW, P, G>& sl
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int par = 0; par < 2; ++par) {
-            const uint32_t off = (nibble_offset(w, 16 * par + 4 * t) | lane_off) + ((gi * 4 + t) * 2 + par) * 256;
+            const uint32_t off =
+                (nibble_offset(w, 16 * par + 4 * t) | lane_off) + 4 * SignLut<GPW>::base(gi, t, par);
             const float v = *reinterpret_cast<const float*>(base + off);
             h[t >> 1] = ((t & 1) == 0 && par == 0) ? v : h[t >> 1] + v;
           }
@@ -1379,7 +1392,7 @@ struct SaFmt {
 
 // Chunk length of the table kernel: the tables (8 KiB per wave at four groups)
 // plus the chunk staging must leave room for two workgroups per CU.
-constexpr int kChunkGemvLut = 14;
+constexpr int kChunkGemvLut = 13;
 
 // Sign-plane mat-vec and head (M = 1) for storage format F.  ARGMAX selects
 // the epilogue.
