@@ -197,11 +197,18 @@ __device__ __forceinline__ void plane_operands_t(const PlaneViews& v, int t, con
   b[3] = t < 2 ? (lo & d.m7) | d.c7 : ((t == 2 ? v.v1 : v.w) & d.m15) | d.c15;
 }
 
-// 1 + c per pair position ip (0 at the two +-1 positions, whose activations
-// are negated), as bf16 pairs: the weights of the chain start.
-__device__ __forceinline__ constexpr uint32_t plane_init_weight(int ip) {
-  constexpr uint32_t w[4] = {0x41884188u, 0x41104110u, 0x40A040A0u, 0x40404040u};  // 17, 9, 5, 3
-  return (ip & 3) == 3 ? (ip < 8 ? w[3] : 0u) : w[ip & 3];
+// Chain-start weights (1 + c) of the 16 pair positions of a k block, as
+// bf16 pairs: 17, 9, 5, 3 for the positions decoded over bases 16, 8, 4, 2,
+// and 0 at the two plain +-1 positions (pairs 11 and 15).
+__device__ __forceinline__ void plane_chain_weights(uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+  lo[0] = opaque_vgpr<0x41884188u>();  // 17
+  lo[1] = opaque_vgpr<0x41104110u>();  // 9
+  lo[2] = opaque_vgpr<0x40A040A0u>();  // 5
+  lo[3] = opaque_vgpr<0x40404040u>();  // 3: k blocks 0 and 1
+  hi[0] = lo[0];
+  hi[1] = lo[1];
+  hi[2] = lo[2];
+  hi[3] = opaque_vgpr<0u>();  // the +-1 positions of k blocks 2 and 3
 }
 
 // Sum over the four lanes r, r+16, r+32, r+48 of a wave (the q index), via
@@ -272,6 +279,35 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t* a, const uint32_
   u32x4_t bv = {b[0], b[1], b[2], b[3]};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                  __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+}
+
+// Chain starts of the sign-plane MFMA tiles: -Z per group of GPW (per half
+// group, k blocks 0-1 and 2-3, when H = 2), Z[m] = sum_k (1 + c_k) x[m][k],
+// as an MFMA chain of the activation operands against the constant operand
+// (1 + c_k).  Every column of the product holds Z, so each lane receives it
+// for the rows 4q + i its accumulators hold, with no cross-lane moves.
+template <int GPW, int H>
+__device__ __forceinline__ void plane_chain_starts(const uint32_t (&xa)[GPW][16], f32x4_t (&cs)[GPW][2]) {
+  uint32_t lo[4], hi[4];
+  plane_chain_weights(lo, hi);
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    f32x4_t z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+    z0 = mfma16x16x32(&xa[gi][0], lo, z0);
+    z0 = mfma16x16x32(&xa[gi][4], lo, z0);
+    if constexpr (H == 2) {
+      z1 = mfma16x16x32(&xa[gi][8], hi, z1);
+      z1 = mfma16x16x32(&xa[gi][12], hi, z1);
+    } else {
+      z0 = mfma16x16x32(&xa[gi][8], hi, z0);
+      z0 = mfma16x16x32(&xa[gi][12], hi, z0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cs[gi][0][e] = -z0[e];
+      cs[gi][1][e] = -z1[e];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1161,14 +1197,11 @@ struct PlaneFmt {
       for (int gi = 0; gi < GPW; ++gi) {
         xa[gi][11] ^= 0x80008000u;
         xa[gi][15] ^= 0x80008000u;
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (plane_init_weight(j) != 0u) s = dot2(xa[gi][j], plane_init_weight(j), s);
-        const float srow = sum_over_q(s);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx.cinit[gi][i] = -__shfl(srow, 4 * q + i);
       }
+      f32x4_t cs[GPW][2];
+      plane_chain_starts<GPW, 1>(xa, cs);
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) mx.cinit[gi] = cs[gi][0];
       mx.d = plane_decode();
     } else {
       mx.one = sign_decode();
@@ -1308,17 +1341,13 @@ struct SaFmt {
       for (int gi = 0; gi < GPW; ++gi) {
         xa[gi][11] ^= 0x80008000u;
         xa[gi][15] ^= 0x80008000u;
-        float s[2] = {0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (plane_init_weight(j) != 0u) s[j >> 3] = dot2(xa[gi][j], plane_init_weight(j), s[j >> 3]);
-#pragma unroll
-        for (int h = 0; h < (G == 64 ? 2 : 1); ++h) {
-          const float srow = sum_over_q(G == 64 ? s[h] : s[0] + s[1]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx.cinit[gi][h][i] = -__shfl(srow, 4 * q + i);
-        }
       }
+      f32x4_t cs[GPW][2];
+      plane_chain_starts<GPW, G == 64 ? 2 : 1>(xa, cs);
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int h = 0; h < (G == 64 ? 2 : 1); ++h) mx.cinit[gi][h] = cs[gi][h];
       mx.d = plane_decode();
     } else {
       mx.one = sign_decode();

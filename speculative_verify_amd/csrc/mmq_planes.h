@@ -39,20 +39,6 @@
 
 namespace {
 
-// Chain-start weights (1 + c) of the 16 pair positions of a k block, as
-// bf16 pairs: 17, 9, 5, 3 for the positions decoded over bases 16, 8, 4, 2,
-// and 0 at the two plain +-1 positions (pairs 11 and 15).
-__device__ __forceinline__ void plane_chain_weights(uint32_t (&lo)[4], uint32_t (&hi)[4]) {
-  lo[0] = opaque_vgpr<0x41884188u>();  // 17
-  lo[1] = opaque_vgpr<0x41104110u>();  // 9
-  lo[2] = opaque_vgpr<0x40A040A0u>();  // 5
-  lo[3] = opaque_vgpr<0x40404040u>();  // 3: k blocks 0 and 1
-  hi[0] = lo[0];
-  hi[1] = lo[1];
-  hi[2] = lo[2];
-  hi[3] = opaque_vgpr<0u>();  // the +-1 positions of k blocks 2 and 3
-}
-
 // fp16-alpha binary planes.
 template <int P_>
 struct MmqPlanes {
