@@ -360,11 +360,14 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
 // Host side: the launch of a 16 < M <= 64 sign-plane block (arguments
 // already checked).  Block height R: the per-step registers (A fragments of
 // MT m-tiles, R x MT accumulator tiles, two ring slots of R x P sign dwords
-// and scales) fit 256 a lane up to R = 3 at two m-tiles and three planes or
-// fewer, R = 1 at four m-tiles and six planes (which still spills a few
-// registers), else R = 2; within that, R = ceil(row tiles / CUs), so that
-// about one block lands on each CU.
-constexpr int mmq_planes_rmax(int MT, int P) { return MT <= 2 && P <= 3 ? 3 : MT >= 4 && P >= 6 ? 1 : 2; }
+// and scales) allow R = 3 up to three planes, R = 1 at four m-tiles and six
+// planes, else R = 2; within that, R = ceil(row tiles / CUs), so that about
+// one block lands on each CU.  At four m-tiles and three planes a block of
+// three spills 11 to 18 registers, reloaded at every step, and is still
+// 11-13% faster at N = 12288 than blocks of two (768 row tiles: one block a
+// CU instead of 384 blocks on 256 CUs); six planes at four m-tiles still
+// spill a few registers at R = 1.
+constexpr int mmq_planes_rmax(int MT, int P) { return P <= 3 ? 3 : MT >= 4 && P >= 6 ? 1 : 2; }
 
 template <class F>
 int launch_mmq_planes(const char* fn, const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_t M, int64_t N,
