@@ -1358,7 +1358,61 @@ struct SaFmt {
                                                const MmaX<GPW, MAXW>& mx) {
     constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
     float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (mma_fast_shape<GPW, MAXW>()) {
+    if constexpr (mma_fast_shape<GPW, MAXW>() && P <= 4 && G != 64) {
+      // Up to four planes at G >= 128: a plane's chains over the wave's
+      // column tiles are interleaved k block by k block, so consecutive
+      // MFMAs are independent.  (At G = 64 the halves double the chains and
+      // the codes the slot, and the interleaved form spills registers.)
+      constexpr int H = 1;
+      constexpr int IL = GPW;
+      float4 ys[SB];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) ys[sb] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int g0c = 0; g0c < GPW; g0c += IL)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          PlaneViews v[IL];
+          f32x4_t c[IL][H];
+#pragma unroll
+          for (int u = 0; u < IL; ++u) {
+            v[u] = plane_views(sl.w[g0c + u][p]);
+#pragma unroll
+            for (int h = 0; h < H; ++h) c[u][h] = mx.cinit[g0c + u][h];
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < IL; ++u) {
+              uint32_t b[4];
+              plane_operands_t(v[u], t, mx.d, b);
+              c[u][H == 2 ? t >> 1 : 0] = mfma16x16x32(&xa[g0c + u][4 * t], b, c[u][H == 2 ? t >> 1 : 0]);
+            }
+#pragma unroll
+          for (int u = 0; u < IL; ++u)
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+              const int gi = g0c + u;
+              const float a = (float)sl.code(p, gi, 2 * h);
+              float4& y = ys[gi >> 1 < SB ? gi >> 1 : SB - 1];
+              y.x = fmaf(a, c[u][h][0], y.x);
+              y.y = fmaf(a, c[u][h][1], y.y);
+              y.z = fmaf(a, c[u][h][2], y.z);
+              y.w = fmaf(a, c[u][h][3], y.w);
+            }
+        }
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const float d = sl.dscale(2 * sb);
+        yv.x = fmaf(d, ys[sb].x, yv.x);
+        yv.y = fmaf(d, ys[sb].y, yv.y);
+        yv.z = fmaf(d, ys[sb].z, yv.z);
+        yv.w = fmaf(d, ys[sb].w, yv.w);
+      }
+      return make_float4(-yv.x, -yv.y, -yv.z, -yv.w);
+    } else if constexpr (mma_fast_shape<GPW, MAXW>()) {
+      // Five or six planes, or G = 64: each (column tile, plane) runs its
+      // own chains.
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
