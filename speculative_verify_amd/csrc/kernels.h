@@ -99,6 +99,15 @@ __device__ __forceinline__ uint32_t opaque_vgpr() {
   return v;
 }
 
+// The wave's index in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot tell that threadIdx.x >> 6 is the same in every lane, and
+// would otherwise form every address term derived from it (the wave's
+// column tiles) with vector instructions at each step.  (In the 16 < M <= 64
+// sign-plane kernel this made the M = 64 calls 4-5% faster; in the other
+// kernels, whose per-step addressing is lighter, it made no difference or
+// cost 1-4%.)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // A copy of v the compiler cannot see through (its known bits are lost).  Only
 // VALU instructions read the result.
 __device__ __forceinline__ uint32_t opaque_copy(uint32_t v) {

@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(64 * kMmqWaves)
   // The ring's next slot is refilled at the start of a step, so a ring of one
   // slot would overwrite the step's own weights.
   static_assert(D >= 2, "the weight ring needs two slots");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int q = lane >> 4, r = lane & 15;
   const typename F::View bv = F::view(blob, KT, NT);
   // Rows >= M lie past the end of this range and read zero.
