@@ -1295,6 +1295,76 @@ struct PlaneFmt {
       return yv;
     }
   }
+
+  // Two 16-row m-tiles at once (the 17..32-row form, full-register shapes,
+  // P <= 4): every decoded operand feeds both m-tiles' chains, so the
+  // weights are read and decoded once for the 32 rows.  Chains are
+  // interleaved over IL column tiles (two, so that both m-tiles' chains fit
+  // beside the two blocks of activations).
+  template <int GPW>
+  struct Mma2 {
+    f32x4_t cinit[2][GPW];
+    PlaneDecode d;
+  };
+  template <int GPW>
+  static __device__ __forceinline__ void prepare_mma2(uint32_t (&xa)[2][GPW][16], Mma2<GPW>& mx) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        xa[mt][gi][11] ^= 0x80008000u;
+        xa[mt][gi][15] ^= 0x80008000u;
+      }
+      f32x4_t cs[GPW][2];
+      plane_chain_starts<GPW, 1>(xa[mt], cs);
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) mx.cinit[mt][gi] = cs[gi][0];
+    }
+    mx.d = plane_decode();
+  }
+  template <int GPW>
+  static __device__ __forceinline__ void mma2(const Slot<GPW>& sl, const uint32_t (&xa)[2][GPW][16],
+                                              const Mma2<GPW>& mx, float4 (&yv)[2]) {
+    static_assert(P <= 4, "two m-tiles hold the operands of up to four planes");
+    constexpr int IL = GPW < 2 ? GPW : 2;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) yv[mt] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int g0c = 0; g0c < GPW; g0c += IL) {
+        PlaneViews v[IL];
+        f32x4_t c[2][IL];
+#pragma unroll
+        for (int u = 0; u < IL; ++u) {
+          v[u] = plane_views(sl.w[g0c + u][p]);
+          c[0][u] = mx.cinit[0][g0c + u];
+          c[1][u] = mx.cinit[1][g0c + u];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int u = 0; u < IL; ++u) {
+            uint32_t b[4];
+            plane_operands_t(v[u], t, mx.d, b);
+            c[0][u] = mfma16x16x32(&xa[0][g0c + u][4 * t], b, c[0][u]);
+            c[1][u] = mfma16x16x32(&xa[1][g0c + u][4 * t], b, c[1][u]);
+          }
+#pragma unroll
+        for (int u = 0; u < IL; ++u) {
+          const float a = sl.a[p].f16(g0c + u);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            yv[mt].x = fmaf(a, c[mt][u][0], yv[mt].x);
+            yv[mt].y = fmaf(a, c[mt][u][1], yv[mt].y);
+            yv[mt].z = fmaf(a, c[mt][u][2], yv[mt].z);
+            yv[mt].w = fmaf(a, c[mt][u][3], yv[mt].w);
+          }
+        }
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) yv[mt] = make_float4(-yv[mt].x, -yv[mt].y, -yv[mt].z, -yv[mt].w);
+  }
 };
 
 // sa*: u8 codes per (plane, row, group of G) and one fp16 d per (row,
@@ -1479,6 +1549,77 @@ struct SaFmt {
       }
       return yv;
     }
+  }
+
+  // Two 16-row m-tiles at once (the 17..32-row form, G >= 128, P <= 4), as
+  // PlaneFmt::mma2: every decoded operand feeds both m-tiles' chains.
+  template <int GPW>
+  struct Mma2 {
+    f32x4_t cinit[2][GPW];
+    PlaneDecode d;
+  };
+  template <int GPW>
+  static __device__ __forceinline__ void prepare_mma2(uint32_t (&xa)[2][GPW][16], Mma2<GPW>& mx) {
+    static_assert(G != 64, "the two-m-tile form takes whole-tile codes");
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        xa[mt][gi][11] ^= 0x80008000u;
+        xa[mt][gi][15] ^= 0x80008000u;
+      }
+      f32x4_t cs[GPW][2];
+      plane_chain_starts<GPW, 1>(xa[mt], cs);
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) mx.cinit[mt][gi] = cs[gi][0];
+    }
+    mx.d = plane_decode();
+  }
+  template <int GPW>
+  static __device__ __forceinline__ void mma2(const Slot<GPW>& sl, const uint32_t (&xa)[2][GPW][16],
+                                              const Mma2<GPW>& mx, float4 (&yv)[2]) {
+    static_assert(P <= 4 && G != 64, "two m-tiles hold up to four planes of whole-tile codes");
+    // Each chain is weighted by its alpha = d x a, exact in fp32 (an fp16
+    // significand times an 8-bit code), so no per-super-block sums are held.
+    constexpr int IL = GPW < 2 ? GPW : 2;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) yv[mt] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int g0c = 0; g0c < GPW; g0c += IL) {
+        PlaneViews v[IL];
+        f32x4_t c[2][IL];
+#pragma unroll
+        for (int u = 0; u < IL; ++u) {
+          v[u] = plane_views(sl.w[g0c + u][p]);
+          c[0][u] = mx.cinit[0][g0c + u];
+          c[1][u] = mx.cinit[1][g0c + u];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int u = 0; u < IL; ++u) {
+            uint32_t b[4];
+            plane_operands_t(v[u], t, mx.d, b);
+            c[0][u] = mfma16x16x32(&xa[0][g0c + u][4 * t], b, c[0][u]);
+            c[1][u] = mfma16x16x32(&xa[1][g0c + u][4 * t], b, c[1][u]);
+          }
+#pragma unroll
+        for (int u = 0; u < IL; ++u) {
+          const int gi = g0c + u;
+          const float a = sl.dscale(gi) * (float)sl.code(p, gi, 0);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            yv[mt].x = fmaf(a, c[mt][u][0], yv[mt].x);
+            yv[mt].y = fmaf(a, c[mt][u][1], yv[mt].y);
+            yv[mt].z = fmaf(a, c[mt][u][2], yv[mt].z);
+            yv[mt].w = fmaf(a, c[mt][u][3], yv[mt].w);
+          }
+        }
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) yv[mt] = make_float4(-yv[mt].x, -yv[mt].y, -yv[mt].z, -yv[mt].w);
   }
 };
 
@@ -1925,6 +2066,74 @@ __global__ void __launch_bounds__(64 * MAXW)
   });
   if constexpr (ARGMAX)
     gemm_argmax_epilogue<MAXW>(best, wave, lane, nwaves, ws, M, N, ho);
+}
+
+// Sign-plane mat-mul for blocks of 17..32 rows at K <= 4096 (eight waves or
+// fewer), format F with a two-m-tile tile (PlaneFmt, or SaFmt at G >= 128):
+// the M <= 16 kernel with both m-tiles of X in registers, as
+// k_gemm_w4a16_x2 does for W4A16, so the weights are read and decoded once
+// for the block.
+template <class F, int GPW, int D>
+__global__ void __launch_bounds__(64 * 8)
+    k_gemm_planes_x2(const uint8_t* __restrict__ blob, const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
+                     int M, int N, int KT, int NT) {
+  constexpr int MAXW = 8, C = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r = lane & 15;
+  const int g0 = wave * GPW;
+  const int K = KT * 128;
+  const typename F::View bv = F::view(blob, KT, NT);
+  const int T = tiles_of_wg(NT);
+
+  // Rows 16..M-1 of the second m-tile read zero past M (buffer range).
+  XRows<GPW> xr0, xr1;
+  load_x_rows<GPW>(X, M, K, g0, KT, lane, xr0);
+  load_x_rows<GPW>(X + (size_t)16 * K, M - 16, K, g0, KT, lane, xr1);
+  __builtin_amdgcn_sched_barrier(0);
+  typename F::template Slot<GPW> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    F::template load<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __shared__ ChunkStage<float4, C, MAXW, 64> stage[2];
+  __shared__ uint4 xt[MAXW][2][256];  // a wave's two transposition regions (2 x 4 KiB)
+  uint32_t xa[2][GPW][16];
+  transpose_x_rows<GPW>(xr0, xt[wave][0], lane, q, r, xa[0]);
+  transpose_x_rows<GPW>(xr1, xt[wave][1], lane, q, r, xa[1]);
+  typename F::template Mma2<GPW> mx;
+  F::template prepare_mma2<GPW>(xa, mx);
+  RowBest4 unused;
+
+  int i0 = 0;
+  auto step = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int i = i0 + j;
+    float4 yv[2];
+    F::template mma2<GPW>(ring[j], xa, mx, yv);
+    stage[0].put(i, i < T, wave, lane, yv[0]);
+    stage[1].put(i, i < T, wave, lane, yv[1]);
+    // Slot j is refilled only after its last use, so it keeps its registers.
+    __builtin_amdgcn_sched_barrier(0);
+    F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+    const int ci = i % C;
+    if (i < T && (ci == C - 1 || i == T - 1)) {
+      __syncthreads();
+      const int first = i - ci;
+      const int mt = wave / C, cc = wave % C;  // (m-tile, tile of the chunk) of waves 0-3
+      if (mt < 2 && cc <= ci)
+        gemm_emit<false>(stage[mt].sum(i, cc, nwaves, lane), q, r, row_tile(first + cc), M - 16 * mt, N,
+                         Y + (size_t)16 * mt * N, unused);
+    }
+  };
+  // Whole rounds of the ring, then the tiles of a partial last round one by
+  // one, so no step runs on an empty tile.
+  const int whole = T - T % D;
+  for (; i0 < whole; i0 += D) static_for<0, D>(step);
+  static_for<0, D - 1>([&](auto jc) {
+    if (decltype(jc)::value < T - whole) step(jc);
+  });
 }
 
 }  // namespace

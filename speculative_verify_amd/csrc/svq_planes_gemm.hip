@@ -31,6 +31,25 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
     return SVQ_OK;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096 && P <= 4) {
+    // Two m-tiles held in registers: the M <= 16 kernel's eight-wave shape,
+    // each decoded weight feeding both m-tiles.
+    Shape sh;
+    if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
+    dispatch_p(P, [&](auto Pc) {
+      if constexpr (decltype(Pc)::value <= 4) {
+        using F = PlaneFmt<decltype(Pc)::value>;
+        auto go = [&](auto Gc) {
+          hipLaunchKernelGGL((k_gemm_planes_x2<F, decltype(Gc)::value, 1>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+                             st, packed, X, Y, M, (int)N, sh.KT, sh.NT);
+        };
+        if (sh.gpw == 1) go(ic<1>{});
+        else if (sh.gpw == 2) go(ic<2>{});
+        else go(ic<4>{});
+      }
+    });
+    return launched("gemm_smallm_binplane");
+  }
   if (M > SVQ_MAX_M) {
     // Blocks of 17..64 rows: the weights are read and decoded once for the
     // whole block (mmq_planes.h).
