@@ -359,6 +359,28 @@ def test_gemm_planes_midm_every_m(kind):
         check_close(got, Y, A, f"{kind} M={M} P={P}")
 
 
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_gemm_planes_two_mtiles(K):
+    # Blocks of 17..32 rows at K <= 4096 with up to four planes (and sa* at
+    # G >= 128) keep both m-tiles of X in registers; K = 2048 and 4096 take
+    # two and four column tiles a wave.  Several tiles a workgroup
+    # (N = 9000), a ragged last tile and a ragged second m-tile.
+    rng = np.random.default_rng(4150 + K)
+    N = 9000
+    for M, P in [(17, 1), (24, 3), (32, 4), (29, 2)]:
+        X = synth.activations(rng, M, K)
+        signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+        Y, A = oracle.linear_binplane(signs, alpha, X)
+        print(f"two m-tiles planes K={K} M={M} P={P}", flush=True)
+        check_close(run_gemm_binplane(signs, alpha, X), Y, A, f"planes K={K} M={M} P={P}")
+    for M, P, G in [(17, 2, 128), (32, 3, 256), (25, 4, 128)]:
+        X = synth.activations(rng, M, K)
+        s2, c2, d2 = synth.sa_weights(rng, N, K, P, G)
+        Y, A = oracle.linear_sa(s2, c2, d2, X, G=G)
+        print(f"two m-tiles sa K={K} M={M} P={P} G={G}", flush=True)
+        check_close(run_gemm_sa(s2, c2, d2, X, G), Y, A, f"sa K={K} M={M} P={P} G={G}")
+
+
 @pytest.mark.parametrize("M", [65, 100, 128, 193])
 def test_gemm_above_64_rows(M):
     # Blocks above 64 rows (prefill chunks) run as consecutive launches of 64
