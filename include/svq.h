@@ -251,8 +251,10 @@ int gemv_binplane(const uint8_t* packed, const uint16_t* x, uint16_t* y,
  * sec. 3.2: block size 16):  Y[m][n] = the W4A16 result for row m of X.
  * Blocks of 16 < M <= 64 rows (a prefill chunk; the ShiftAddQwen README
  * places batches below 64 in the quantized mat-mul regime) take the same
- * kernel with two 16-row tiles of X (M <= 32, K <= 4096) or a kernel that
- * streams X with the weights; the result is defined the same way.  Larger
+ * kernel: with two 16-row tiles of X (M <= 32, K <= 4096, more row tiles
+ * than CUs), or with each 16-row tile of the block on workgroups of its own
+ * (other blocks at K <= 4096); above K = 4096, a kernel that streams X with
+ * the weights.  The result is defined the same way.  Larger
  * blocks (up to SVQ_MAX_M_GEMM rows) run as consecutive launches of
  * SVQ_BLOCK_M rows each, each reading the weights once.
  *   X  [M][K] bf16 bits, 16-byte aligned;  Y [M][N] bf16 bits, 2-byte aligned.
@@ -264,8 +266,8 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
 /*
  * gemm_smallm_binplane -- DEVICE pointers, asynchronous on `stream`.
  * Y[m][n] = the binary-plane result for row m of X, M in 1..SVQ_MAX_M_GEMM
- * (17..64 rows: a kernel that streams X and decodes each weight tile once for
- * the block; above 64, consecutive launches of SVQ_BLOCK_M rows).
+ * (17..64 rows: as gemm_smallm_w4a16, the two-m-tile form taking up to four
+ * planes; above 64, consecutive launches of SVQ_BLOCK_M rows).
  */
 int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y,
                          int32_t M, int64_t N, int64_t K, int32_t G, int32_t P,
@@ -288,8 +290,9 @@ int gemv_sa(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
  * gemm_smallm_sa -- DEVICE pointers, asynchronous on `stream`.
  * Y[m][n] = the sa* result for row m of X, M in 1..SVQ_MAX_M_GEMM (the
  * verify pass over a drafted block, as gemm_smallm_w4a16; the README's
- * batches below 64 run its quantized mat-mul: 17..64 rows take the streaming
- * block kernel, larger blocks consecutive launches of SVQ_BLOCK_M rows).
+ * batches below 64 run its quantized mat-mul: 17..64 rows as
+ * gemm_smallm_w4a16, the two-m-tile form taking up to four planes at
+ * G >= 128; larger blocks consecutive launches of SVQ_BLOCK_M rows).
  * Errors: as gemv_sa, plus SHAPE for M outside 1..SVQ_MAX_M_GEMM.
  */
 int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y,

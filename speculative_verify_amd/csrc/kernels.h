@@ -675,6 +675,32 @@ __device__ __forceinline__ int tiles_of_wg(int NT) { return (NT - 1 - (int)block
 // Row tile of the workgroup's i-th iteration.
 __device__ __forceinline__ int row_tile(int i) { return blockIdx.x + i * gridDim.x; }
 
+// Row tiles of an M <= 16 mat-mul workgroup.  With ms == 1 the grid walks
+// the row tiles in grid-stride order (row_tile, tiles_of_wg).  With ms > 1
+// one launch covers a block of 16 < M <= 64 rows as ms 16-row m-tiles:
+// workgroup b computes m-tile (b / 8) % ms for the row tiles j, j + G / ms,
+// ... (G workgroups, a multiple of 8 ms), j = b % 8 + 8 (b / (8 ms)).  The
+// ms workgroups of one row-tile set then share b % 8, which round-robin
+// dispatch places on one XCD, and run side by side, so the later readers of
+// a weight tile find it in that XCD's L2.
+struct TileWalk {
+  int first, stride, mt;
+  __device__ __forceinline__ int tile(int i) const { return first + i * stride; }
+  __device__ __forceinline__ int count(int NT) const { return first < NT ? (NT - 1 - first) / stride + 1 : 0; }
+};
+
+__device__ __forceinline__ TileWalk tile_walk(int ms) {
+  const int b = (int)blockIdx.x, c = b >> 3, g = (int)gridDim.x >> 3;  // dispatch rounds of 8 workgroups
+  int cq, gq;  // c / ms and g / ms, by constant divisors (ms <= 4)
+  switch (ms) {
+    case 1: return TileWalk{b, (int)gridDim.x, 0};
+    case 2: cq = c >> 1; gq = g >> 1; break;
+    case 3: cq = c / 3; gq = g / 3; break;
+    default: cq = c >> 2; gq = g >> 2; break;
+  }
+  return TileWalk{(b & 7) + 8 * cq, 8 * gq, c - cq * ms};
+}
+
 // ---------------------------------------------------------------------------
 // M = 1 mat-vec cores.  Each returns the lane's partial sum for row r over its
 // k sub-ranges of the wave's groups.  zc[g] (lane_zero_code_chains) is the
@@ -1792,12 +1818,20 @@ __device__ __forceinline__ void gemm_emit(const float4& tot, int q, int r, int r
 template <int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemm_w4a16(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
-                 uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT) {
+                 uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT, int ms) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
   const BlobView bv = int4_view(blob, KT, NT);
-  const int T = tiles_of_wg(NT);
+  // The heads never split their rows (M <= 16).
+  const TileWalk tw = ARGMAX ? TileWalk{(int)blockIdx.x, (int)gridDim.x, 0} : tile_walk(ms);
+  const int T = tw.count(NT);
+  if constexpr (!ARGMAX) {
+    // This workgroup's m-tile: 16 rows of X (K / 2 dwords each) and of Y.
+    Xw += (size_t)tw.mt * 16 * KT * 64;
+    Y += (size_t)tw.mt * 16 * N;
+    M = M - 16 * tw.mt < 16 ? M - 16 * tw.mt : 16;
+  }
 
   // In the full-register shapes X comes in coalesced and is transposed
   // through LDS; the lean ones (16 waves of four column tiles, 128
@@ -1814,7 +1848,7 @@ __global__ void __launch_bounds__(64 * MAXW)
   Int4Slot<GPW> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    load_int4_tile<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    load_int4_tile<GPW>(ring[j], bv, tw.tile(j), j < T, g0, lane, r);
     // Issue each slot's loads in the same order the loop refills them.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1875,14 +1909,14 @@ __global__ void __launch_bounds__(64 * MAXW)
     stage.put(i, i < T, wave, lane, yv);
     // Slot j is refilled only after its last use, so it keeps its registers.
     __builtin_amdgcn_sched_barrier(0);
-    load_int4_tile<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+    load_int4_tile<GPW>(ring[j], bv, tw.tile(i + D), i + D < T, g0, lane, r);
     const int ci = i % C;
     if (i < T && (ci == C - 1 || i == T - 1)) {
       __syncthreads();
       const int first = i - ci;
       // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
       // same outputs of every tile, so its columns arrive in increasing n.
-      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, best);
+      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, tw.tile(first + wave), M, N, Y, best);
     }
   };
   // Whole rounds of the ring, then the tiles of a partial last round (held in
@@ -1994,12 +2028,20 @@ __global__ void __launch_bounds__(64 * 8)
 template <class F, int GPW, int MAXW, int D, bool ARGMAX>
 __global__ void __launch_bounds__(64 * MAXW)
     k_gemm_planes(const uint8_t* __restrict__ blob, const uint32_t* __restrict__ Xw, uint16_t* __restrict__ Y,
-                    uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT) {
+                    uint8_t* __restrict__ ws, HeadOut ho, int M, int N, int KT, int NT, int ms) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int g0 = wave * GPW;
   const typename F::View bv = F::view(blob, KT, NT);
-  const int T = tiles_of_wg(NT);
+  // The heads never split their rows (M <= 16).
+  const TileWalk tw = ARGMAX ? TileWalk{(int)blockIdx.x, (int)gridDim.x, 0} : tile_walk(ms);
+  const int T = tw.count(NT);
+  if constexpr (!ARGMAX) {
+    // This workgroup's m-tile: 16 rows of X (K / 2 dwords each) and of Y.
+    Xw += (size_t)tw.mt * 16 * KT * 64;
+    Y += (size_t)tw.mt * 16 * N;
+    M = M - 16 * tw.mt < 16 ? M - 16 * tw.mt : 16;
+  }
 
   // In the full-register shapes X comes in coalesced and is transposed
   // through LDS; the lean ones (16 waves of four column tiles, 128
@@ -2016,7 +2058,7 @@ __global__ void __launch_bounds__(64 * MAXW)
   typename F::template Slot<GPW> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    F::template load<GPW>(ring[j], bv, row_tile(j), j < T, g0, lane, r);
+    F::template load<GPW>(ring[j], bv, tw.tile(j), j < T, g0, lane, r);
     // Issue each slot's loads in the same order the loop refills them.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -2047,14 +2089,14 @@ __global__ void __launch_bounds__(64 * MAXW)
     stage.put(i, i < T, wave, lane, yv);
     // Slot j is refilled only after its last use, so it keeps its registers.
     __builtin_amdgcn_sched_barrier(0);
-    F::template load<GPW>(ring[j], bv, row_tile(i + D), i + D < T, g0, lane, r);
+    F::template load<GPW>(ring[j], bv, tw.tile(i + D), i + D < T, g0, lane, r);
     const int ci = i % C;
     if (i < T && (ci == C - 1 || i == T - 1)) {
       __syncthreads();
       const int first = i - ci;
       // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
       // same outputs of every tile, so its columns arrive in increasing n.
-      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, row_tile(first + wave), M, N, Y, best);
+      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, tw.tile(first + wave), M, N, Y, best);
     }
   };
   // Whole rounds of the ring, then the tiles of a partial last round (held in

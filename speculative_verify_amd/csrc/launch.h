@@ -125,6 +125,50 @@ inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* 
   return SVQ_OK;
 }
 
+// Launch shape of a block of 16 < M <= 64 rows run as ms = ceil(M / 16)
+// m-tiles on the M <= 16 kernels in one launch (TileWalk in kernels.h):
+// ms * gper workgroups, gper a multiple of 8 of at most CUs / ms that does
+// not exceed the row tiles rounded up to 8; the ring depth follows the row
+// tiles each workgroup owns, as in plan().
+inline int plan_msplit(int64_t N, int64_t K, int32_t M, LaunchPref pref, Shape* s, int* ms) {
+  if (int rc = plan(N, K, 4, pref, s)) return rc;
+  int cus = 0;
+  if (int rc = device_cus(&cus)) return rc;
+  *ms = (M + 15) / 16;
+  const int sets = (s->NT + 7) / 8;
+  int per = cus / (8 * *ms);
+  per = per < 1 ? 1 : per > sets ? sets : per;
+  const int gper = 8 * per;
+  s->grid = gper * *ms;
+  const int tmin = s->NT / gper;
+  const int dmax = env_int("SVQ_PIPE_DEPTH", 1, 6, pref.max_depth);
+  const bool shallow = tmin <= pref.shallow && env_int("SVQ_PIPE_DEPTH", 1, 6, 0) == 0;
+  s->depth = tmin < 1 || shallow ? 1 : tmin > dmax ? dmax : tmin;
+  return SVQ_OK;
+}
+
+// Kernel choice for a block of 16 < M <= 64 rows at K <= 4096 (interleaved
+// A/B runs on MI355X, K = 4096 unless noted, against the streaming kernels
+// of mmq.h / mmq_planes.h that read X with the weights):
+// * the m-split (plan_msplit) was faster wherever it replaced them:
+//   W4A16 M = 48 and 64 by 10-31% (N = 4096 and 12288; M = 64 at K = 2048
+//   by 12%), sign planes and sa* M = 48 and 64 by 8-20%, P = 6 and sa* at
+//   G = 64 by 8-24% (M = 32 and 64);
+// * against the two-m-tile kernel (k_gemm_w4a16_x2, k_gemm_planes_x2:
+//   M <= 32, P <= 4, sa* G >= 128), which decodes each weight tile once for
+//   both m-tiles, the m-split won only where every workgroup owns a single
+//   row tile (W4A16 M = 32, N = 4096: -10%) and lost where they own several
+//   (N = 32768: +8% W4A16, +14% sign planes; N = 12288: +1-6% at M = 24 and
+//   32 for sign planes and sa*, within noise for W4A16).
+// So the two-m-tile kernel takes M <= 32 when the row tiles outnumber the
+// CUs and the m-split takes every other block.
+inline int use_two_mtiles(int64_t N, int32_t M, bool applies, bool* out) {
+  int cus = 0;
+  if (int rc = device_cus(&cus)) return rc;
+  *out = applies && M <= 2 * SVQ_MAX_M && (N + 15) / 16 > cus;
+  return SVQ_OK;
+}
+
 // Set by dispatch() when a planned launch is wider than every kernel shape it
 // may instantiate (the launch is then skipped); reported by launched().
 inline thread_local bool g_shape_mismatch = false;

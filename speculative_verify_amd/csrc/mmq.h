@@ -6,6 +6,9 @@
 //
 // The M <= 16 kernels keep a wave's whole K slice of X in registers; at
 // M = 64 that slice no longer fits, so here X streams with the weights.
+// Blocks at K <= 4096 run on the M <= 16 kernel instead (each 16-row tile on
+// workgroups of its own, or two tiles in registers), which measured faster
+// for every block height; this kernel serves K above 4096.
 // Work decomposition: a workgroup owns R consecutive 16-row weight tiles (a
 // block) at a time, grid-stride over blocks; its 8 waves split K, wave w
 // walking the 128-wide column tiles [w * CK, (w + 1) * CK) of the block.  A

@@ -5,6 +5,8 @@
 //   Y[m][n] = sum_g sum_p alpha[p][n][g] * sum_{k in g} b[p][n][k] * X[m][k]
 //   (ShiftAddQwen README, intro and "Method / Format"; the README places
 //   batches below 64 in its quantized mat-mul regime)
+// Blocks at K <= 4096 run on the M <= 16 kernel instead (see mmq.h); this
+// kernel serves K above 4096.
 //
 // The decomposition is the W4A16 streaming kernel's (mmq.h): a workgroup owns
 // R consecutive 16-row weight tiles (a block) at a time, its 8 waves split K,

@@ -34,7 +34,7 @@ int launch_head_w4a16(const char* fn, const uint8_t* packed, const uint16_t* X, 
   } else {
     dispatch(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, (uint16_t*)nullptr, ws, h, M, (int)N, sh.KT, sh.NT);
+                         packed, Xw, (uint16_t*)nullptr, ws, h, M, (int)N, sh.KT, sh.NT, 1);
     });
   }
   return launched(fn);
@@ -112,7 +112,22 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
     return SVQ_OK;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096) {
+  bool two = false;
+  if (M > SVQ_MAX_M && K <= 4096)
+    if (int rc = use_two_mtiles(N, M, true, &two)) return rc;
+  if (M > SVQ_MAX_M && K <= 4096 && !two) {
+    // The block as ceil(M / 16) m-tiles of the M <= 16 kernel in one launch.
+    Shape sh;
+    int ms = 1;
+    if (int rc = plan_msplit(N, K, M, kPrefGemmW4, &sh, &ms)) return rc;
+    const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+    dispatch(sh, [&](auto G, auto W, auto D) {
+      hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
+                         packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT, ms);
+    });
+    return launched("gemm_smallm_w4a16");
+  }
+  if (two) {
     // Two m-tiles held in registers: the M <= 16 kernel's eight-wave shape.
     Shape sh;
     if (int rc = plan(N, K, 4, kPrefGemmW4, &sh)) return rc;
@@ -134,6 +149,7 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
     return launched("gemm_smallm_w4a16");
   }
   if (M > SVQ_MAX_M) {
+    // Blocks of 17..64 rows above K = 4096: X streams with the weights.
     MmqShape sh;
     if (int rc = plan_mmq(N, M, &sh)) return rc;
     const int KT = (int)(K / 128), NT = (int)((N + 15) / 16);
@@ -171,7 +187,7 @@ int gemm_smallm_w4a16(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int
   const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
   dispatch(sh, [&](auto G, auto W, auto D) {
     hipLaunchKernelGGL((k_gemm_w4a16<SVQ_KARGS(G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                       packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
+                       packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT, 1);
   });
   return launched("gemm_smallm_w4a16");
 }

@@ -31,7 +31,25 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
     return SVQ_OK;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096 && P <= 4) {
+  bool two = false;
+  if (M > SVQ_MAX_M && K <= 4096)
+    if (int rc = use_two_mtiles(N, M, P <= 4, &two)) return rc;
+  if (M > SVQ_MAX_M && K <= 4096 && !two) {
+    // The block as ceil(M / 16) m-tiles of the M <= 16 kernel in one launch.
+    Shape sh;
+    int ms = 1;
+    if (int rc = plan_msplit(N, K, M, kPrefGemmPlanes, &sh, &ms)) return rc;
+    const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+    dispatch_p(P, [&](auto Pc) {
+      using F = PlaneFmt<decltype(Pc)::value>;
+      dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
+        hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
+                           st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT, ms);
+      });
+    });
+    return launched("gemm_smallm_binplane");
+  }
+  if (two) {
     // Two m-tiles held in registers: the M <= 16 kernel's eight-wave shape,
     // each decoded weight feeding both m-tiles.
     Shape sh;
@@ -51,8 +69,8 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
     return launched("gemm_smallm_binplane");
   }
   if (M > SVQ_MAX_M) {
-    // Blocks of 17..64 rows: the weights are read and decoded once for the
-    // whole block (mmq_planes.h).
+    // Blocks of 17..64 rows above K = 4096: the weights are read and decoded
+    // once for the whole block (mmq_planes.h).
     int rc = SVQ_OK;
     dispatch_p(P, [&](auto Pc) {
       rc = launch_mmq_planes<MmqPlanes<decltype(Pc)::value>>("gemm_smallm_binplane", packed, X, Y, M, N, K, st);
@@ -66,7 +84,7 @@ int gemm_smallm_binplane(const uint8_t* packed, const uint16_t* X, uint16_t* Y, 
     using F = PlaneFmt<decltype(Pc)::value>;
     dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0, st,
-                         packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
+                         packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT, 1);
     });
   });
   return launched("gemm_smallm_binplane");
@@ -91,7 +109,7 @@ int lmhead_argmax_binplane(const uint8_t* packed, const uint16_t* X, int32_t M, 
     using F = PlaneFmt<decltype(Pc)::value>;
     dispatch<kMaxDepthPlanesGemm>(sh, [&](auto G, auto W, auto D) {
       hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), true>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                         st, packed, Xw, (uint16_t*)nullptr, ws, with_levels(ho, sh), M, (int)N, sh.KT, sh.NT);
+                         st, packed, Xw, (uint16_t*)nullptr, ws, with_levels(ho, sh), M, (int)N, sh.KT, sh.NT, 1);
     });
   });
   return launched(fn);

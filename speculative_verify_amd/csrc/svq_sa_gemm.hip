@@ -1,7 +1,8 @@
 // svq_sa_gemm.hip -- small-M device entry point for the sa* storage of sign
 // planes (ShiftAddQwen README, "Method / Format"): the verify mat-mul over a
 // drafted block of M <= 16 rows on 16x16x32 bf16 MFMA, and blocks of up to
-// 64 rows on the streaming kernel of mmq_planes.h.
+// 64 rows on the same kernel (or the streaming kernel of mmq_planes.h above
+// K = 4096).
 //   Y = X W^T with W[n][k] = d[n][k/256] * sum_p a[p][n][k/G] * b[p][n][k]
 #include <hip/hip_runtime.h>
 
@@ -28,7 +29,33 @@ int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_
     return SVQ_OK;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (M > SVQ_MAX_M && M <= 2 * SVQ_MAX_M && K <= 4096 && P <= 4 && G != 64) {
+  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
+  // The M <= 16 kernel over ms m-tiles of 16 rows (ms = 1 for M <= 16).
+  auto launch_tiles = [&](const Shape& sh, int ms) {
+    dispatch_group(G, [&](auto Gc) {
+      dispatch_p(P, [&](auto Pc) {
+        if constexpr (decltype(Pc)::value >= 2) {
+          using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
+          dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
+            hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves),
+                               0, st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT, ms);
+          });
+        }
+      });
+    });
+    return launched("gemm_smallm_sa");
+  };
+  bool two = false;
+  if (M > SVQ_MAX_M && K <= 4096)
+    if (int rc = use_two_mtiles(N, M, P <= 4 && G != 64, &two)) return rc;
+  if (M > SVQ_MAX_M && K <= 4096 && !two) {
+    // The block as ceil(M / 16) m-tiles of the M <= 16 kernel in one launch.
+    Shape sh;
+    int ms = 1;
+    if (int rc = plan_msplit(N, K, M, kPrefGemmPlanes, &sh, &ms)) return rc;
+    return launch_tiles(sh, ms);
+  }
+  if (two) {
     // Two m-tiles held in registers (k_gemm_planes_x2), each decoded weight
     // feeding both m-tiles.
     Shape sh;
@@ -51,8 +78,8 @@ int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_
     return launched("gemm_smallm_sa");
   }
   if (M > SVQ_MAX_M) {
-    // Blocks of 17..64 rows: the weights are read and decoded once for the
-    // whole block (mmq_planes.h).
+    // Blocks of 17..64 rows above K = 4096: the weights are read and decoded
+    // once for the whole block (mmq_planes.h).
     int rc = SVQ_OK;
     dispatch_group(G, [&](auto Gc) {
       dispatch_p(P, [&](auto Pc) {
@@ -65,19 +92,7 @@ int gemm_smallm_sa(const uint8_t* packed, const uint16_t* X, uint16_t* Y, int32_
   }
   Shape sh;
   if (int rc = plan(N, K, 4, kPrefGemmPlanes, &sh)) return rc;
-  const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);
-  dispatch_group(G, [&](auto Gc) {
-    dispatch_p(P, [&](auto Pc) {
-      if constexpr (decltype(Pc)::value >= 2) {
-        using F = SaFmt<decltype(Pc)::value, decltype(Gc)::value>;
-        dispatch<kMaxDepthSa>(sh, [&](auto G, auto W, auto D) {
-          hipLaunchKernelGGL((k_gemm_planes<SVQ_KARGS_F(F, G, W, D), false>), dim3(sh.grid), dim3(64 * sh.waves), 0,
-                             st, packed, Xw, Y, (uint8_t*)nullptr, HeadOut{}, M, (int)N, sh.KT, sh.NT);
-        });
-      }
-    });
-  });
-  return launched("gemm_smallm_sa");
+  return launch_tiles(sh, 1);
 }
 
 }  // extern "C"

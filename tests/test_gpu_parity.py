@@ -320,11 +320,13 @@ def test_gemm_w4a16_two_mtiles_many_tiles_per_workgroup(M, N, K):
     check_close(got[:, rows], Y, A, f"M={M} N={N} K={K} sample")
 
 
-@pytest.mark.parametrize("M,N,K,P", [(17, 300, 512, 3), (40, 1000, 1024, 2), (64, 4096, 4096, 3), (64, 77, 2048, 6)])
+@pytest.mark.parametrize("M,N,K,P", [(17, 300, 512, 3), (40, 1000, 1024, 2), (64, 4096, 4096, 3), (64, 77, 2048, 6),
+                                   (40, 700, 8192, 3), (24, 300, 6144, 6)])
 def test_gemm_planes_midm(M, N, K, P):
-    # Sign planes (fp16 alphas and sa* codes) above 16 rows: the streaming
-    # kernel that decodes each weight tile once for all m-tiles, each row
-    # against the oracle.
+    # Sign planes (fp16 alphas and sa* codes) above 16 rows, each row against
+    # the oracle: the 16-row tiles of the block on workgroups of their own at
+    # K <= 4096, the streaming kernel that decodes each weight tile once for
+    # all m-tiles above.
     rng = np.random.default_rng(M * 7 + N + K + P)
     signs, alpha = synth.binplane_weights(rng, N, K, P=P)
     X = synth.activations(rng, M, K)
@@ -403,8 +405,9 @@ def test_gemm_above_64_rows(M):
 
 @pytest.mark.parametrize("M,N,K,P", [(40, 40000, 1024, 3), (64, 20000, 2048, 2), (24, 33333, 512, 4)])
 def test_gemm_planes_midm_many_blocks_per_workgroup(M, N, K, P):
-    # Enough row tiles that every workgroup walks several blocks (grid-stride
-    # over blocks, the X and weight cursors crossing block boundaries).
+    # Enough row tiles that every workgroup walks many of them (at K <= 4096
+    # each 16-row tile of the block on workgroups of its own; the ragged
+    # last m-tile of M = 40 and 24).
     rng = np.random.default_rng(M + N + K + P)
     signs, alpha = synth.binplane_weights(rng, N, K, P=P)
     X = synth.activations(rng, M, K)
@@ -415,6 +418,54 @@ def test_gemm_planes_midm_many_blocks_per_workgroup(M, N, K, P):
     s2, codes, d = synth.sa_weights(rng, N, K, max(P, 2), G)
     Y, A = oracle.linear_sa(s2, codes, d, X, G=G)
     check_close(run_gemm_sa(s2, codes, d, X, G), Y, A, f"sa M={M} N={N}")
+
+
+@pytest.mark.parametrize("M,N,K,P", [(40, 20000, 6144, 3), (64, 13000, 8192, 2)])
+def test_gemm_planes_midm_streaming_many_blocks(M, N, K, P):
+    # Above K = 4096 the streaming kernel: every workgroup walks several
+    # blocks (grid-stride over blocks, the X and weight cursors crossing
+    # block boundaries); checked on a sample of output rows.
+    rng = np.random.default_rng(M + N + K + P)
+    signs, alpha = synth.binplane_weights(rng, N, K, P=P)
+    X = synth.activations(rng, M, K)
+    rows = np.unique(np.concatenate([np.arange(0, 48), np.arange(N - 40, N), rng.integers(0, N, 400)]))
+    print(f"planes streaming many blocks M={M} N={N} K={K} P={P}", flush=True)
+    got = run_gemm_binplane(signs, alpha, X)
+    Y, A = oracle.linear_binplane(signs[:, rows], alpha[:, rows], X)
+    check_close(got[:, rows], Y, A, f"planes M={M} N={N} K={K} sample")
+    G = 128 if P % 2 else 64
+    s2, codes, d = synth.sa_weights(rng, N, K, max(P, 2), G)
+    got = run_gemm_sa(s2, codes, d, X, G)
+    Y, A = oracle.linear_sa(s2[:, rows], codes[:, rows], d[rows], X, G=G)
+    check_close(got[:, rows], Y, A, f"sa M={M} N={N} K={K} G={G} sample")
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("w4a16", 47, 20000, 2048), ("w4a16", 18, 40, 4096), ("w4a16", 64, 12000, 4096),
+                                        ("planes", 33, 9000, 4096), ("planes", 50, 35, 1024),
+                                        ("sa", 64, 5000, 4096), ("sa", 20, 1000, 4096)])
+def test_gemm_msplit_layouts(kind, M, N, K):
+    # Blocks of 17..64 rows at K <= 4096 as 16-row tiles on workgroups of
+    # their own: ragged last m-tiles (47, 33, 50, 18, 20 rows), workgroups
+    # that own many row tiles (N = 20000, 12000, 9000), and workgroups that
+    # own none (N = 40 and 35: fewer row tiles than workgroups per m-tile);
+    # checked on a sample of output rows.
+    rng = np.random.default_rng(M * 31 + N + K)
+    X = synth.activations(rng, M, K)
+    rows = np.unique(np.concatenate([np.arange(0, min(N, 48)), np.arange(max(0, N - 40), N), rng.integers(0, N, 300)]))
+    print(f"msplit {kind} M={M} N={N} K={K}", flush=True)
+    if kind == "w4a16":
+        codes, scales = synth.int4_weights(rng, N, K)
+        got = run_gemm_w4a16(codes, scales, X)
+        Y, A = oracle.linear_w4a16(codes[rows], scales[rows], X)
+    elif kind == "planes":
+        signs, alpha = synth.binplane_weights(rng, N, K, P=3)
+        got = run_gemm_binplane(signs, alpha, X)
+        Y, A = oracle.linear_binplane(signs[:, rows], alpha[:, rows], X)
+    else:
+        signs, codes, d = synth.sa_weights(rng, N, K, 3, 128)
+        got = run_gemm_sa(signs, codes, d, X, 128)
+        Y, A = oracle.linear_sa(signs[:, rows], codes[:, rows], d[rows], X, G=128)
+    check_close(got[:, rows], Y, A, f"{kind} M={M} N={N} K={K} sample")
 
 
 @pytest.mark.parametrize("M,P", [(20, 1), (33, 3), (64, 6)])
