@@ -928,7 +928,8 @@ def _under_knobs(fn, monkeypatch):
 
 @pytest.mark.parametrize("kind,M", [("w4a16", 1), ("w4a16", 16), ("w4a16", 5), ("binplane", 1), ("binplane", 16),
                                     ("sa", 1), ("sa", 16), ("head", 1), ("head", 16), ("bphead", 1),
-                                    ("bphead", 16), ("verify", 16)])
+                                    ("bphead", 16), ("verify", 16), ("w4a16", 40), ("w4a16", 24),
+                                    ("binplane", 64), ("sa", 33)])
 def test_outputs_do_not_depend_on_launch_shape(kind, M, monkeypatch):
     N, K, P, G = 5008, 4096, 3, 64  # 313 row tiles (the device generators need whole tiles)
     X = synth.device_activations(M, K, 11).view(torch.int16)
@@ -978,6 +979,40 @@ def test_outputs_do_not_depend_on_launch_shape(kind, M, monkeypatch):
     ref = outs[0][1]
     for knobs, out in outs[1:]:
         assert np.array_equal(out, ref), f"{kind} M={M}: outputs differ under {knobs}"
+
+
+@pytest.mark.parametrize("kind,M,N", [("w4a16", 64, 3008), ("w4a16", 47, 704), ("planes", 40, 3008),
+                                      ("planes", 20, 2000), ("sa", 64, 1200), ("sa", 33, 3008)])
+def test_msplit_block_equals_its_16_row_slices(kind, M, N):
+    # A block of 17..64 rows at K <= 4096 with no more row tiles than CUs runs
+    # as 16-row m-tiles of the M <= 16 kernel in one launch: the same
+    # arithmetic per output as separate calls on each 16-row slice, so the
+    # outputs must match those calls bit for bit.
+    K, P, G = 4096, 3, 128
+    X = synth.device_activations(M, K, 31 + M).view(torch.int16)
+    if kind == "w4a16":
+        blob = synth.device_int4_blob(N, K, 32)
+    elif kind == "planes":
+        blob = synth.device_binplane_blob(N, K, P, 33)
+    else:
+        blob = synth.device_sa_blob(N, K, P, G, 34)
+
+    def run(Xs, m):
+        Y = torch.empty((m, N), dtype=torch.int16, device="cuda")
+        if kind == "w4a16":
+            svq.gemm_smallm_w4a16(blob, Xs, Y, m, N, K)
+        elif kind == "planes":
+            svq.gemm_smallm_binplane(blob, Xs, Y, m, N, K, P)
+        else:
+            svq.gemm_smallm_sa(blob, Xs, Y, m, N, K, P, G)
+        return Y
+
+    print(f"m-split {kind} M={M} N={N} against its slices", flush=True)
+    whole = run(X, M).cpu().numpy()
+    for m0 in range(0, M, 16):
+        m = min(16, M - m0)
+        part = run(X[m0:m0 + m].contiguous(), m).cpu().numpy()
+        assert np.array_equal(whole[m0:m0 + m], part), f"{kind} M={M}: rows {m0}..{m0 + m - 1} differ"
 
 
 # ---------------------------------------------------------------------------
