@@ -102,10 +102,10 @@ __device__ __forceinline__ uint32_t opaque_vgpr() {
 // The wave's index in its workgroup, as a wave-uniform (scalar) value: the
 // compiler cannot tell that threadIdx.x >> 6 is the same in every lane, and
 // would otherwise form every address term derived from it (the wave's
-// column tiles) with vector instructions at each step.  (In the 16 < M <= 64
-// sign-plane kernel this made the M = 64 calls 4-5% faster; in the other
-// kernels, whose per-step addressing is lighter, it made no difference or
-// cost 1-4%.)
+// column tiles) with vector instructions at each step.  (In the streaming
+// 16 < M <= 64 sign-plane kernel this made the M = 64 calls 4-5% faster; in
+// the other kernels, whose per-step addressing is lighter, it made no
+// difference or cost 1-4%.)
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // A copy of v the compiler cannot see through (its known bits are lost).  Only
@@ -1136,33 +1136,76 @@ __device__ __forceinline__ uint32_t nibble_offset(uint32_t w, int shift) {
   return shift >= 2 ? (w >> (shift - 2)) & 0x3Cu : (w << (2 - shift)) & 0x3Cu;
 }
 
+// Byte offsets ((w >> (4 j - 2)) & 0x3C) | lane_off of the eight nibbles j
+// of two sign dwords: one 64-bit shift of the pair hi:lo places nibble j of
+// both dwords at bits 2-5 (the bits shifted in from the other dword land
+// outside the mask), and a 64-bit shift issues at about the cost of a 32-bit
+// one.
+__device__ __forceinline__ void nibble_offsets2(uint32_t lo, uint32_t hi, uint32_t lane_off, uint32_t (&ol)[8],
+                                                uint32_t (&oh)[8]) {
+  const uint64_t w = (uint64_t)hi << 32 | lo;
+  uint64_t s[8];
+  asm("v_lshlrev_b64 %0, 2, %1" : "=v"(s[0]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 2, %1" : "=v"(s[1]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 6, %1" : "=v"(s[2]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 10, %1" : "=v"(s[3]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 14, %1" : "=v"(s[4]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 18, %1" : "=v"(s[5]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 22, %1" : "=v"(s[6]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 26, %1" : "=v"(s[7]) : "v"(w));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ol[j] = ((uint32_t)s[j] & 0x3Cu) | lane_off;
+    oh[j] = ((uint32_t)(s[j] >> 32) & 0x3Cu) | lane_off;
+  }
+}
+
+// The same offsets for one dword.
+__device__ __forceinline__ void nibble_offsets1(uint32_t w, uint32_t lane_off, uint32_t (&o)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = nibble_offset(w, 4 * j) | lane_off;
+}
+
+// Offsets of the sign dwords u0 and u0 + 1 of a run (o1 unused when the run
+// ends at u0).
+template <int U, class W>
+__device__ __forceinline__ void nibble_offsets_at(W&& w, int u0, uint32_t lane_off, uint32_t (&o0)[8],
+                                                  uint32_t (&o1)[8]) {
+  if (u0 + 1 < U) nibble_offsets2(w(u0), w(u0 + 1), lane_off, o0, o1);
+  else nibble_offsets1(w(u0), lane_off, o0);
+}
+
 // Lane's partial for row r over its k sub-ranges of the wave's groups, all
 // planes: sum_p alpha_p * (eight table reads per group).  lane_off is the
 // byte offset of the lane's table row (wave's tables + 64 q); the nibble's
 // offset has disjoint bits, so one AND-OR forms each address and the
-// (group, t, parity) part is the read's constant offset.
+// (group, t, parity) part is the read's constant offset.  Nibble j = 4
+// parity + t of a dword holds the signs of block t, parity.
 template <int GPW, int P>
 __device__ __forceinline__ float binplane_tile_partial_lut(const SignSlot<GPW, P>& sl, const SignLut<GPW>* luts,
                                                            uint32_t lane_off) {
   const char* base = reinterpret_cast<const char*>(luts);
+  auto sum8 = [&](int gi, const uint32_t (&o)[8]) {
+    float acc;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const float v = *reinterpret_cast<const float*>(base + o[4 * par + t] + 4 * SignLut<GPW>::base(gi, t, par));
+        acc = (t == 0 && par == 0) ? v : acc + v;
+      }
+    return acc;
+  };
+  // The (group, plane) dwords in order u = gi P + p, two at a time.
+  constexpr int U = GPW * P;
   float part = 0.f;
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const uint32_t w = sl.w[gi][p];
-      float acc;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int par = 0; par < 2; ++par) {
-          const uint32_t off =
-              (nibble_offset(w, 16 * par + 4 * t) | lane_off) + 4 * SignLut<GPW>::base(gi, t, par);
-          const float v = *reinterpret_cast<const float*>(base + off);
-          acc = (t == 0 && par == 0) ? v : acc + v;
-        }
-      part = fmaf(sl.a[p].f16(gi), acc, part);
-    }
+  for (int u = 0; u < U; u += 2) {
+    uint32_t o0[8], o1[8];
+    nibble_offsets_at<U>([&](int v) { return sl.w[v / P][v % P]; }, u, lane_off, o0, o1);
+    part = fmaf(sl.a[u % P].f16(u / P), sum8(u / P, o0), part);
+    if (u + 1 < U) part = fmaf(sl.a[(u + 1) % P].f16((u + 1) / P), sum8((u + 1) / P, o1), part);
+  }
   return part;
 }
 
@@ -1174,32 +1217,37 @@ __device__ __forceinline__ float sa_tile_partial_lut(const SaSlot<GPW, P, G>& sl
                                                      uint32_t lane_off) {
   const char* base = reinterpret_cast<const char*>(luts);
   constexpr int SB = GPW >= 2 ? GPW / 2 : 1;
+  constexpr int GB = GPW >= 2 ? 2 : 1;  // column tiles of a super-block held by the wave
+  constexpr int U = GB * P;
+  // Table sums of column tile gi, plane p, folded into the super-block sum.
+  auto fold = [&](int gi, int p, const uint32_t (&o)[8], float& acc) {
+    float h[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const float v = *reinterpret_cast<const float*>(base + o[4 * par + t] + 4 * SignLut<GPW>::base(gi, t, par));
+        h[t >> 1] = ((t & 1) == 0 && par == 0) ? v : h[t >> 1] + v;
+      }
+    if constexpr (G == 64) {
+      acc = fmaf((float)sl.code(p, gi, 0), h[0], acc);
+      acc = fmaf((float)sl.code(p, gi, 2), h[1], acc);
+    } else {
+      acc = fmaf((float)sl.code(p, gi, 0), h[0] + h[1], acc);
+    }
+  };
   float part = 0.f;
 #pragma unroll
   for (int sb = 0; sb < SB; ++sb) {
     float acc = 0.f;
+    // The super-block's (column tile, plane) dwords in order, two at a time.
 #pragma unroll
-    for (int gi = 2 * sb; gi < 2 * sb + 2 && gi < GPW; ++gi)
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint32_t w = sl.w[gi][p];
-        float h[2];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int par = 0; par < 2; ++par) {
-            const uint32_t off =
-                (nibble_offset(w, 16 * par + 4 * t) | lane_off) + 4 * SignLut<GPW>::base(gi, t, par);
-            const float v = *reinterpret_cast<const float*>(base + off);
-            h[t >> 1] = ((t & 1) == 0 && par == 0) ? v : h[t >> 1] + v;
-          }
-        if constexpr (G == 64) {
-          acc = fmaf((float)sl.code(p, gi, 0), h[0], acc);
-          acc = fmaf((float)sl.code(p, gi, 2), h[1], acc);
-        } else {
-          acc = fmaf((float)sl.code(p, gi, 0), h[0] + h[1], acc);
-        }
-      }
+    for (int u = 0; u < U; u += 2) {
+      uint32_t o0[8], o1[8];
+      nibble_offsets_at<U>([&](int v) { return sl.w[GB * sb + v / P][v % P]; }, u, lane_off, o0, o1);
+      fold(GB * sb + u / P, u % P, o0, acc);
+      if (u + 1 < U) fold(GB * sb + (u + 1) / P, (u + 1) % P, o1, acc);
+    }
     part = fmaf(sl.dscale(2 * sb), acc, part);
   }
   return part;
