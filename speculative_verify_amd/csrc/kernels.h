@@ -140,6 +140,24 @@ __device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i, const PairDecod
   return ((w >> (4 * i)) & d.mask) | d.orv;
 }
 
+// int4_pair of pairs i = 0..3 of the two code dwords lo and hi, with one
+// 64-bit shift of hi:lo per nonzero i in place of two 32-bit ones: the bits
+// a shift moves from hi into lo land at bits 20 and up, outside the mask.
+__device__ __forceinline__ void int4_pairs2(uint32_t lo, uint32_t hi, const PairDecode& d, uint32_t (&bl)[4],
+                                            uint32_t (&bh)[4]) {
+  const uint64_t w = (uint64_t)hi << 32 | lo;
+  uint64_t s[4];
+  s[0] = w;
+  asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s[1]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s[2]) : "v"(w));
+  asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s[3]) : "v"(w));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bl[i] = ((uint32_t)s[i] & d.mask) | d.orv;
+    bh[i] = ((uint32_t)(s[i] >> 32) & d.mask) | d.orv;
+  }
+}
+
 // bf16 pair (b_even, b_odd) in {-1, +1} for pair ip = 4t + i of a sign dword.
 __device__ __forceinline__ uint32_t sign_pair(uint32_t w, int ip, const PairDecode& d) {
   return ((w << (15 - ip)) & d.mask) | d.orv;
@@ -740,12 +758,14 @@ __device__ __forceinline__ float w4a16_tile_partial(const Int4Slot<GPW>& sl, con
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const uint32_t w[4] = {sl.c[gi].x, sl.c[gi].y, sl.c[gi].z, sl.c[gi].w};
+    uint32_t b[4][4];
+    int4_pairs2(sl.c[gi].x, sl.c[gi].y, magic, b[0], b[1]);
+    int4_pairs2(sl.c[gi].z, sl.c[gi].w, magic, b[2], b[3]);
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = dot2(int4_pair(w[t], i, magic), xp[gi][4 * t + i], acc);
+      for (int i = 0; i < 4; ++i) acc = dot2(b[t][i], xp[gi][4 * t + i], acc);
     part = fmaf(sl.s.bf16(gi), acc - zc[gi], part);
   }
   return part;
@@ -1962,14 +1982,19 @@ __global__ void __launch_bounds__(64 * MAXW)
 #pragma unroll
       for (int u = 0; u < IL; ++u) c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t0 = 0; t0 < 4; t0 += 2) {
+        // k blocks t0 and t0 + 1 of every chain decoded together
+        // (int4_pairs2 on adjacent code dwords), then the MFMAs in k-block
+        // order.
+        uint32_t b[IL][2][4];
 #pragma unroll
-        for (int u = 0; u < IL; ++u) {
-          const uint32_t w = (&ring[j].c[g0c + u].x)[t];
-          const uint32_t bq[4] = {int4_pair(w, 0, magic), int4_pair(w, 1, magic), int4_pair(w, 2, magic),
-                                  int4_pair(w, 3, magic)};
-          c[u] = mfma16x16x32(&xa[g0c + u][4 * t], bq, c[u]);
-        }
+        for (int u = 0; u < IL; ++u)
+          int4_pairs2((&ring[j].c[g0c + u].x)[t0], (&ring[j].c[g0c + u].x)[t0 + 1], magic, b[u][0], b[u][1]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int u = 0; u < IL; ++u) c[u] = mfma16x16x32(&xa[g0c + u][4 * (t0 + tt)], b[u][tt], c[u]);
+      }
 #pragma unroll
       for (int u = 0; u < IL; ++u) {
         const float sc = ring[j].s.bf16(g0c + u);
