@@ -862,11 +862,29 @@ struct ChunkStage {
     if (lane < L) buf[k][wave][lane] = v;
   }
 
-  // Sum over the waves of tile c of the chunk that holds tile i.
+  // Sum over the waves of tile c of the chunk that holds tile i, in wave
+  // order.  With U > 1 the reads go out U at a time (nwaves is uniform), so
+  // the sum waits for one LDS round trip per U waves instead of one per
+  // wave.  The scalar partials of the eight-wave mat-vecs take all seven at
+  // once; the mat-muls choose U by their register headroom (an unrolled
+  // float4 read holds four registers until its add).
+  template <int U = (sizeof(V) == sizeof(float) && MAXW <= 8) ? MAXW - 1 : 1>
   __device__ __forceinline__ V sum(int i, int c, int nwaves, int l) const {
     const int k = ((i / C) & 1) * C + c;
     V s = buf[k][0][l];
-    for (int w = 1; w < nwaves; ++w) s += buf[k][w][l];
+    if constexpr (U > 1) {
+#pragma unroll
+      for (int w0 = 1; w0 < MAXW; w0 += U) {
+        V t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) t[u] = buf[k][w0 + u < nwaves ? w0 + u : 0][l];  // nwaves <= MAXW
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (w0 + u < nwaves) s += t[u];
+      }
+    } else {
+      for (int w = 1; w < nwaves; ++w) s += buf[k][w][l];
+    }
     return s;
   }
 };
@@ -994,12 +1012,25 @@ __device__ __forceinline__ void gemv_argmax_epilogue(float best_v, int best_i, i
   best_over_wave(best_v, best_i);
   if (lane == 0) part[wave] = ArgBest{best_v, best_i};
   __syncthreads();
-  if (threadIdx.x == 0)
-    for (int w = 1; w < nwaves; ++w)
+  if (threadIdx.x == 0) {
+    // Up to eight waves, every wave's entry is read at once (unrolled over
+    // MAXW; nwaves is uniform), then folded in wave order.
+    constexpr int U = MAXW <= 8 ? MAXW : 1;
+    ArgBest t[U];
+#pragma unroll
+    for (int w = 0; w < U; ++w) t[w] = part[w < nwaves ? w : 0];
+#pragma unroll
+    for (int w = 1; w < U; ++w)
+      if (w < nwaves && better(t[w].v, t[w].idx, best_v, best_i)) {
+        best_v = t[w].v;
+        best_i = t[w].idx;
+      }
+    for (int w = U; w < nwaves; ++w)
       if (better(part[w].v, part[w].idx, best_v, best_i)) {
         best_v = part[w].v;
         best_i = part[w].idx;
       }
+  }
   argmax_complete(argmax_key(best_v, best_i), threadIdx.x == 0 && best_i < N, 0, ws, 1, N, ho);
 }
 
@@ -1877,12 +1908,19 @@ __device__ __forceinline__ void gemm_argmax_epilogue(RowBest4& b, int wave, int 
   __syncthreads();
   float bvv = -FLT_MAX;
   int bii = INT_MAX;
-  if ((int)threadIdx.x < M)
-    for (int w = 0; w < nwaves; ++w)
-      if (better(fin[w][threadIdx.x].v, fin[w][threadIdx.x].idx, bvv, bii)) {
-        bvv = fin[w][threadIdx.x].v;
-        bii = fin[w][threadIdx.x].idx;
+  if ((int)threadIdx.x < M) {
+    // Every wave's entry read at once (unrolled over MAXW; nwaves is
+    // uniform), then folded in wave order.
+    ArgBest t[MAXW];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) t[w] = fin[w < nwaves ? w : 0][threadIdx.x];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w)
+      if (w < nwaves && better(t[w].v, t[w].idx, bvv, bii)) {
+        bvv = t[w].v;
+        bii = t[w].idx;
       }
+  }
   argmax_complete(argmax_key(bvv, bii), (int)threadIdx.x < M && bii < N, threadIdx.x, ws, M, N, ho);
 }
 
@@ -1949,6 +1987,9 @@ __global__ void __launch_bounds__(64 * MAXW)
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
   constexpr int C = chunk_gemm<MAXW>();
+  // Reads in flight in the cross-wave sum of a tile (ChunkStage::sum): as
+  // many as the registers left beside the ring allow.
+  constexpr int kSumW4 = MAXW <= 8 && D <= 2 ? MAXW - 1 : 1;
   __shared__ ChunkStage<float4, C, MAXW, 64> stage;
   if constexpr (kRowsX) {
     __shared__ uint4 xt[MAXW][256];  // a wave's transposition region (4 KiB)
@@ -2015,7 +2056,7 @@ __global__ void __launch_bounds__(64 * MAXW)
       const int first = i - ci;
       // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
       // same outputs of every tile, so its columns arrive in increasing n.
-      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, tw.tile(first + wave), M, N, Y, best);
+      if (wave <= ci) gemm_emit<ARGMAX>(stage.template sum<kSumW4>(i, wave, nwaves, lane), q, r, tw.tile(first + wave), M, N, Y, best);
     }
   };
   // Whole rounds of the ring, then the tiles of a partial last round (held in
@@ -2164,6 +2205,9 @@ __global__ void __launch_bounds__(64 * MAXW)
   // Keep the whole prefetch issued before anything waits on the activations.
   __builtin_amdgcn_sched_barrier(0);
   constexpr int C = chunk_gemm<MAXW>();
+  // Reads in flight in the cross-wave sum of a tile (ChunkStage::sum): as
+  // many as the registers left beside the ring allow.
+  constexpr int kSumPl = MAXW <= 8 && D <= 2 && F::P <= 3 ? MAXW - 1 : 1;
   __shared__ ChunkStage<float4, C, MAXW, 64> stage;
   if constexpr (kRowsX) {
     __shared__ uint4 xt[MAXW][256];  // a wave's transposition region (4 KiB)
@@ -2195,7 +2239,7 @@ __global__ void __launch_bounds__(64 * MAXW)
       const int first = i - ci;
       // Wave c finishes tile c of the chunk (C <= waves); a lane meets the
       // same outputs of every tile, so its columns arrive in increasing n.
-      if (wave <= ci) gemm_emit<ARGMAX>(stage.sum(i, wave, nwaves, lane), q, r, tw.tile(first + wave), M, N, Y, best);
+      if (wave <= ci) gemm_emit<ARGMAX>(stage.template sum<kSumPl>(i, wave, nwaves, lane), q, r, tw.tile(first + wave), M, N, Y, best);
     }
   };
   // Whole rounds of the ring, then the tiles of a partial last round (held in
