@@ -75,9 +75,13 @@ inline int env_int(const char* name, int lo, int hi, int dflt) {
 // wave_quantum: the M <= 16 kernels finish the tiles of a chunk one wave per
 // tile (up to four tiles), so their workgroups carry a multiple of four waves.
 // Measured on MI355X (rocprofv3 kernel traces of the decode, verify and head
-// shapes at K = 4096, sweeping both knobs): the M = 1 mat-vecs run best at
-// two workgroups per CU with a ring of <= 2 tiles, everything else at one
-// workgroup per CU; a ring of 2 tiles already keeps more bytes in flight
+// shapes at K = 4096, sweeping both knobs): the sign-plane and sa* mat-vecs
+// run best at two workgroups per CU while the row tiles number at most three
+// per CU and at one above (interleaved A/B, five rounds: N = 12288 3.4%
+// slower at one, N = 8192 alike, N = 16384 and 28672 6-8% faster), the
+// W4A16 mat-vec at one at every size (3-14% faster than at two for
+// N = 8192..28672, K = 2048..8192), everything else at one workgroup per
+// CU, all with a ring of <= 2 tiles; a ring of 2 tiles already keeps more bytes in flight
 // than the memory system's bandwidth-latency product, and deeper rings were
 // slower (the M = 16 sign-plane head at 32768 rows, eight tiles a
 // workgroup: 26.4 us at a ring of 2, 28.7 at 3).  Workgroups of the M <= 16
@@ -97,8 +101,12 @@ inline int env_int(const char* name, int lo, int hi, int dflt) {
 // and twice the waves double the per-wave prologue and the cross-wave sums.
 struct LaunchPref {
   int wgs_per_cu, max_depth, shallow;
+  // Above wide_tiles row tiles per CU, wide_wgs workgroups per CU instead
+  // (0: no such rule).
+  int wide_tiles = 0, wide_wgs = 0;
 };
-constexpr LaunchPref kPrefGemv = {2, 2, 0};
+constexpr LaunchPref kPrefGemv = {2, 2, 0, 3, 1};
+constexpr LaunchPref kPrefGemvW4 = {1, 2, 0};
 constexpr LaunchPref kPrefGemmW4 = {1, 2, 2};
 constexpr LaunchPref kPrefGemmPlanes = {1, 2, 2};
 constexpr LaunchPref kPrefHeadM1 = {1, 2, 0};
@@ -114,7 +122,8 @@ inline int plan(int64_t N, int64_t K, int wave_quantum, LaunchPref pref, Shape* 
   s->waves = (s->waves + wave_quantum - 1) / wave_quantum * wave_quantum;
   // SVQ_WG_PER_CU / SVQ_PIPE_DEPTH / SVQ_GRID_MAX override the preferences
   // (for tuning runs).
-  int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, pref.wgs_per_cu);
+  const int wpc = pref.wide_tiles > 0 && s->NT > pref.wide_tiles * cus ? pref.wide_wgs : pref.wgs_per_cu;
+  int want = cus * env_int("SVQ_WG_PER_CU", 1, 8, wpc);
   const int gmax = env_int("SVQ_GRID_MAX", 1, 1 << 20, want);
   if (gmax < want) want = gmax;
   s->grid = s->NT < want ? s->NT : want;

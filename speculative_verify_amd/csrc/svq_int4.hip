@@ -89,7 +89,7 @@ int gemv_w4a16(const uint8_t* packed, const uint16_t* x, uint16_t* y, int64_t N,
                void* stream) {
   if (int rc = check_linear("gemv_w4a16", packed, x, y, 1, N, K, G, 0)) return rc;
   Shape sh;
-  if (int rc = plan(N, K, 1, kPrefGemv, &sh)) return rc;
+  if (int rc = plan(N, K, 1, kPrefGemvW4, &sh)) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(x);
   dispatch<6, 2>(sh, [&](auto G, auto W, auto D) {
