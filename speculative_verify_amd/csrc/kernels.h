@@ -476,7 +476,9 @@ __device__ __forceinline__ void expand_x(const uint32_t (&xo)[GPW], uint32_t (&x
   for (int gi = 0; gi < GPW; ++gi) {
     static_for<0, 16>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      xp[gi][j] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x150 + j, 0xF, 0xF, false);  // row_newbcast:j
+      // Every lane is written (all rows and banks enabled), so the move
+      // needs no old value and the compiler no initialising move.
+      xp[gi][j] = __builtin_amdgcn_mov_dpp(xo[gi], 0x150 + j, 0xF, 0xF, false);  // row_newbcast:j
     });
   }
 }
@@ -1168,10 +1170,10 @@ __device__ __forceinline__ void build_sign_lut(SignLut<GPW>& lut, const uint32_t
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     uint32_t b[4];
-    b[0] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x00, 0xF, 0xF, false);  // quad_perm [0, 0, 0, 0]
-    b[1] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0x55, 0xF, 0xF, false);  // quad_perm [1, 1, 1, 1]
-    b[2] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0xAA, 0xF, 0xF, false);  // quad_perm [2, 2, 2, 2]
-    b[3] = __builtin_amdgcn_update_dpp(0u, xo[gi], 0xFF, 0xF, 0xF, false);  // quad_perm [3, 3, 3, 3]
+    b[0] = __builtin_amdgcn_mov_dpp(xo[gi], 0x00, 0xF, 0xF, false);  // quad_perm [0, 0, 0, 0]
+    b[1] = __builtin_amdgcn_mov_dpp(xo[gi], 0x55, 0xF, 0xF, false);  // quad_perm [1, 1, 1, 1]
+    b[2] = __builtin_amdgcn_mov_dpp(xo[gi], 0xAA, 0xF, 0xF, false);  // quad_perm [2, 2, 2, 2]
+    b[3] = __builtin_amdgcn_mov_dpp(xo[gi], 0xFF, 0xF, 0xF, false);  // quad_perm [3, 3, 3, 3]
 #pragma unroll
     for (int i = 0; i < 4; ++i) b[i] = own ? b[i] : 0u;
     const f32x4_t e0 = mfma16x16x32(s0, b, zero);
