@@ -178,6 +178,30 @@ def test_gemv_binplane_ragged(N, K, P):
     check_close(run_gemv_binplane(signs, alpha, x), y[0], a[0], f"N={N} K={K} P={P}")
 
 
+@pytest.mark.parametrize("kind", ["w4a16", "binplane", "sa"])
+def test_gemv_wide_matrices(kind):
+    # Above three row tiles per CU every mat-vec runs one workgroup a CU with
+    # a two-tile ring (N = 20000: 1250 row tiles, a ragged last tile and a
+    # partial last ring round on some workgroups).
+    N, K = 20000, 4096
+    rng = np.random.default_rng(4242)
+    x = synth.activations(rng, 1, K)
+    print(f"gemv wide {kind} N={N} K={K}", flush=True)
+    if kind == "w4a16":
+        codes, scales = synth.int4_weights(rng, N, K)
+        y, a = oracle.linear_w4a16(codes, scales, x)
+        got = run_gemv_w4a16(codes, scales, x)
+    elif kind == "binplane":
+        signs, alpha = synth.binplane_weights(rng, N, K, P=3)
+        y, a = oracle.linear_binplane(signs, alpha, x)
+        got = run_gemv_binplane(signs, alpha, x)
+    else:
+        signs, codes, d = synth.sa_weights(rng, N, K, P=3, G=128)
+        y, a = oracle.linear_sa(signs, codes, d, x, G=128)
+        got = run_gemv_sa(signs, codes, d, x, G=128)
+    check_close(got, y[0], a[0], f"wide {kind}")
+
+
 def test_gemv_binplane_onehot_unit_plane_is_exact():
     N, K = 20, 256
     rng = np.random.default_rng(6)
